@@ -1,0 +1,161 @@
+/*
+ * lmhead.h - C ABI of the fused LM-head log-prob / entropy op for MI355X (gfx950).
+ *
+ * The op takes final hidden states X [N, H] and the vocabulary weight W [V, H]
+ * (both bf16, row-major) and returns, per token, the log-probability of its
+ * target token and the entropy of its next-token distribution, plus the
+ * backward pass into dX and dW, without ever writing the [N, V] logits to
+ * memory.
+ *
+ * Sources (all behaviour below is defined by these pages):
+ *  - prime-rl PR #3326, "Don't compute the logprobs and their gradients for
+ *    tokens no loss com...": author comment (the vocab matmul is where the
+ *    FLOPs are; tokens no loss reads are skipped) and Overview (a keep mask
+ *    selects positions; compact -> chunked log-prob/entropy -> expand back,
+ *    with zero log-prob and entropy at skipped positions; default token chunk
+ *    8192).
+ *  - SkyRL PR #2374, "feat(megatron): fuse LM-head entropy for RL": "How it
+ *    works" and "Usage" (one projection gives selected-token log-probs and
+ *    entropy; metric-only entropy adds no gradient work; entropy-loss mode
+ *    keeps the entropy derivative; the caller's gradient requirement selects
+ *    it), and the gemini-code-assist review (entropy saved for backward, not
+ *    recomputed).
+ *  - twinkle PR #283, "Fix three memory defects in the Megatron path",
+ *    section 1 (float32 compute; float32 log-probs and entropies for bf16
+ *    inputs; the softmax is recomputed in backward from saved inputs, never
+ *    stored).
+ *
+ * Definitions, per kept row i with z = W x_i (fp32 accumulation of bf16
+ * products) and LSE_i = log sum_v exp(z_v):
+ *   logp_i    = z_{t_i} - LSE_i
+ *   entropy_i = -sum_v p_v log p_v,   p_v = exp(z_v - LSE_i)   (nats)
+ * Skipped rows (keep_mask[i] == 0) get logp = +0.0 and entropy = +0.0, their
+ * dX row is +0.0 and they contribute nothing to dW.
+ * Backward, for the loss L = sum_i g_lp[i] logp_i + [entropy_requires_grad]
+ * g_H[i] entropy_i:
+ *   dZ_i = g_lp[i] (onehot(t_i) - p) - [entropy_requires_grad] g_H[i] p (log p + entropy_i)
+ *   dX_i = dZ_i W          dW = sum_i dZ_i^T x_i
+ * dZ is rounded to bf16 (round to nearest even) before the two products.
+ *
+ * Conventions
+ *  - Every tensor pointer is a DEVICE pointer, caller-owned, 16-byte aligned
+ *    (256-byte alignment recommended). The library never allocates device
+ *    memory and never synchronises, except in the two calls marked "syncs".
+ *  - All work is enqueued on `stream` (a hipStream_t; 0 = the null stream)
+ *    in stream order. Calls are reentrant and keep no state between calls
+ *    other than a per-device cache of the compute-unit count.
+ *  - Every call returns an lmhead_status. All argument checks run on the host
+ *    before anything is enqueued; a failing call enqueues nothing.
+ *  - Sizes: N >= 0, V >= 1, H >= 64 with H % 64 == 0 (else
+ *    LMHEAD_ERR_UNSUPPORTED). N and V are otherwise arbitrary.
+ *  - Results are bitwise reproducible run to run for the same inputs and
+ *    arguments (fixed reduction orders, no floating-point atomics).
+ */
+#ifndef LMHEAD_H
+#define LMHEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMHEAD_OK = 0,
+  LMHEAD_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, bad flag combination, misalignment */
+  LMHEAD_ERR_UNSUPPORTED = 2,   /* H % 64 != 0 or H < 64, sizes beyond int32 indexing */
+  LMHEAD_ERR_WORKSPACE = 3,     /* saved or workspace buffer smaller than the size query returns */
+  LMHEAD_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+  LMHEAD_ERR_TARGET_RANGE = 5   /* a kept row's target is outside [0, V) */
+} lmhead_status;
+
+/* Bytes of the `saved` buffer lmhead_fwd fills for lmhead_bwd: a small header,
+ * the ascending kept-row positions, a per-row position map, and per kept row
+ * the log-sum-exp and the entropy (16 bytes per row plus 1 KiB). The saved
+ * state never holds a full-vocabulary activation (twinkle PR #283, section 1).
+ * Returns 0 if N < 0. */
+size_t lmhead_saved_bytes(int64_t N);
+
+/* Workspace bytes lmhead_fwd needs for N rows and vocabulary V: per kept row
+ * and per 256-wide vocabulary tile, three fp32 partial statistics, plus the
+ * target logit. Returns 0 on invalid sizes. */
+size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V);
+
+/* Workspace bytes lmhead_bwd needs: one bf16 dZ buffer of
+ * min(token_chunk, N) rows by V rounded up to 256 columns.
+ * token_chunk <= 0 selects the default 8192 (prime-rl PR #3326, Overview).
+ * Returns 0 on invalid sizes. */
+size_t lmhead_bwd_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t token_chunk);
+
+/* Forward: compaction of the kept rows, the fused projection with per-row
+ * online max / sum-exp / sum p*z statistics over vocabulary tiles, the
+ * target-logit pick, the fixed-order merge, and the expand-back.
+ *
+ *  hidden     bf16 [N, H] row-major
+ *  weight     bf16 [V, H] row-major
+ *  targets    int32 [N]; only kept rows are read. A kept target outside
+ *             [0, V) yields logp = NaN at that row and is reported by
+ *             lmhead_check_status.
+ *  keep_mask  uint8 [N], nonzero = keep; NULL = keep every row
+ *  logp       fp32 [N] out, fully written (+0.0 at skipped rows)
+ *  entropy    fp32 [N] out, fully written; must be NULL iff !return_entropy
+ *  entropy_requires_grad  requires return_entropy (else INVALID_ARG); it is
+ *             recorded in `saved` and selects the backward's entropy term.
+ *  saved      device buffer of >= lmhead_saved_bytes(N) bytes, out
+ *  workspace  device buffer of >= lmhead_fwd_workspace_bytes(N, H, V) bytes;
+ *             free for reuse once the enqueued work has completed.
+ *  N == 0 is valid and enqueues a header write only.
+ */
+int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
+               const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V,
+               int return_entropy, int entropy_requires_grad,
+               float* logp, float* entropy,
+               void* saved, size_t saved_bytes,
+               void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* Backward: per chunk of `token_chunk` kept rows, recompute the logit tile,
+ * form dZ (above) in bf16, then dX rows = dZ W (scattered back to the rows'
+ * original positions) and dW (+)= dZ^T X. The first chunk writes dW, later
+ * chunks add to it in ascending chunk order.
+ *
+ *  hidden, weight, targets, N, H, V: exactly as passed to lmhead_fwd
+ *  entropy_requires_grad: as passed to lmhead_fwd
+ *  saved      the buffer lmhead_fwd filled, unmodified
+ *  grad_logp  fp32 [N]; skipped rows are not read
+ *  grad_entropy fp32 [N]; must be NULL iff !entropy_requires_grad
+ *  grad_hidden fp32 [N, H] out, fully overwritten (+0.0 rows where skipped)
+ *  grad_weight fp32 [V, H] out, fully overwritten
+ *  token_chunk rows per chunk; <= 0 selects 8192
+ *  workspace  >= lmhead_bwd_workspace_bytes(N, H, V, token_chunk) bytes
+ */
+int lmhead_bwd(const void* hidden, const void* weight, const int32_t* targets,
+               int64_t N, int64_t H, int64_t V, int entropy_requires_grad,
+               const void* saved, size_t saved_bytes,
+               const float* grad_logp, const float* grad_entropy,
+               float* grad_hidden, float* grad_weight,
+               int64_t token_chunk, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* Syncs `stream`, then reads the number of kept rows from `saved` into
+ * *n_kept_host (the token fraction the trainer logs, prime-rl PR #3326,
+ * Overview). */
+int lmhead_read_n_kept(const void* saved, int64_t* n_kept_host, void* stream);
+
+/* Syncs `stream`, then returns LMHEAD_ERR_TARGET_RANGE if the forward that
+ * filled `saved` met a kept row whose target is outside [0, V), else
+ * LMHEAD_OK. */
+int lmhead_check_status(const void* saved, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* lmhead_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int lmhead_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMHEAD_H */

@@ -1,0 +1,223 @@
+"""Fused LM-head log-prob / entropy op for MI355X (gfx950).
+
+Thin Python binding over liblmhead.so (C ABI in include/lmhead.h). The
+functions named ``lmhead_*`` marshal torch tensors to the C calls of the same
+name; every step of the computation runs in the library's HIP kernels. PyTorch
+provides device memory and the current stream only.
+
+``fused_logprobs`` wraps the two calls in a ``torch.autograd.Function`` with the
+argument set of the pages' fused head: ``keep_mask`` (prime-rl PR #3326,
+Overview), ``return_entropy`` / ``entropy_requires_grad`` (SkyRL PR #2374,
+"How it works" and "Usage"), float32 outputs for bf16 inputs (twinkle PR #283,
+section 1), and a token chunk that defaults to 8192 (prime-rl PR #3326,
+Overview).
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import LMHeadError, check
+
+__all__ = [
+    "lmhead_saved_bytes", "lmhead_fwd_workspace_bytes", "lmhead_bwd_workspace_bytes",
+    "lmhead_fwd", "lmhead_bwd", "lmhead_read_n_kept", "lmhead_check_status",
+    "lmhead_status_string", "lmhead_version", "fused_logprobs", "LMHeadError",
+    "DEFAULT_TOKEN_CHUNK",
+]
+
+DEFAULT_TOKEN_CHUNK = 8192
+
+
+def _L():
+    return _lib.load()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def lmhead_saved_bytes(N: int) -> int:
+    return int(_L().lmhead_saved_bytes(N))
+
+
+def lmhead_fwd_workspace_bytes(N: int, H: int, V: int) -> int:
+    return int(_L().lmhead_fwd_workspace_bytes(N, H, V))
+
+
+def lmhead_bwd_workspace_bytes(N: int, H: int, V: int, token_chunk: int = 0) -> int:
+    return int(_L().lmhead_bwd_workspace_bytes(N, H, V, token_chunk))
+
+
+def lmhead_status_string(status: int) -> str:
+    return _L().lmhead_status_string(status).decode()
+
+
+def lmhead_version() -> int:
+    return int(_L().lmhead_version())
+
+
+def lmhead_fwd(hidden, weight, targets, keep_mask=None, return_entropy=False,
+               entropy_requires_grad=False, *, logp=None, entropy=None, saved=None,
+               workspace=None, stream=None):
+    """Forward. hidden bf16 [N, H], weight bf16 [V, H], targets int32 [N],
+    keep_mask uint8/bool [N] or None. Returns (logp fp32 [N], entropy fp32 [N]
+    or None, saved uint8 tensor). Output and scratch buffers may be passed in
+    preallocated; the rest are allocated with torch."""
+    _need(hidden, "hidden", torch.bfloat16)
+    if hidden.dim() != 2:
+        raise ValueError("hidden must be [N, H]")
+    N, H = hidden.shape
+    dev = hidden.device
+    _need(weight, "weight", torch.bfloat16, device=dev)
+    if weight.dim() != 2 or weight.shape[1] != H:
+        raise ValueError("weight must be [V, H]")
+    V = weight.shape[0]
+    _need(targets, "targets", torch.int32, (N,), dev)
+    if keep_mask is not None:
+        if keep_mask.dtype == torch.bool:
+            keep_mask = keep_mask.view(torch.uint8)
+        _need(keep_mask, "keep_mask", torch.uint8, (N,), dev)
+    if logp is None:
+        logp = torch.empty(N, dtype=torch.float32, device=dev)
+    _need(logp, "logp", torch.float32, (N,), dev)
+    if return_entropy:
+        if entropy is None:
+            entropy = torch.empty(N, dtype=torch.float32, device=dev)
+        _need(entropy, "entropy", torch.float32, (N,), dev)
+    else:
+        entropy = None
+    L = _L()
+    sb = int(L.lmhead_saved_bytes(N))
+    if saved is None:
+        saved = torch.empty(sb, dtype=torch.uint8, device=dev)
+    wb = int(L.lmhead_fwd_workspace_bytes(N, H, V))
+    if workspace is None:
+        workspace = torch.empty(max(wb, 1), dtype=torch.uint8, device=dev)
+    st = L.lmhead_fwd(_ptr(hidden), _ptr(weight), _ptr(targets), _ptr(keep_mask), N, H, V,
+                      int(bool(return_entropy)), int(bool(entropy_requires_grad)),
+                      _ptr(logp), _ptr(entropy), _ptr(saved), saved.numel(),
+                      _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    check("lmhead_fwd", st)
+    return logp, entropy, saved
+
+
+def lmhead_bwd(hidden, weight, targets, saved, grad_logp, grad_entropy=None,
+               entropy_requires_grad=False, token_chunk=0, *, grad_hidden=None,
+               grad_weight=None, workspace=None, stream=None):
+    """Backward. Returns (grad_hidden fp32 [N, H], grad_weight fp32 [V, H])."""
+    _need(hidden, "hidden", torch.bfloat16)
+    N, H = hidden.shape
+    dev = hidden.device
+    _need(weight, "weight", torch.bfloat16, device=dev)
+    V = weight.shape[0]
+    _need(targets, "targets", torch.int32, (N,), dev)
+    _need(saved, "saved", torch.uint8, device=dev)
+    _need(grad_logp, "grad_logp", torch.float32, (N,), dev)
+    if entropy_requires_grad:
+        _need(grad_entropy, "grad_entropy", torch.float32, (N,), dev)
+    else:
+        grad_entropy = None
+    if grad_hidden is None:
+        grad_hidden = torch.empty(N, H, dtype=torch.float32, device=dev)
+    if grad_weight is None:
+        grad_weight = torch.empty(V, H, dtype=torch.float32, device=dev)
+    _need(grad_hidden, "grad_hidden", torch.float32, (N, H), dev)
+    _need(grad_weight, "grad_weight", torch.float32, (V, H), dev)
+    L = _L()
+    wb = int(L.lmhead_bwd_workspace_bytes(N, H, V, token_chunk))
+    if workspace is None:
+        workspace = torch.empty(max(wb, 1), dtype=torch.uint8, device=dev)
+    st = L.lmhead_bwd(_ptr(hidden), _ptr(weight), _ptr(targets), N, H, V,
+                      int(bool(entropy_requires_grad)), _ptr(saved), saved.numel(),
+                      _ptr(grad_logp), _ptr(grad_entropy), _ptr(grad_hidden),
+                      _ptr(grad_weight), int(token_chunk), _ptr(workspace), workspace.numel(),
+                      _stream(stream, dev))
+    check("lmhead_bwd", st)
+    return grad_hidden, grad_weight
+
+
+def lmhead_read_n_kept(saved, stream=None) -> int:
+    out = ctypes.c_int64(0)
+    check("lmhead_read_n_kept",
+          _L().lmhead_read_n_kept(_ptr(saved), ctypes.byref(out), _stream(stream, saved.device)))
+    return int(out.value)
+
+
+def lmhead_check_status(saved, stream=None) -> int:
+    return int(_L().lmhead_check_status(_ptr(saved), _stream(stream, saved.device)))
+
+
+class _FusedLMHead(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, hidden, weight, targets, keep_mask, return_entropy, entropy_requires_grad,
+                token_chunk):
+        logp, ent, saved = lmhead_fwd(hidden, weight, targets, keep_mask, return_entropy,
+                                      entropy_requires_grad)
+        ctx.save_for_backward(hidden, weight, targets, saved)
+        ctx.erg = bool(entropy_requires_grad)
+        ctx.ret_ent = bool(return_entropy)
+        ctx.token_chunk = int(token_chunk)
+        if not return_entropy:
+            return logp
+        if not entropy_requires_grad:
+            ctx.mark_non_differentiable(ent)
+        return logp, ent
+
+    @staticmethod
+    def backward(ctx, g_logp, g_ent=None):
+        hidden, weight, targets, saved = ctx.saved_tensors
+        g_logp = g_logp.float().contiguous()
+        if ctx.erg:
+            g_ent = (torch.zeros_like(g_logp) if g_ent is None else g_ent.float().contiguous())
+        gX, gW = lmhead_bwd(hidden, weight, targets, saved, g_logp,
+                            g_ent if ctx.erg else None, ctx.erg, ctx.token_chunk)
+        gX = gX.to(hidden.dtype) if ctx.needs_input_grad[0] else None
+        gW = gW.to(weight.dtype) if ctx.needs_input_grad[1] else None
+        return gX, gW, None, None, None, None, None
+
+
+def fused_logprobs(hidden, weight, targets, keep_mask=None, return_entropy=False,
+                   entropy_requires_grad=False, token_chunk_size=DEFAULT_TOKEN_CHUNK):
+    """Selected-target log-probs (and entropy) of ``hidden @ weight.T`` without
+    materialising the logits. ``hidden`` may be [..., H]; outputs have the
+    leading shape of ``hidden`` and dtype float32. Rows where ``keep_mask`` is
+    false get 0 and no gradient."""
+    if entropy_requires_grad and not return_entropy:
+        raise ValueError("entropy_requires_grad requires return_entropy")
+    lead = hidden.shape[:-1]
+    h2 = hidden.reshape(-1, hidden.shape[-1]).contiguous()
+    t = targets.reshape(-1).to(torch.int32).contiguous()
+    km = None
+    if keep_mask is not None:
+        km = keep_mask.reshape(-1).to(torch.uint8).contiguous()
+    out = _FusedLMHead.apply(h2, weight.contiguous(), t, km, bool(return_entropy),
+                             bool(entropy_requires_grad), int(token_chunk_size))
+    if return_entropy:
+        lp, ent = out
+        return lp.reshape(lead), ent.reshape(lead)
+    return out.reshape(lead)

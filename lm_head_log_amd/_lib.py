@@ -1,0 +1,63 @@
+"""ctypes loader for liblmhead.so. No fallback: a missing library is an error."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblmhead.so")
+
+# Every symbol include/lmhead.h declares, with its ctypes signature.
+c_size = ctypes.c_size_t
+c_i64 = ctypes.c_int64
+c_int = ctypes.c_int
+c_vp = ctypes.c_void_p
+
+SIGNATURES = {
+    "lmhead_saved_bytes": (c_size, [c_i64]),
+    "lmhead_fwd_workspace_bytes": (c_size, [c_i64, c_i64, c_i64]),
+    "lmhead_bwd_workspace_bytes": (c_size, [c_i64, c_i64, c_i64, c_i64]),
+    "lmhead_fwd": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_int,
+                           c_vp, c_vp, c_vp, c_size, c_vp, c_size, c_vp]),
+    "lmhead_bwd": (c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_size,
+                           c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_size, c_vp]),
+    "lmhead_read_n_kept": (c_int, [c_vp, ctypes.POINTER(c_i64), c_vp]),
+    "lmhead_check_status": (c_int, [c_vp, c_vp]),
+    "lmhead_status_string": (ctypes.c_char_p, [c_int]),
+    "lmhead_version": (c_int, []),
+}
+
+_lib = None
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load liblmhead.so (once). Raises if it is missing or lacks a symbol."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(
+            f"{p} is missing: build it with `python -m lm_head_log_amd.build` "
+            "(hipcc, gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)  # AttributeError if the symbol is not exported
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+class LMHeadError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = load().lmhead_status_string(status).decode()
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+def check(fn: str, status: int) -> None:
+    if status != 0:
+        raise LMHeadError(fn, status)

@@ -1,0 +1,842 @@
+// lmhead.hip - fused LM-head log-prob / entropy op for MI355X (gfx950):
+// kernels and the C ABI declared in include/lmhead.h.
+//
+// Forward (prime-rl PR #3326 Overview: compact -> chunked log-prob/entropy ->
+// expand back; SkyRL PR #2374 "How it works": one projection gives both the
+// selected-token log-prob and the entropy):
+//   1. k_compact     keep mask -> ascending kept rows, row -> compact position
+//   2. k_fwd_tiles   Z^T tile = W[vtile] X[kept]^T on MFMA, never stored; per
+//                    token: max, sum 2^(y), sum 2^(y) y over the tile's 256
+//                    vocab rows (y = z log2 e - max), and the target logit
+//   3. k_merge       fixed-order merge of the vocab-tile partials ->
+//                    log-sum-exp, entropy, log-prob; scatter to kept rows
+//   4. k_zero_skipped  +0.0 log-prob / entropy at skipped rows
+// Backward (twinkle PR #283 section 1: recompute the softmax from saved inputs;
+// SkyRL PR #2374 review: entropy is saved by the forward, not recomputed):
+//   1. k_zero_rows   +0.0 dX rows at skipped positions
+//   2. k_gather      X_c = X[kept] (bf16), the k-operand of dW
+//   3. per chunk of kept rows:
+//      k_dz_tiles    recompute Z^T tile, p = exp(z - LSE),
+//                    dZ = g_lp (onehot - p) - g_H p (z - LSE + H), bf16
+//      k_dx_tiles    dX[kept rows] = dZ W             (K = vocab)
+//      k_dw_tiles    dW (+)= dZ^T X_c                 (K = chunk rows)
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/lmhead.h"
+#include "gemm_core.h"
+
+#define LMH_API extern "C" __attribute__((visibility("default")))
+
+namespace lmh {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kDefaultChunk = 8192;
+constexpr int kVersion = 100;  // 0.1.0
+
+// ---------------------------------------------------------------------------
+// Saved-state layout (device memory, filled by the forward).
+// ---------------------------------------------------------------------------
+struct SavedHeader {
+  int32_t n_kept;
+  int32_t status;  // lmhead_status of the forward's device-side checks
+  int32_t N, H, V;
+  int32_t flags;   // bit 0: return_entropy, bit 1: entropy_requires_grad
+};
+constexpr size_t kHeaderBytes = 1024;
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct SavedView {
+  SavedHeader* hdr;
+  int32_t* kept_idx;  // [N] ascending kept rows (first n_kept valid)
+  int32_t* pos;       // [N] compact position of each row, -1 if skipped
+  float* lse;         // [N] log-sum-exp per kept row (compact order)
+  float* ent;         // [N] entropy per kept row (compact order)
+};
+
+static inline size_t saved_bytes_for(int64_t N) {
+  return kHeaderBytes + 4 * align256((size_t)N * 4);
+}
+
+static inline SavedView saved_view(void* base, int64_t N) {
+  char* p = static_cast<char*>(base);
+  const size_t a = align256((size_t)N * 4);
+  SavedView v;
+  v.hdr = reinterpret_cast<SavedHeader*>(p);
+  v.kept_idx = reinterpret_cast<int32_t*>(p + kHeaderBytes);
+  v.pos = reinterpret_cast<int32_t*>(p + kHeaderBytes + a);
+  v.lse = reinterpret_cast<float*>(p + kHeaderBytes + 2 * a);
+  v.ent = reinterpret_cast<float*>(p + kHeaderBytes + 3 * a);
+  return v;
+}
+
+static inline int n_vtiles(int64_t V) { return (int)((V + kBM - 1) / kBM); }
+
+static inline size_t fwd_ws_bytes(int64_t N, int64_t V) {
+  const size_t nv = (size_t)n_vtiles(V);
+  return align256((size_t)N * 4) + 3 * align256(nv * (size_t)N * 4);
+}
+
+static inline int64_t dz_ld(int64_t V) { return (V + 255) / 256 * 256; }
+
+static inline int64_t chunk_rows(int64_t N, int64_t token_chunk) {
+  const int64_t c = token_chunk > 0 ? token_chunk : kDefaultChunk;
+  return c < N ? c : N;
+}
+
+static inline size_t bwd_ws_bytes(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
+  const int64_t C = chunk_rows(N, token_chunk);
+  return align256((size_t)N * (size_t)H * 2) + align256((size_t)C * (size_t)dz_ld(V) * 2);
+}
+
+// ---------------------------------------------------------------------------
+// Compaction (one workgroup; each thread owns a contiguous segment).
+// ---------------------------------------------------------------------------
+constexpr int kCompactThreads = 1024;
+
+__global__ __launch_bounds__(kCompactThreads) void k_compact(
+    const uint8_t* __restrict__ keep, const int32_t* __restrict__ targets, int N, int H, int V,
+    int flags, int32_t* __restrict__ kept_idx, int32_t* __restrict__ pos,
+    SavedHeader* __restrict__ hdr) {
+  __shared__ int scan[kCompactThreads];
+  const int tid = threadIdx.x;
+  const int seg = (N + kCompactThreads - 1) / kCompactThreads;
+  const int beg = min(N, tid * seg);
+  const int end = min(N, beg + seg);
+  int cnt = 0;
+  for (int i = beg; i < end; ++i) cnt += keep ? (keep[i] != 0) : 1;
+  scan[tid] = cnt;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the per-thread counts.
+  for (int off = 1; off < kCompactThreads; off <<= 1) {
+    const int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int o = scan[tid] - cnt;
+  int bad = 0;
+  for (int i = beg; i < end; ++i) {
+    const bool k = keep ? (keep[i] != 0) : true;
+    if (k) {
+      kept_idx[o] = i;
+      pos[i] = o;
+      ++o;
+      const int t = targets[i];
+      bad |= (t < 0 || t >= V);
+    } else {
+      pos[i] = -1;
+    }
+  }
+  bad = __syncthreads_or(bad);
+  if (tid == 0) {
+    hdr->n_kept = scan[kCompactThreads - 1];
+    hdr->status = bad ? LMHEAD_ERR_TARGET_RANGE : LMHEAD_OK;
+    hdr->N = N;
+    hdr->H = H;
+    hdr->V = V;
+    hdr->flags = flags;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Online softmax statistics in base-2 units.
+// A partial (m, s, b) over a set S of logits z means, with y = z log2(e):
+//   m = max_S y,  s = sum_S 2^(y - m),  b = sum_S 2^(y - m) (y - m).
+// Two partials merge exactly (up to rounding) as
+//   m = max(m1, m2), a_k = 2^(m_k - m), s = sum a_k s_k,
+//   b = sum a_k (b_k + (m_k - m) s_k).
+// Then LSE = (m + log2 s) ln 2 and entropy = (log2 s - b / s) ln 2.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void stat_merge(float& m, float& s, float& b, float m2, float s2,
+                                           float b2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;  // both empty
+  float a1 = 0.f, a2 = 0.f, t1 = 0.f, t2 = 0.f;
+  if (m != -INFINITY) {
+    const float d = m - mn;
+    a1 = exp2f(d);
+    t1 = a1 * (b + d * s);
+    a1 *= s;
+  }
+  if (m2 != -INFINITY) {
+    const float d = m2 - mn;
+    a2 = exp2f(d);
+    t2 = a2 * (b2 + d * s2);
+    a2 *= s2;
+  }
+  m = mn;
+  s = a1 + a2;
+  b = t1 + t2;
+}
+
+// ---------------------------------------------------------------------------
+// Forward tiles: M = vocab (A = W rows), N = kept tokens (B = X rows via the
+// kept-row map), K = H. Epilogue reduces over the tile's vocab rows.
+// ---------------------------------------------------------------------------
+struct FwdParams {
+  const uint16_t* W;
+  const uint16_t* X;
+  const int32_t* targets;
+  const int32_t* kept_idx;
+  const SavedHeader* hdr;
+  int H, V, n_vt;
+  int64_t ldp;  // pitch (elements) between vocab tiles in the partial arrays
+  float* pm;
+  float* ps;
+  float* pb;
+  float* zt;
+};
+
+__global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
+  __shared__ uint4 lds_a[2 * kStageChunks];
+  __shared__ uint4 lds_b[2 * kStageChunks];
+  __shared__ float red[2][3][kBN];
+
+  const int rows = P.hdr->n_kept;
+  const int mt = P.n_vt;
+  const int nt = (rows + kBN - 1) / kBN;
+  const int ntiles = mt * nt;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nk = P.H / kBK;
+
+  for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
+    const int t = xcd_logical(round, gridDim.x);
+    if (t >= ntiles) continue;
+    int tm, tn;
+    tile_coords(t, mt, nt, tm, tn);
+
+    KMajorStager sa;
+    KMajorStager sb;
+    sa.init(P.W, P.H, nullptr, tm * kBM, P.V, tid);
+    sb.init(P.X, P.H, P.kept_idx, tn * kBN, rows, tid);
+    f32x16_t acc[4][4];
+    mainloop(sa, sb, nk, lds_a, lds_b, acc);
+
+    const int vbase = tm * kBM + wm * 128;
+    const bool full = vbase + 128 <= P.V;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cl = wn * 128 + j * 32 + (lane & 31);  // token inside the tile
+      const int c = tn * kBN + cl;                     // compact row
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = full || (vbase + acc_row(i, r, lane) < P.V);
+          if (ok) mx = fmaxf(mx, acc[i][j][r]);
+        }
+      float s = 0.f, b = 0.f;
+      const float m2 = mx * kLog2e;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = full || (vbase + acc_row(i, r, lane) < P.V);
+            const float y = fmaf(acc[i][j][r], kLog2e, -m2);
+            const float e = ok ? __builtin_amdgcn_exp2f(y) : 0.f;
+            s += e;
+            b = fmaf(e, ok ? y : 0.f, b);
+          }
+      }
+      float m = (mx == -INFINITY) ? -INFINITY : m2;
+      // the other half of the wave holds the other 64 rows of the same token
+      const float mo = __shfl_xor(m, 32);
+      const float so = __shfl_xor(s, 32);
+      const float bo = __shfl_xor(b, 32);
+      stat_merge(m, s, b, mo, so, bo);
+      if (lane < 32) {
+        red[wm][0][cl] = m;
+        red[wm][1][cl] = s;
+        red[wm][2][cl] = b;
+      }
+      // target pick: exactly one lane in the grid holds z[t] for this token
+      if (c < rows) {
+        const int tt = P.targets[P.kept_idx[c]];
+        const int local = tt - vbase;
+        const int w = local & 31;
+        const bool hit = local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
+        if (hit) {
+          const int want = (local >> 5) * 16 + ((w >> 3) << 2) + (w & 3);
+          float z = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z = (want == i * 16 + r) ? acc[i][j][r] : z;
+          P.zt[c] = z;
+        }
+      }
+    }
+    __syncthreads();
+    {
+      const int cl = tid;  // one token per thread
+      const int c = tn * kBN + cl;
+      float m = red[0][0][cl], s = red[0][1][cl], b = red[0][2][cl];
+      stat_merge(m, s, b, red[1][0][cl], red[1][1][cl], red[1][2][cl]);
+      if (c < rows) {
+        const int64_t o = (int64_t)tm * P.ldp + c;
+        P.pm[o] = m;
+        P.ps[o] = s;
+        P.pb[o] = b;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the vocab-tile partials, in ascending tile order within each of 4
+// interleaved splits, then splits 0..3 in order. Writes the saved LSE and
+// entropy and scatters log-prob / entropy to the kept rows.
+// ---------------------------------------------------------------------------
+constexpr int kMergeRows = 64;
+
+__global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm,
+                                               const float* __restrict__ ps,
+                                               const float* __restrict__ pb,
+                                               const float* __restrict__ zt, int64_t ldp, int n_vt,
+                                               const int32_t* __restrict__ targets, int V,
+                                               SavedView sv, float* __restrict__ logp,
+                                               float* __restrict__ entropy) {
+  __shared__ float sh[3][4][kMergeRows];
+  const int rows = sv.hdr->n_kept;
+  const int r = threadIdx.x & (kMergeRows - 1);
+  const int split = threadIdx.x / kMergeRows;
+  const int c = blockIdx.x * kMergeRows + r;
+  if (blockIdx.x * kMergeRows >= rows) return;
+  float m = -INFINITY, s = 0.f, b = 0.f;
+  if (c < rows) {
+    for (int vt = split; vt < n_vt; vt += 4) {
+      const int64_t o = (int64_t)vt * ldp + c;
+      stat_merge(m, s, b, pm[o], ps[o], pb[o]);
+    }
+  }
+  sh[0][split][r] = m;
+  sh[1][split][r] = s;
+  sh[2][split][r] = b;
+  __syncthreads();
+  if (split == 0 && c < rows) {
+    for (int k = 1; k < 4; ++k) stat_merge(m, s, b, sh[0][k][r], sh[1][k][r], sh[2][k][r]);
+    const float l2s = log2f(s);
+    const float lse = (m + l2s) * kLn2;
+    const float ent = (l2s - b / s) * kLn2;
+    const int row = sv.kept_idx[c];
+    const int t = targets[row];
+    const float lp = (t >= 0 && t < V) ? zt[c] - lse : __builtin_nanf("");
+    sv.lse[c] = lse;
+    sv.ent[c] = ent;
+    logp[row] = lp;
+    if (entropy) entropy[row] = ent;
+  }
+}
+
+__global__ void k_zero_skipped(const int32_t* __restrict__ pos, int N, float* __restrict__ logp,
+                               float* __restrict__ entropy) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < N && pos[i] < 0) {
+    logp[i] = 0.f;
+    if (entropy) entropy[i] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward kernels.
+// ---------------------------------------------------------------------------
+__global__ void k_zero_rows(const int32_t* __restrict__ pos, int N, int H, float* __restrict__ dX) {
+  const int i = blockIdx.x;
+  if (i >= N || pos[i] >= 0) return;
+  float4* row = reinterpret_cast<float4*>(dX + (int64_t)i * H);
+  for (int k = threadIdx.x; k < H / 4; k += blockDim.x) row[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__global__ void k_gather(const uint16_t* __restrict__ X, const SavedHeader* __restrict__ hdr,
+                         const int32_t* __restrict__ kept_idx, int H, uint16_t* __restrict__ Xc) {
+  const int c = blockIdx.x;
+  if (c >= hdr->n_kept) return;
+  const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)kept_idx[c] * H);
+  uint4* dst = reinterpret_cast<uint4*>(Xc + (int64_t)c * H);
+  for (int k = threadIdx.x; k < H / 8; k += blockDim.x) dst[k] = src[k];
+}
+
+struct DzParams {
+  const uint16_t* W;
+  const uint16_t* X;
+  const int32_t* targets;
+  const float* g_lp;
+  const float* g_h;  // null when the entropy term is off
+  SavedView sv;
+  int H, V, n_vt;
+  int c0, C;  // chunk start (compact rows) and capacity
+  int64_t ldz;
+  uint16_t* dZ;  // [C, ldz] bf16
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  // round to nearest even (values are finite)
+  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+  a = (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;
+  b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+  return a | b;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
+  __shared__ uint4 lds_a[2 * kStageChunks];
+  __shared__ uint4 lds_b[2 * kStageChunks];
+
+  const int n_kept = P.sv.hdr->n_kept;
+  const int rows = min(P.C, n_kept - P.c0);
+  if (rows <= 0) return;
+  const int mt = P.n_vt;
+  const int nt = (rows + kBN - 1) / kBN;
+  const int ntiles = mt * nt;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nk = P.H / kBK;
+  const int32_t* kidx = P.sv.kept_idx + P.c0;
+
+  for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
+    const int t = xcd_logical(round, gridDim.x);
+    if (t >= ntiles) continue;
+    int tm, tn;
+    tile_coords(t, mt, nt, tm, tn);
+
+    KMajorStager sa;
+    KMajorStager sb;
+    sa.init(P.W, P.H, nullptr, tm * kBM, P.V, tid);
+    sb.init(P.X, P.H, kidx, tn * kBN, rows, tid);
+    f32x16_t acc[4][4];
+    mainloop(sa, sb, nk, lds_a, lds_b, acc);
+
+    const int vbase = tm * kBM + wm * 128;
+    const bool full = vbase + 128 <= P.V;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = tn * kBN + wn * 128 + j * 32 + (lane & 31);  // chunk row
+      if (c >= rows) continue;
+      const int cc = P.c0 + c;
+      const int row = kidx[c];
+      const float lse = P.sv.lse[cc];
+      const float glp = P.g_lp[row];
+      const int tt = P.targets[row];
+      // dz = -p * (glp + gh * (lp + ent)) = p * (ca + cb * lp), lp = z - lse
+      float ca = -glp, cb = 0.f;
+      if (P.g_h) {
+        const float gh = P.g_h[row];
+        ca = -(glp + gh * P.sv.ent[cc]);
+        cb = -gh;
+      }
+      const float nl2 = -lse * kLog2e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float z = acc[i][j][r];
+          const float p = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, nl2));
+          const float lp = z - lse;
+          float d = p * fmaf(cb, lp, ca);
+          const bool ok = full || (vbase + acc_row(i, r, lane) < P.V);
+          acc[i][j][r] = ok ? d : 0.f;
+        }
+      const int local = tt - vbase;
+      const int w = local & 31;
+      const bool hit = local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
+      if (hit) {
+        const int want = (local >> 5) * 16 + ((w >> 3) << 2) + (w & 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (want == i * 16 + r) acc[i][j][r] += glp;
+      }
+      uint16_t* drow = P.dZ + (int64_t)c * P.ldz;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int v0 = vbase + i * 32 + 8 * g + 4 * (lane >> 5);
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+          pk.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *reinterpret_cast<uint2*>(drow + v0) = pk;
+        }
+    }
+  }
+}
+
+struct DxParams {
+  const uint16_t* dZ;  // [C, ldz]
+  const uint16_t* W;   // [V, H]
+  SavedView sv;
+  int H, V;
+  int c0, C;
+  int64_t ldz;
+  int kpad;  // K extent: V rounded up to 64 (dZ pad columns are zero)
+  float* dX;
+};
+
+__global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
+  __shared__ uint4 lds_a[2 * kStageChunks];
+  __shared__ uint4 lds_b[2 * kStageChunks];
+
+  const int n_kept = P.sv.hdr->n_kept;
+  const int rows = min(P.C, n_kept - P.c0);
+  if (rows <= 0) return;
+  const int mt = (rows + kBM - 1) / kBM;
+  const int nt = (P.H + kBN - 1) / kBN;
+  const int ntiles = mt * nt;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nk = P.kpad / kBK;
+  const int32_t* kidx = P.sv.kept_idx + P.c0;
+
+  for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
+    const int t = xcd_logical(round, gridDim.x);
+    if (t >= ntiles) continue;
+    int tm, tn;
+    tile_coords(t, mt, nt, tm, tn);
+
+    KMajorStager sa;   // dZ rows (chunk tokens), k = vocab
+    MNMajorStager sb;  // W: element (k = v, n = h) at W[v * H + h]
+    sa.init(P.dZ, P.ldz, nullptr, tm * kBM, rows, tid);
+    sb.init(P.W, P.H, P.V, tn * kBN, P.H, tid);
+    f32x16_t acc[4][4];
+    mainloop(sa, sb, nk, lds_a, lds_b, acc);
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = tm * kBM + wm * 128 + acc_row(i, r, lane);
+        if (m >= rows) continue;
+        float* drow = P.dX + (int64_t)kidx[m] * P.H;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = tn * kBN + wn * 128 + j * 32 + (lane & 31);
+          if (n < P.H) drow[n] = acc[i][j][r];
+        }
+      }
+  }
+}
+
+struct DwParams {
+  const uint16_t* dZ;  // [C, ldz]: element (k = c, m = v) at dZ[c * ldz + v]
+  const uint16_t* Xc;  // [n_kept, H] gathered rows: element (k = c, n = h)
+  const SavedHeader* hdr;
+  int H, V;
+  int c0, C;
+  int64_t ldz;
+  int accumulate;
+  float* dW;
+};
+
+__global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
+  __shared__ uint4 lds_a[2 * kStageChunks];
+  __shared__ uint4 lds_b[2 * kStageChunks];
+
+  const int n_kept = P.hdr->n_kept;
+  int rows = min(P.C, n_kept - P.c0);
+  if (rows <= 0) {
+    if (P.accumulate) return;  // nothing to add
+    rows = 0;                  // first chunk with no kept rows: write zeros
+  }
+  const int mt = (P.V + kBM - 1) / kBM;
+  const int nt = (P.H + kBN - 1) / kBN;
+  const int ntiles = mt * nt;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nk = (rows + kBK - 1) / kBK;
+  const uint16_t* xc = P.Xc + (int64_t)P.c0 * P.H;
+
+  for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
+    const int t = xcd_logical(round, gridDim.x);
+    if (t >= ntiles) continue;
+    int tm, tn;
+    tile_coords(t, mt, nt, tm, tn);
+
+    MNMajorStager sa;  // dZ^T: k = chunk row, m = vocab
+    MNMajorStager sb;  // X_c: k = chunk row, n = hidden
+    sa.init(P.dZ, P.ldz, rows, tm * kBM, (int)P.ldz, tid);
+    sb.init(xc, P.H, rows, tn * kBN, P.H, tid);
+    f32x16_t acc[4][4];
+    mainloop(sa, sb, nk, lds_a, lds_b, acc);
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = tm * kBM + wm * 128 + acc_row(i, r, lane);
+        if (m >= P.V) continue;
+        float* wrow = P.dW + (int64_t)m * P.H;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = tn * kBN + wn * 128 + j * 32 + (lane & 31);
+          if (n < P.H) {
+            float v = acc[i][j][r];
+            if (P.accumulate) v += wrow[n];
+            wrow[n] = v;
+          }
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+static int g_cu_count[64];
+
+static int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = g_cu_count[dev];
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_cu_count[dev] = n;
+  }
+  return n;
+}
+
+// Persistent grid: at most one workgroup per CU, a multiple of the XCD count.
+static int persistent_grid(int64_t max_tiles) {
+  int64_t g = cu_count();
+  g = g / kXcds * kXcds;
+  if (g < kXcds) g = kXcds;
+  int64_t need = (max_tiles + kXcds - 1) / kXcds * kXcds;
+  if (need < kXcds) need = kXcds;
+  return (int)(need < g ? need : g);
+}
+
+static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+static int check_sizes(int64_t N, int64_t H, int64_t V) {
+  if (N < 0 || H <= 0 || V <= 0) return LMHEAD_ERR_INVALID_ARG;
+  if (H % 64 != 0) return LMHEAD_ERR_UNSUPPORTED;
+  // int32 indexing of rows, columns and per-tile partial offsets
+  if (N > INT32_MAX / 4 || H > (1 << 20) || V > (INT32_MAX / 4)) return LMHEAD_ERR_UNSUPPORTED;
+  return LMHEAD_OK;
+}
+
+#define LMH_LAUNCH_CHECK()                                   \
+  do {                                                       \
+    if (hipGetLastError() != hipSuccess) return LMHEAD_ERR_HIP; \
+  } while (0)
+
+}  // namespace lmh
+
+using namespace lmh;
+
+LMH_API size_t lmhead_saved_bytes(int64_t N) {
+  if (N < 0) return 0;
+  return saved_bytes_for(N);
+}
+
+LMH_API size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V) {
+  if (check_sizes(N, H, V) != LMHEAD_OK) return 0;
+  return fwd_ws_bytes(N, V);
+}
+
+LMH_API size_t lmhead_bwd_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
+  if (check_sizes(N, H, V) != LMHEAD_OK) return 0;
+  return bwd_ws_bytes(N, H, V, token_chunk);
+}
+
+LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
+                       const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V,
+                       int return_entropy, int entropy_requires_grad, float* logp, float* entropy,
+                       void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int st = check_sizes(N, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!saved) return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (!hidden || !weight || !targets || !logp)) return LMHEAD_ERR_INVALID_ARG;
+  if (!weight) return LMHEAD_ERR_INVALID_ARG;
+  if ((return_entropy != 0) != (entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
+  if (entropy_requires_grad && !return_entropy) return LMHEAD_ERR_INVALID_ARG;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace))
+    return LMHEAD_ERR_INVALID_ARG;
+  if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
+  const size_t ws_need = fwd_ws_bytes(N, V);
+  if (workspace_bytes < ws_need || (ws_need > 0 && !workspace)) return LMHEAD_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SavedView sv = saved_view(saved, N);
+  const int flags = (return_entropy ? 1 : 0) | (entropy_requires_grad ? 2 : 0);
+
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, keep_mask, targets, (int)N,
+                     (int)H, (int)V, flags, sv.kept_idx, sv.pos, sv.hdr);
+  LMH_LAUNCH_CHECK();
+  if (N == 0) return LMHEAD_OK;
+
+  const int nv = n_vtiles(V);
+  char* w = static_cast<char*>(workspace);
+  FwdParams P;
+  P.W = static_cast<const uint16_t*>(weight);
+  P.X = static_cast<const uint16_t*>(hidden);
+  P.targets = targets;
+  P.kept_idx = sv.kept_idx;
+  P.hdr = sv.hdr;
+  P.H = (int)H;
+  P.V = (int)V;
+  P.n_vt = nv;
+  P.ldp = N;
+  P.zt = reinterpret_cast<float*>(w);
+  const size_t a = align256((size_t)N * 4);
+  const size_t pa = align256((size_t)nv * (size_t)N * 4);
+  P.pm = reinterpret_cast<float*>(w + a);
+  P.ps = reinterpret_cast<float*>(w + a + pa);
+  P.pb = reinterpret_cast<float*>(w + a + 2 * pa);
+  const int64_t max_tiles = (int64_t)nv * ((N + kBN - 1) / kBN);
+  hipLaunchKernelGGL(k_fwd_tiles, dim3(persistent_grid(max_tiles)), dim3(kThreads), 0, s, P);
+  LMH_LAUNCH_CHECK();
+
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)((N + kMergeRows - 1) / kMergeRows)), dim3(256), 0, s,
+                     P.pm, P.ps, P.pb, P.zt, (int64_t)N, nv, targets, (int)V, sv, logp, entropy);
+  LMH_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_zero_skipped, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, sv.pos,
+                     (int)N, logp, entropy);
+  LMH_LAUNCH_CHECK();
+  return LMHEAD_OK;
+}
+
+LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* targets, int64_t N,
+                       int64_t H, int64_t V, int entropy_requires_grad, const void* saved,
+                       size_t saved_bytes, const float* grad_logp, const float* grad_entropy,
+                       float* grad_hidden, float* grad_weight, int64_t token_chunk,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_sizes(N, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (!saved || !weight || !grad_weight) return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (!hidden || !targets || !grad_logp || !grad_hidden)) return LMHEAD_ERR_INVALID_ARG;
+  if ((entropy_requires_grad != 0) != (grad_entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace) ||
+      !aligned16(grad_hidden) || !aligned16(grad_weight))
+    return LMHEAD_ERR_INVALID_ARG;
+  if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
+  const size_t ws_need = bwd_ws_bytes(N, H, V, token_chunk);
+  if (workspace_bytes < ws_need || (ws_need > 0 && !workspace)) return LMHEAD_ERR_WORKSPACE;
+  const int64_t C = chunk_rows(N, token_chunk);
+  const int64_t ldz = dz_ld(V);
+  if (C * ldz > ((int64_t)1 << 40)) return LMHEAD_ERR_UNSUPPORTED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SavedView sv = saved_view(const_cast<void*>(saved), N);
+  char* w = static_cast<char*>(workspace);
+  uint16_t* Xc = reinterpret_cast<uint16_t*>(w);
+  uint16_t* dZ = reinterpret_cast<uint16_t*>(w + align256((size_t)N * (size_t)H * 2));
+
+  if (N > 0) {
+    hipLaunchKernelGGL(k_zero_rows, dim3((unsigned)N), dim3(256), 0, s, sv.pos, (int)N, (int)H,
+                       grad_hidden);
+    LMH_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_gather, dim3((unsigned)N), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(hidden), sv.hdr, sv.kept_idx, (int)H, Xc);
+    LMH_LAUNCH_CHECK();
+  }
+
+  const int nv = n_vtiles(V);
+  const int64_t nchunks = N > 0 ? (N + C - 1) / C : 1;
+  for (int64_t ch = 0; ch < nchunks; ++ch) {
+    const int c0 = (int)(ch * C);
+    if (N > 0) {
+      DzParams D;
+      D.W = static_cast<const uint16_t*>(weight);
+      D.X = static_cast<const uint16_t*>(hidden);
+      D.targets = targets;
+      D.g_lp = grad_logp;
+      D.g_h = entropy_requires_grad ? grad_entropy : nullptr;
+      D.sv = sv;
+      D.H = (int)H;
+      D.V = (int)V;
+      D.n_vt = nv;
+      D.c0 = c0;
+      D.C = (int)C;
+      D.ldz = ldz;
+      D.dZ = dZ;
+      const int64_t dz_tiles = (int64_t)nv * ((C + kBN - 1) / kBN);
+      hipLaunchKernelGGL(k_dz_tiles, dim3(persistent_grid(dz_tiles)), dim3(kThreads), 0, s, D);
+      LMH_LAUNCH_CHECK();
+
+      DxParams X;
+      X.dZ = dZ;
+      X.W = static_cast<const uint16_t*>(weight);
+      X.sv = sv;
+      X.H = (int)H;
+      X.V = (int)V;
+      X.c0 = c0;
+      X.C = (int)C;
+      X.ldz = ldz;
+      X.kpad = (int)((V + 63) / 64 * 64);
+      X.dX = grad_hidden;
+      const int64_t dx_tiles = ((C + kBM - 1) / kBM) * ((H + kBN - 1) / kBN);
+      hipLaunchKernelGGL(k_dx_tiles, dim3(persistent_grid(dx_tiles)), dim3(kThreads), 0, s, X);
+      LMH_LAUNCH_CHECK();
+    }
+    DwParams Wp;
+    Wp.dZ = dZ;
+    Wp.Xc = Xc;
+    Wp.hdr = sv.hdr;
+    Wp.H = (int)H;
+    Wp.V = (int)V;
+    Wp.c0 = c0;
+    Wp.C = (int)C;
+    Wp.ldz = ldz;
+    Wp.accumulate = ch > 0;
+    Wp.dW = grad_weight;
+    const int64_t dw_tiles = (int64_t)nv * ((H + kBN - 1) / kBN);
+    hipLaunchKernelGGL(k_dw_tiles, dim3(persistent_grid(dw_tiles)), dim3(kThreads), 0, s, Wp);
+    LMH_LAUNCH_CHECK();
+  }
+  return LMHEAD_OK;
+}
+
+LMH_API int lmhead_read_n_kept(const void* saved, int64_t* n_kept_host, void* stream) {
+  if (!saved || !n_kept_host) return LMHEAD_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, saved, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return LMHEAD_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return LMHEAD_ERR_HIP;
+  *n_kept_host = v;
+  return LMHEAD_OK;
+}
+
+LMH_API int lmhead_check_status(const void* saved, void* stream) {
+  if (!saved) return LMHEAD_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SavedHeader h;
+  if (hipMemcpyAsync(&h, saved, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return LMHEAD_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return LMHEAD_ERR_HIP;
+  return h.status;
+}
+
+LMH_API const char* lmhead_status_string(int status) {
+  switch (status) {
+    case LMHEAD_OK: return "ok";
+    case LMHEAD_ERR_INVALID_ARG: return "invalid argument";
+    case LMHEAD_ERR_UNSUPPORTED: return "unsupported size (H must be a positive multiple of 64)";
+    case LMHEAD_ERR_WORKSPACE: return "saved or workspace buffer too small";
+    case LMHEAD_ERR_HIP: return "HIP runtime error";
+    case LMHEAD_ERR_TARGET_RANGE: return "a kept row's target is outside [0, V)";
+    default: return "unknown status";
+  }
+}
+
+LMH_API int lmhead_version(void) { return kVersion; }

@@ -1,0 +1,183 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, sizes its buffers as documented, and rejects bad arguments on the host
+before anything is enqueued. No GPU is needed: every call below fails
+validation (or is a pure size query) and never reaches the HIP runtime."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmhead.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from lm_head_log_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from lm_head_log_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lmhead_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_signatures():
+    from lm_head_log_amd import _lib
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_names_match_c_names():
+    import lm_head_log_amd as m
+    for name in declared_functions():
+        assert callable(getattr(m, name)), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.lmhead_version() >= 100
+    for s in range(6):
+        assert lib.lmhead_status_string(s)
+    assert b"unknown" in lib.lmhead_status_string(99)
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+def test_saved_bytes_is_16_bytes_per_row_plus_header(lib):
+    assert lib.lmhead_saved_bytes(-1) == 0
+    assert lib.lmhead_saved_bytes(0) == 1024
+    for N in (1, 100, 16384, 262144):
+        assert lib.lmhead_saved_bytes(N) == 1024 + 4 * _align(4 * N)
+
+
+def test_saved_state_is_far_below_one_full_vocab_activation(lib):
+    """twinkle PR #283, Experiment results: at N=16384, V=151936 one full-vocab
+    activation is 4.6 GiB (bf16). The saved state is per row, never per logit."""
+    g = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "pages_figures.txt")):
+        line = line.split("#", 1)[0]
+        if "=" in line:
+            k, v = line.split("=", 1)
+            g[k.strip()] = float(v.split()[0])
+    N, V = int(g["twinkle_N"]), int(g["twinkle_V"])
+    full_bf16 = N * V * 2
+    assert abs(full_bf16 / 2 ** 30 - g["twinkle_full_vocab_bf16_gib"]) < 0.05
+    assert abs(2 * full_bf16 / 2 ** 30 - g["twinkle_full_vocab_fp32_gib"]) < 0.05
+    assert lib.lmhead_saved_bytes(N) < full_bf16 / 10000
+
+
+def test_workspace_sizes(lib):
+    N, H, V = 16384, 4096, 131072
+    nv = V // 256
+    assert lib.lmhead_fwd_workspace_bytes(N, H, V) == _align(4 * N) + 3 * _align(nv * N * 4)
+    # default chunk 8192 rows of bf16 dZ, plus the gathered kept rows
+    assert lib.lmhead_bwd_workspace_bytes(N, H, V, 0) == _align(N * H * 2) + _align(8192 * V * 2)
+    assert lib.lmhead_bwd_workspace_bytes(N, H, V, 100) == _align(N * H * 2) + _align(100 * V * 2)
+    # V not a multiple of 256: dZ rows are padded to 256 columns
+    assert lib.lmhead_bwd_workspace_bytes(10, 64, 1000, 0) == _align(10 * 64 * 2) + _align(10 * 1024 * 2)
+    # invalid sizes
+    assert lib.lmhead_fwd_workspace_bytes(10, 100, 1000) == 0
+    assert lib.lmhead_fwd_workspace_bytes(-1, 64, 1000) == 0
+    assert lib.lmhead_bwd_workspace_bytes(10, 64, 0, 0) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)   # 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p(0x10002)
+
+
+def _fwd(lib, **kw):
+    a = dict(hidden=FAKE, weight=FAKE, targets=FAKE, keep=None, N=8, H=64, V=100,
+             ret=1, erg=1, logp=FAKE, ent=FAKE, saved=FAKE, saved_bytes=1 << 20,
+             ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.lmhead_fwd(a["hidden"], a["weight"], a["targets"], a["keep"], a["N"], a["H"],
+                          a["V"], a["ret"], a["erg"], a["logp"], a["ent"], a["saved"],
+                          a["saved_bytes"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _bwd(lib, **kw):
+    a = dict(hidden=FAKE, weight=FAKE, targets=FAKE, N=8, H=64, V=100, erg=1, saved=FAKE,
+             saved_bytes=1 << 20, glp=FAKE, gh=FAKE, gX=FAKE, gW=FAKE, chunk=0, ws=FAKE,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.lmhead_bwd(a["hidden"], a["weight"], a["targets"], a["N"], a["H"], a["V"],
+                          a["erg"], a["saved"], a["saved_bytes"], a["glp"], a["gh"], a["gX"],
+                          a["gW"], a["chunk"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), 1),
+    (dict(V=0), 1),
+    (dict(H=0), 1),
+    (dict(H=100), 2),
+    (dict(H=32), 2),
+    (dict(hidden=None), 1),
+    (dict(weight=None), 1),
+    (dict(targets=None), 1),
+    (dict(logp=None), 1),
+    (dict(saved=None), 1),
+    (dict(ent=None), 1),              # return_entropy without an entropy buffer
+    (dict(ret=0), 1),                 # entropy buffer without return_entropy
+    (dict(ret=0, ent=None), 1),       # entropy_requires_grad without return_entropy
+    (dict(hidden=ODD), 1),            # misaligned
+    (dict(saved_bytes=100), 3),
+    (dict(ws_bytes=10), 3),
+    (dict(ws=None), 3),
+])
+def test_fwd_host_validation(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-5), 1),
+    (dict(H=96), 2),
+    (dict(saved=None), 1),
+    (dict(gW=None), 1),
+    (dict(gX=None), 1),
+    (dict(glp=None), 1),
+    (dict(gh=None), 1),               # entropy grad requested without its upstream grad
+    (dict(erg=0), 1),                 # upstream entropy grad without the flag
+    (dict(gX=ODD), 1),
+    (dict(saved_bytes=8), 3),
+    (dict(ws_bytes=0), 3),
+    (dict(chunk=4, ws_bytes=10), 3),
+])
+def test_bwd_host_validation(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+
+
+def test_sync_calls_reject_null(lib):
+    n = ctypes.c_int64(0)
+    assert lib.lmhead_read_n_kept(None, ctypes.byref(n), None) == 1
+    assert lib.lmhead_read_n_kept(FAKE, None, None) == 1
+    assert lib.lmhead_check_status(None, None) == 1
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    from lm_head_log_amd import _lib
+    with pytest.raises(ImportError):
+        _lib.load(str(tmp_path / "nope.so"))
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import lm_head_log_amd as m
+    h = torch.zeros(4, 64, dtype=torch.bfloat16)
+    w = torch.zeros(10, 64, dtype=torch.bfloat16)
+    t = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        m.lmhead_fwd(h, w, t)
+    with pytest.raises(TypeError):
+        m.lmhead_fwd(h.float(), w, t)

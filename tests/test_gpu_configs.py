@@ -1,0 +1,86 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (default token chunk, persistent grids over the whole batch).
+
+Rows are independent in the forward and in dX, so a seeded sample of kept rows
+is checked against the oracle row by row; dW is checked by a second GPU call
+whose keep mask selects exactly the sampled rows, which the oracle can compute.
+Properties that hold at any size (kept positions, +0.0 at skipped rows, the
+log-prob / entropy bounds) are checked over every row.
+"""
+
+import gc
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests.gpu_helpers import (TOL_ENT, TOL_GRAD_REL, TOL_LOGP, assert_pos_zero, rel_fro,
+                               run, say)
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = 512
+
+
+def _full_check(w, sample_seed, backward=True):
+    g = run(w, backward=backward)
+    kept = w.kept_rows()
+    np.testing.assert_array_equal(g["kept_idx"], kept)
+    assert g["status"] == 0
+    skipped = np.setdiff1d(np.arange(w.N), kept)
+    assert_pos_zero(g["logp"][skipped], "logp skipped")
+    assert_pos_zero(g["entropy"][skipped], "entropy skipped")
+    # bounds over every kept row: logp <= 0, 0 <= entropy <= ln V
+    assert np.all(g["logp"][kept] <= 1e-5)
+    assert np.all(g["entropy"][kept] >= -1e-5)
+    assert np.all(g["entropy"][kept] <= math.log(w.V) + 1e-5)
+    if backward:
+        assert_pos_zero(g["dX"][skipped], "dX skipped")
+    rows = wl.sample_rows(kept, SAMPLE, sample_seed)
+    W64 = oracle.bf16_to_f64(w.weight)
+    ref = oracle.rows_fwd_bwd(w.hidden, w.weight, w.targets, rows, w.g_logp, w.g_entropy,
+                              w.entropy_requires_grad, W64=W64, want_dw=backward)
+    e_lp = np.abs(g["logp"][rows] - ref["logp"]).max()
+    e_h = np.abs(g["entropy"][rows] - ref["entropy"]).max()
+    say(f"{w.name}: logp err {e_lp:.3e} entropy err {e_h:.3e}")
+    assert e_lp <= TOL_LOGP and e_h <= TOL_ENT
+    if backward:
+        ex = rel_fro(g["dX"][rows], ref["dX"])
+        say(f"{w.name}: dX rel err {ex:.3e}")
+        assert ex <= TOL_GRAD_REL
+        del g
+        gc.collect()
+        g2 = run(w, keep=wl.row_mask(w.N, rows))
+        ew = rel_fro(g2["dW"], ref["dW"])
+        # the same rows give the same dX whether or not other rows are kept
+        ex2 = rel_fro(g2["dX"][rows], ref["dX"])
+        say(f"{w.name}: dW rel err {ew:.3e} (sampled-rows call), dX {ex2:.3e}")
+        assert ew <= TOL_GRAD_REL and ex2 <= TOL_GRAD_REL
+        # column sums of dW vanish (each dZ row sums to zero), up to bf16 dZ rounding
+        colsum = np.abs(g2["dW"].astype(np.float64).sum(axis=0)).max()
+        assert colsum <= 1e-2 * np.linalg.norm(g2["dW"])
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("frac", [1.0, 0.23])
+def test_config2_dense_rl(frac):
+    say(f"case: config2 N16384 H4096 V131072 keep {frac}")
+    _full_check(wl.config2(frac), 2)
+
+
+def test_config3_packed_grpo():
+    say("case: config3 packed GRPO N16384 H4096 V151936 (metric-only entropy)")
+    _full_check(wl.config3(), 3)
+
+
+def test_config4_fp32_stress():
+    say("case: config4 fp32 stress N16384 H2560 V151936")
+    _full_check(wl.config4(), 4)
+
+
+def test_config5_scoring_forward():
+    say("case: config5 scoring N262144 H5120 V152064 forward only")
+    _full_check(wl.config5(), 5, backward=False)
