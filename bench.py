@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused LM-head op: forward + backward tokens/s and TFLOP/s
+(% of the bf16 dense MFMA peak) at the dense RL shape N=16384, H=4096,
+V=131072 (SkyRL PR #2374, Performance), differentiable entropy, every row kept.
+
+One step = lmhead_fwd + lmhead_bwd over one synthetic batch whose inputs are
+already resident in HBM; every buffer is preallocated. Prints ONE JSON line on
+stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--keep 1.0]
+                    [--config 2] [--token-chunk 0] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+KERNELS_GEMM = ("fwd_tiles", "dz_tiles", "dx_tiles", "dw_tiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_workload(cfg: int, keep: float):
+    import workloads as wl
+    if cfg == 1:
+        return wl.config1()
+    if cfg == 2:
+        return wl.config2(keep)
+    return wl.CONFIGS[cfg]()
+
+
+def cpu_baseline(w, rows_n: int):
+    """The oracle, as it stands, on a bounded sample of kept rows of the same
+    batch (forward + backward including those rows' dW)."""
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rows = wl.sample_rows(w.kept_rows(), rows_n, 99)
+    t0 = time.perf_counter()
+    oracle.rows_fwd_bwd(w.hidden, w.weight, w.targets, rows, w.g_logp, w.g_entropy,
+                        w.entropy_requires_grad, want_dw=w.backward)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(len(rows) / dt, 3),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(rows)} kept rows of the same batch, float64 numpy, "
+                   f"forward{' + backward incl. dW' if w.backward else ''}, "
+                   f"{dt:.1f} s including the bf16 weight decode"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--keep", type=float, default=1.0)
+    ap.add_argument("--token-chunk", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=128)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the op shards by rows or vocabulary, but no multi-GPU path is built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lm_head_log_amd as lmh
+    from lm_head_log_amd import _lib
+    _lib.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    w = make_workload(args.config, args.keep)
+    log(f"workload {w.name} generated in {time.time() - t0:.1f}s")
+    N, H, V = w.N, w.H, w.V
+    X = torch.from_numpy(w.hidden.view(np.int16)).view(torch.bfloat16).to(dev)
+    W = torch.from_numpy(w.weight.view(np.int16)).view(torch.bfloat16).to(dev)
+    t = torch.from_numpy(w.targets).to(dev)
+    km = None if w.keep is None else torch.from_numpy(w.keep).to(dev)
+    glp = torch.from_numpy(w.g_logp).to(dev)
+    erg = w.entropy_requires_grad
+    gh = torch.from_numpy(w.g_entropy).to(dev) if erg else None
+    ret = w.return_entropy
+    n_kept = int(w.keep.sum()) if w.keep is not None else N
+
+    logp = torch.empty(N, dtype=torch.float32, device=dev)
+    ent = torch.empty(N, dtype=torch.float32, device=dev) if ret else None
+    saved = torch.empty(lmh.lmhead_saved_bytes(N), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(max(1, lmh.lmhead_fwd_workspace_bytes(N, H, V)), dtype=torch.uint8,
+                       device=dev)
+    do_bwd = w.backward
+    if do_bwd:
+        ws_b = torch.empty(max(1, lmh.lmhead_bwd_workspace_bytes(N, H, V, args.token_chunk)),
+                           dtype=torch.uint8, device=dev)
+        gX = torch.empty(N, H, dtype=torch.float32, device=dev)
+        gW = torch.empty(V, H, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        lmh.lmhead_fwd(X, W, t, km, ret, erg, logp=logp, entropy=ent, saved=saved,
+                       workspace=ws_f, stream=stream)
+        if do_bwd:
+            lmh.lmhead_bwd(X, W, t, saved, glp, gh, erg, args.token_chunk, grad_hidden=gX,
+                           grad_weight=gW, workspace=ws_b, stream=stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    assert lmh.lmhead_read_n_kept(saved) == n_kept
+
+    torch.cuda.synchronize()
+    lmh.lmhead_profile_begin()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    prof = lmh.lmhead_profile_end()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step")
+
+    fl_gemm = 2.0 * n_kept * H * V  # one logit-sized contraction over kept rows
+    n_gemm = 4 if do_bwd else 1
+    flops_step = n_gemm * fl_gemm
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    kern = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
+            for k, v in prof.items() if v[1] > 0}
+    for k, v in kern.items():
+        log(f"  kernel {k:13s} {v['ms_per_step']:9.3f} ms/step  "
+            f"({v['launches_per_step']:.0f} launches)")
+    dom = max((k for k in kern if k in KERNELS_GEMM), key=lambda k: kern[k]["ms_per_step"])
+    dom_ms = kern[dom]["ms_per_step"]
+    achieved = fl_gemm / (dom_ms * 1e-3) / 1e12
+    for k in KERNELS_GEMM:
+        if k in kern:
+            kern[k]["tflops"] = round(fl_gemm / (kern[k]["ms_per_step"] * 1e-3) / 1e12, 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, args.cpu_rows)
+        log(f"cpu baseline {cpu}")
+
+    out = {
+        "metric": "fused LM-head fwd+bwd tokens/s & TFLOP/s (% bf16 MFMA peak), H4096 V131072",
+        "value": round(N / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name + (" fwd+bwd" if do_bwd else " fwd"),
+            "N": N, "H": H, "V": V, "n_kept": n_kept,
+            "keep_fraction": round(n_kept / max(N, 1), 4),
+            "return_entropy": bool(ret), "entropy_requires_grad": bool(erg),
+            "token_chunk": args.token_chunk or 8192,
+        },
+        "tflops": round(tflops, 1),
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "kept_tokens_per_s": round(n_kept / (ms_step * 1e-3), 1),
+        "flops_per_step": flops_step,
+        "kernels": kern,
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

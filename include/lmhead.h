@@ -100,6 +100,7 @@ size_t lmhead_bwd_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t token
  *  keep_mask  uint8 [N], nonzero = keep; NULL = keep every row
  *  logp       fp32 [N] out, fully written (+0.0 at skipped rows)
  *  entropy    fp32 [N] out, fully written; must be NULL iff !return_entropy
+ *             (not checked when N == 0, where any output may be NULL)
  *  entropy_requires_grad  requires return_entropy (else INVALID_ARG); it is
  *             recorded in `saved` and selects the backward's entropy term.
  *  saved      device buffer of >= lmhead_saved_bytes(N) bytes, out
@@ -124,7 +125,7 @@ int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
  *  entropy_requires_grad: as passed to lmhead_fwd
  *  saved      the buffer lmhead_fwd filled, unmodified
  *  grad_logp  fp32 [N]; skipped rows are not read
- *  grad_entropy fp32 [N]; must be NULL iff !entropy_requires_grad
+ *  grad_entropy fp32 [N]; must be NULL iff !entropy_requires_grad (N > 0)
  *  grad_hidden fp32 [N, H] out, fully overwritten (+0.0 rows where skipped)
  *  grad_weight fp32 [V, H] out, fully overwritten
  *  token_chunk rows per chunk; <= 0 selects 8192
@@ -153,6 +154,25 @@ const char* lmhead_status_string(int status);
 
 /* Library ABI version (major * 10000 + minor * 100 + patch). */
 int lmhead_version(void);
+
+/* Per-kernel timing for benchmarks (not needed to use the op).
+ * Kernel kinds, in order: compact, fwd_tiles, merge, zero_skipped, zero_rows,
+ * gather, dz_tiles, dx_tiles, dw_tiles. */
+#define LMHEAD_NUM_KERNELS 9
+
+/* Static name of kernel kind `kind` (NULL if out of range). */
+const char* lmhead_kernel_name(int kind);
+
+/* While profiling is on, every launch the library makes (from any host thread,
+ * on any stream) is bracketed by a hipEvent pair recorded on the launch
+ * stream. lmhead_profile_begin clears previous records; it creates events but
+ * allocates no device memory. */
+int lmhead_profile_begin(void);
+
+/* Stops recording, waits for the recorded events, and writes per-kind totals:
+ * ms[k] = summed event time of kind k's launches, launches[k] = their count
+ * (arrays of LMHEAD_NUM_KERNELS; either may be NULL). Syncs the events. */
+int lmhead_profile_end(double* ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ __all__ = [
     "lmhead_saved_bytes", "lmhead_fwd_workspace_bytes", "lmhead_bwd_workspace_bytes",
     "lmhead_fwd", "lmhead_bwd", "lmhead_read_n_kept", "lmhead_check_status",
     "lmhead_status_string", "lmhead_version", "fused_logprobs", "LMHeadError",
-    "DEFAULT_TOKEN_CHUNK",
+    "DEFAULT_TOKEN_CHUNK", "lmhead_kernel_name", "lmhead_profile_begin", "lmhead_profile_end",
 ]
 
 DEFAULT_TOKEN_CHUNK = 8192
@@ -170,6 +170,24 @@ def lmhead_read_n_kept(saved, stream=None) -> int:
 
 def lmhead_check_status(saved, stream=None) -> int:
     return int(_L().lmhead_check_status(_ptr(saved), _stream(stream, saved.device)))
+
+
+def lmhead_kernel_name(kind: int):
+    n = _L().lmhead_kernel_name(kind)
+    return None if n is None else n.decode()
+
+
+def lmhead_profile_begin() -> None:
+    check("lmhead_profile_begin", _L().lmhead_profile_begin())
+
+
+def lmhead_profile_end() -> dict:
+    """Per-kernel {name: (total_ms, launches)} recorded since lmhead_profile_begin."""
+    k = _lib.NUM_KERNELS
+    ms = (ctypes.c_double * k)()
+    cnt = (ctypes.c_int64 * k)()
+    check("lmhead_profile_end", _L().lmhead_profile_end(ms, cnt))
+    return {lmhead_kernel_name(i): (float(ms[i]), int(cnt[i])) for i in range(k)}
 
 
 class _FusedLMHead(torch.autograd.Function):

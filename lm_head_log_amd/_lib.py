@@ -26,7 +26,12 @@ SIGNATURES = {
     "lmhead_check_status": (c_int, [c_vp, c_vp]),
     "lmhead_status_string": (ctypes.c_char_p, [c_int]),
     "lmhead_version": (c_int, []),
+    "lmhead_kernel_name": (ctypes.c_char_p, [c_int]),
+    "lmhead_profile_begin": (c_int, []),
+    "lmhead_profile_end": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
 }
+
+NUM_KERNELS = 9
 
 _lib = None
 

@@ -25,6 +25,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "../../include/lmhead.h"
 #include "gemm_core.h"
 
@@ -436,14 +439,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
         ca = -(glp + gh * P.sv.ent[cc]);
         cb = -gh;
       }
-      const float nl2 = -lse * kLog2e;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float z = acc[i][j][r];
-          const float p = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, nl2));
+          // subtract before scaling: z - lse is exact near the row maximum
           const float lp = z - lse;
+          const float p = __builtin_amdgcn_exp2f(lp * kLog2e);
           float d = p * fmaf(cb, lp, ca);
           const bool ok = full || (vbase + acc_row(i, r, lane) < P.V);
           acc[i][j][r] = ok ? d : 0.f;
@@ -633,9 +636,63 @@ static int check_sizes(int64_t N, int64_t H, int64_t V) {
   return LMHEAD_OK;
 }
 
-#define LMH_LAUNCH_CHECK()                                   \
-  do {                                                       \
-    if (hipGetLastError() != hipSuccess) return LMHEAD_ERR_HIP; \
+// Optional per-kernel timing (benchmarks only): hipEvent pairs recorded on
+// the launch stream around every launch while profiling is on.
+enum KernelKind {
+  KK_COMPACT = 0, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS, KK_GATHER, KK_DZ, KK_DX,
+  KK_DW, KK_COUNT
+};
+static const char* const kKernelNames[KK_COUNT] = {
+    "compact", "fwd_tiles", "merge", "zero_skipped", "zero_rows",
+    "gather",  "dz_tiles",  "dx_tiles", "dw_tiles"};
+
+struct ProfRec {
+  hipEvent_t a, b;
+  int kind;
+};
+static std::mutex g_prof_mu;
+static bool g_prof_on = false;
+static std::vector<ProfRec> g_prof_recs;
+static std::vector<hipEvent_t> g_prof_pool;
+
+static hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launches kernel `k` with the given configuration on stream s; returns a
+// lmhead_status. Records timing events when profiling is on.
+template <typename Kern, typename... Args>
+static int launch(int kind, Kern k, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (g_prof_on) {
+      a = prof_event();
+      b = prof_event();
+    }
+  }
+  if (a && b && hipEventRecord(a, s) != hipSuccess) return LMHEAD_ERR_HIP;
+  hipLaunchKernelGGL(k, grid, block, 0, s, args...);
+  if (hipGetLastError() != hipSuccess) return LMHEAD_ERR_HIP;
+  if (a && b) {
+    if (hipEventRecord(b, s) != hipSuccess) return LMHEAD_ERR_HIP;
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof_recs.push_back(ProfRec{a, b, kind});
+  }
+  return LMHEAD_OK;
+}
+
+#define LMH_TRY(expr)                  \
+  do {                                 \
+    const int st_ = (expr);            \
+    if (st_ != LMHEAD_OK) return st_;  \
   } while (0)
 
 }  // namespace lmh
@@ -667,7 +724,8 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
   if (!saved) return LMHEAD_ERR_INVALID_ARG;
   if (N > 0 && (!hidden || !weight || !targets || !logp)) return LMHEAD_ERR_INVALID_ARG;
   if (!weight) return LMHEAD_ERR_INVALID_ARG;
-  if ((return_entropy != 0) != (entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
+  // an empty output may have a NULL address, so presence is only checked for N > 0
+  if (N > 0 && (return_entropy != 0) != (entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
   if (entropy_requires_grad && !return_entropy) return LMHEAD_ERR_INVALID_ARG;
   if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace))
     return LMHEAD_ERR_INVALID_ARG;
@@ -679,9 +737,8 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
   SavedView sv = saved_view(saved, N);
   const int flags = (return_entropy ? 1 : 0) | (entropy_requires_grad ? 2 : 0);
 
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, s, keep_mask, targets, (int)N,
-                     (int)H, (int)V, flags, sv.kept_idx, sv.pos, sv.hdr);
-  LMH_LAUNCH_CHECK();
+  LMH_TRY(launch(KK_COMPACT, k_compact, dim3(1), dim3(kCompactThreads), s, keep_mask, targets,
+                 (int)N, (int)H, (int)V, flags, sv.kept_idx, sv.pos, sv.hdr));
   if (N == 0) return LMHEAD_OK;
 
   const int nv = n_vtiles(V);
@@ -703,15 +760,13 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
   P.ps = reinterpret_cast<float*>(w + a + pa);
   P.pb = reinterpret_cast<float*>(w + a + 2 * pa);
   const int64_t max_tiles = (int64_t)nv * ((N + kBN - 1) / kBN);
-  hipLaunchKernelGGL(k_fwd_tiles, dim3(persistent_grid(max_tiles)), dim3(kThreads), 0, s, P);
-  LMH_LAUNCH_CHECK();
+  LMH_TRY(launch(KK_FWD, k_fwd_tiles, dim3(persistent_grid(max_tiles)), dim3(kThreads), s, P));
 
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)((N + kMergeRows - 1) / kMergeRows)), dim3(256), 0, s,
-                     P.pm, P.ps, P.pb, P.zt, (int64_t)N, nv, targets, (int)V, sv, logp, entropy);
-  LMH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_zero_skipped, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, sv.pos,
-                     (int)N, logp, entropy);
-  LMH_LAUNCH_CHECK();
+  LMH_TRY(launch(KK_MERGE, k_merge, dim3((unsigned)((N + kMergeRows - 1) / kMergeRows)), dim3(256),
+                 s, (const float*)P.pm, (const float*)P.ps, (const float*)P.pb,
+                 (const float*)P.zt, (int64_t)N, nv, targets, (int)V, sv, logp, entropy));
+  LMH_TRY(launch(KK_ZERO_SKIPPED, k_zero_skipped, dim3((unsigned)((N + 255) / 256)), dim3(256), s,
+                 (const int32_t*)sv.pos, (int)N, logp, entropy));
   return LMHEAD_OK;
 }
 
@@ -724,7 +779,8 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
   if (st != LMHEAD_OK) return st;
   if (!saved || !weight || !grad_weight) return LMHEAD_ERR_INVALID_ARG;
   if (N > 0 && (!hidden || !targets || !grad_logp || !grad_hidden)) return LMHEAD_ERR_INVALID_ARG;
-  if ((entropy_requires_grad != 0) != (grad_entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (entropy_requires_grad != 0) != (grad_entropy != nullptr))
+    return LMHEAD_ERR_INVALID_ARG;
   if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace) ||
       !aligned16(grad_hidden) || !aligned16(grad_weight))
     return LMHEAD_ERR_INVALID_ARG;
@@ -742,12 +798,11 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
   uint16_t* dZ = reinterpret_cast<uint16_t*>(w + align256((size_t)N * (size_t)H * 2));
 
   if (N > 0) {
-    hipLaunchKernelGGL(k_zero_rows, dim3((unsigned)N), dim3(256), 0, s, sv.pos, (int)N, (int)H,
-                       grad_hidden);
-    LMH_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_gather, dim3((unsigned)N), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(hidden), sv.hdr, sv.kept_idx, (int)H, Xc);
-    LMH_LAUNCH_CHECK();
+    LMH_TRY(launch(KK_ZERO_ROWS, k_zero_rows, dim3((unsigned)N), dim3(256), s,
+                   (const int32_t*)sv.pos, (int)N, (int)H, grad_hidden));
+    LMH_TRY(launch(KK_GATHER, k_gather, dim3((unsigned)N), dim3(256), s,
+                   static_cast<const uint16_t*>(hidden), (const SavedHeader*)sv.hdr,
+                   (const int32_t*)sv.kept_idx, (int)H, Xc));
   }
 
   const int nv = n_vtiles(V);
@@ -770,8 +825,7 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       D.ldz = ldz;
       D.dZ = dZ;
       const int64_t dz_tiles = (int64_t)nv * ((C + kBN - 1) / kBN);
-      hipLaunchKernelGGL(k_dz_tiles, dim3(persistent_grid(dz_tiles)), dim3(kThreads), 0, s, D);
-      LMH_LAUNCH_CHECK();
+      LMH_TRY(launch(KK_DZ, k_dz_tiles, dim3(persistent_grid(dz_tiles)), dim3(kThreads), s, D));
 
       DxParams X;
       X.dZ = dZ;
@@ -785,8 +839,7 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       X.kpad = (int)((V + 63) / 64 * 64);
       X.dX = grad_hidden;
       const int64_t dx_tiles = ((C + kBM - 1) / kBM) * ((H + kBN - 1) / kBN);
-      hipLaunchKernelGGL(k_dx_tiles, dim3(persistent_grid(dx_tiles)), dim3(kThreads), 0, s, X);
-      LMH_LAUNCH_CHECK();
+      LMH_TRY(launch(KK_DX, k_dx_tiles, dim3(persistent_grid(dx_tiles)), dim3(kThreads), s, X));
     }
     DwParams Wp;
     Wp.dZ = dZ;
@@ -800,8 +853,7 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
     Wp.accumulate = ch > 0;
     Wp.dW = grad_weight;
     const int64_t dw_tiles = (int64_t)nv * ((H + kBN - 1) / kBN);
-    hipLaunchKernelGGL(k_dw_tiles, dim3(persistent_grid(dw_tiles)), dim3(kThreads), 0, s, Wp);
-    LMH_LAUNCH_CHECK();
+    LMH_TRY(launch(KK_DW, k_dw_tiles, dim3(persistent_grid(dw_tiles)), dim3(kThreads), s, Wp));
   }
   return LMHEAD_OK;
 }
@@ -840,3 +892,45 @@ LMH_API const char* lmhead_status_string(int status) {
 }
 
 LMH_API int lmhead_version(void) { return kVersion; }
+
+LMH_API const char* lmhead_kernel_name(int kind) {
+  return (kind >= 0 && kind < KK_COUNT) ? kKernelNames[kind] : nullptr;
+}
+
+static void prof_release_locked() {
+  for (auto& r : g_prof_recs) {
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+}
+
+LMH_API int lmhead_profile_begin(void) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  prof_release_locked();
+  g_prof_on = true;
+  return LMHEAD_OK;
+}
+
+LMH_API int lmhead_profile_end(double* ms, int64_t* launches) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_on = false;
+  double tot[KK_COUNT] = {0};
+  int64_t cnt[KK_COUNT] = {0};
+  int st = LMHEAD_OK;
+  for (auto& r : g_prof_recs) {
+    float e = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&e, r.a, r.b) != hipSuccess) {
+      st = LMHEAD_ERR_HIP;
+      continue;
+    }
+    tot[r.kind] += e;
+    cnt[r.kind] += 1;
+  }
+  prof_release_locked();
+  for (int k = 0; k < KK_COUNT; ++k) {
+    if (ms) ms[k] = tot[k];
+    if (launches) launches[k] = cnt[k];
+  }
+  return st;
+}
