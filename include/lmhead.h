@@ -47,7 +47,8 @@
  *  - Every call returns an lmhead_status. All argument checks run on the host
  *    before anything is enqueued; a failing call enqueues nothing.
  *  - Sizes: N >= 0, V >= 1, H >= 64 with H % 64 == 0 (else
- *    LMHEAD_ERR_UNSUPPORTED). N and V are otherwise arbitrary.
+ *    LMHEAD_ERR_UNSUPPORTED). N and V are otherwise arbitrary up to
+ *    N <= 2^28, V <= 2^22, H <= 2^20.
  *  - Results are bitwise reproducible run to run for the same inputs and
  *    arguments (fixed reduction orders, no floating-point atomics).
  */
@@ -77,15 +78,17 @@ typedef enum {
  * Returns 0 if N < 0. */
 size_t lmhead_saved_bytes(int64_t N);
 
-/* Workspace bytes lmhead_fwd needs for N rows and vocabulary V: per kept row
- * and per 256-wide vocabulary tile, three fp32 partial statistics, plus the
- * target logit. Returns 0 on invalid sizes. */
+/* Workspace bytes lmhead_fwd needs for N rows and vocabulary V: per row the
+ * target logit and, per 256-wide vocabulary tile, three fp32 partial
+ * statistics, plus a bf16 copy of the kept rows of X. Returns 0 on invalid
+ * sizes. */
 size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V);
 
-/* Workspace bytes lmhead_bwd needs: one bf16 dZ buffer of
- * min(token_chunk, N) rows by V rounded up to 256 columns.
- * token_chunk <= 0 selects the default 8192 (prime-rl PR #3326, Overview).
- * Returns 0 on invalid sizes. */
+/* Workspace bytes lmhead_bwd needs: bf16 copies of the kept rows of X (row-
+ * and column-major) and of W^T, plus dZ for one chunk of C rows in both
+ * token-major and vocab-major order, where C = token_chunk rounded up to a
+ * multiple of 256 (at most N rounded up to 256). token_chunk <= 0 selects the
+ * default 8192 (prime-rl PR #3326, Overview). Returns 0 on invalid sizes. */
 size_t lmhead_bwd_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t token_chunk);
 
 /* Forward: compaction of the kept rows, the fused projection with per-row
@@ -128,7 +131,7 @@ int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
  *  grad_entropy fp32 [N]; must be NULL iff !entropy_requires_grad (N > 0)
  *  grad_hidden fp32 [N, H] out, fully overwritten (+0.0 rows where skipped)
  *  grad_weight fp32 [V, H] out, fully overwritten
- *  token_chunk rows per chunk; <= 0 selects 8192
+ *  token_chunk rows per chunk, rounded up to a multiple of 256; <= 0 selects 8192
  *  workspace  >= lmhead_bwd_workspace_bytes(N, H, V, token_chunk) bytes
  */
 int lmhead_bwd(const void* hidden, const void* weight, const int32_t* targets,
@@ -156,9 +159,10 @@ const char* lmhead_status_string(int status);
 int lmhead_version(void);
 
 /* Per-kernel timing for benchmarks (not needed to use the op).
- * Kernel kinds, in order: compact, fwd_tiles, merge, zero_skipped, zero_rows,
- * gather, dz_tiles, dx_tiles, dw_tiles. */
-#define LMHEAD_NUM_KERNELS 9
+ * Kernel kinds, in order: compact, gather_rows, fwd_tiles, merge,
+ * zero_skipped, zero_rows, gather_cols, transpose_w, dz_tiles, dx_tiles,
+ * dw_tiles. */
+#define LMHEAD_NUM_KERNELS 11
 
 /* Static name of kernel kind `kind` (NULL if out of range). */
 const char* lmhead_kernel_name(int kind);

@@ -25,6 +25,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -78,22 +79,55 @@ static inline SavedView saved_view(void* base, int64_t N) {
 }
 
 static inline int n_vtiles(int64_t V) { return (int)((V + kBM - 1) / kBM); }
+static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-static inline size_t fwd_ws_bytes(int64_t N, int64_t V) {
+// Forward workspace: target logits [N] | partial m, s, b [n_vt][N] each |
+// gathered kept rows Xc [N][H] (bf16).
+struct FwdWs {
+  size_t zt, pm, ps, pb, xc, total;
+};
+static inline FwdWs fwd_ws(int64_t N, int64_t H, int64_t V) {
   const size_t nv = (size_t)n_vtiles(V);
-  return align256((size_t)N * 4) + 3 * align256(nv * (size_t)N * 4);
+  FwdWs w;
+  w.zt = 0;
+  w.pm = w.zt + align256((size_t)N * 4);
+  w.ps = w.pm + align256(nv * (size_t)N * 4);
+  w.pb = w.ps + align256(nv * (size_t)N * 4);
+  w.xc = w.pb + align256(nv * (size_t)N * 4);
+  w.total = w.xc + align256((size_t)N * (size_t)H * 2);
+  return w;
 }
 
-static inline int64_t dz_ld(int64_t V) { return (V + 255) / 256 * 256; }
-
-static inline int64_t chunk_rows(int64_t N, int64_t token_chunk) {
-  const int64_t c = token_chunk > 0 ? token_chunk : kDefaultChunk;
-  return c < N ? c : N;
+// Backward geometry: chunk capacity C (rows, multiple of 256), dZ pitch ldz
+// (V rounded up to 256), WT pitch ldv (V rounded up to 64), XcT pitch ldc.
+struct BwdGeom {
+  int64_t C, ldz, ldv, ldc;
+};
+static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
+  BwdGeom g;
+  const int64_t want = token_chunk > 0 ? token_chunk : kDefaultChunk;
+  g.C = N > 0 ? std::min(round_up(want, 256), round_up(N, 256)) : 0;
+  g.ldz = round_up(V, 256);
+  g.ldv = round_up(V, 64);
+  g.ldc = round_up(N + 64, 64);
+  return g;
 }
 
-static inline size_t bwd_ws_bytes(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
-  const int64_t C = chunk_rows(N, token_chunk);
-  return align256((size_t)N * (size_t)H * 2) + align256((size_t)C * (size_t)dz_ld(V) * 2);
+// Backward workspace: Xc [N][H] | XcT [H][ldc] | WT [H][ldv] | dZ [C][ldz] |
+// dZT [ldz][C], all bf16.
+struct BwdWs {
+  size_t xc, xct, wt, dz, dzt, total;
+};
+static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
+  const BwdGeom g = bwd_geom(N, V, token_chunk);
+  BwdWs w;
+  w.xc = 0;
+  w.xct = w.xc + align256((size_t)N * (size_t)H * 2);
+  w.wt = w.xct + align256((size_t)H * (size_t)g.ldc * 2);
+  w.dz = w.wt + align256((size_t)H * (size_t)g.ldv * 2);
+  w.dzt = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
+  w.total = w.dzt + align256((size_t)g.ldz * (size_t)g.C * 2);
+  return w;
 }
 
 // ---------------------------------------------------------------------------
@@ -178,12 +212,97 @@ __device__ __forceinline__ void stat_merge(float& m, float& s, float& b, float m
 }
 
 // ---------------------------------------------------------------------------
-// Forward tiles: M = vocab (A = W rows), N = kept tokens (B = X rows via the
-// kept-row map), K = H. Epilogue reduces over the tile's vocab rows.
+// Row gather: Xc[c] = X[kept_idx[c]] for the kept rows (compact order).
+// ---------------------------------------------------------------------------
+__global__ void k_gather_rows(const uint16_t* __restrict__ X, const SavedHeader* __restrict__ hdr,
+                              const int32_t* __restrict__ kept_idx, int H,
+                              uint16_t* __restrict__ Xc) {
+  const int c = blockIdx.x;
+  if (c >= hdr->n_kept) return;
+  const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)kept_idx[c] * H);
+  uint4* dst = reinterpret_cast<uint4*>(Xc + (int64_t)c * H);
+  for (int k = threadIdx.x; k < H / 8; k += blockDim.x) dst[k] = src[k];
+}
+
+// ---------------------------------------------------------------------------
+// 64 x 64 tile transposes through LDS (bf16).
+//   k_transpose_w : WT[h][v] = W[v][h]           (v < V; zero for V <= v < ldv)
+//   k_gather_cols : XcT[h][c] = X[kept_idx[c]][h] (c < n_kept; zero up to ldc)
+// ---------------------------------------------------------------------------
+constexpr int kTp = 64;
+constexpr int kTpPitch = kTp + 8;
+
+__device__ __forceinline__ void transpose_tile(uint16_t (*t)[kTpPitch], uint16_t* __restrict__ out,
+                                               int64_t ld_out) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int r = tid / 8 + 32 * it;  // output row (h)
+    const int ch = tid % 8;           // 8 consecutive output columns
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)t[ch * 8 + 2 * e][r] | ((uint32_t)t[ch * 8 + 2 * e + 1][r] << 16);
+    *reinterpret_cast<uint4*>(out + (int64_t)r * ld_out + ch * 8) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict__ W, int V, int H,
+                                                     uint16_t* __restrict__ WT, int64_t ldv) {
+  __shared__ uint16_t t[kTp][kTpPitch];
+  const int v0 = blockIdx.x * kTp, h0 = blockIdx.y * kTp;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int r = tid / 8 + 32 * it;
+    const int ch = tid % 8;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (v0 + r < V) x = *reinterpret_cast<const uint4*>(W + (int64_t)(v0 + r) * H + h0 + ch * 8);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t[r][ch * 8 + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
+      t[r][ch * 8 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+  transpose_tile(t, WT + (int64_t)h0 * ldv + v0, ldv);
+}
+
+__global__ __launch_bounds__(256) void k_gather_cols(const uint16_t* __restrict__ X,
+                                                     const SavedHeader* __restrict__ hdr,
+                                                     const int32_t* __restrict__ kept_idx, int H,
+                                                     uint16_t* __restrict__ XcT, int64_t ldc) {
+  __shared__ uint16_t t[kTp][kTpPitch];
+  const int n_kept = hdr->n_kept;
+  const int c0 = blockIdx.x * kTp, h0 = blockIdx.y * kTp;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int r = tid / 8 + 32 * it;
+    const int ch = tid % 8;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (c0 + r < n_kept)
+      x = *reinterpret_cast<const uint4*>(X + (int64_t)kept_idx[c0 + r] * H + h0 + ch * 8);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t[r][ch * 8 + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
+      t[r][ch * 8 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+  transpose_tile(t, XcT + (int64_t)h0 * ldc + c0, ldc);
+}
+
+// ---------------------------------------------------------------------------
+// Forward tiles: M = vocab (A = W rows), N = kept tokens (B = Xc rows), K = H.
+// The epilogue reduces over the tile's 256 vocab rows per token.
 // ---------------------------------------------------------------------------
 struct FwdParams {
   const uint16_t* W;
-  const uint16_t* X;
+  const uint16_t* Xc;
   const int32_t* targets;
   const int32_t* kept_idx;
   const SavedHeader* hdr;
@@ -196,8 +315,7 @@ struct FwdParams {
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
-  __shared__ uint4 lds_a[2 * kStageChunks];
-  __shared__ uint4 lds_b[2 * kStageChunks];
+  __shared__ __attribute__((aligned(1024))) char ring[kLdsBytes];
   __shared__ float red[2][3][kBN];
 
   const int rows = P.hdr->n_kept;
@@ -215,13 +333,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     if (t >= ntiles) continue;
     int tm, tn;
     tile_coords(t, mt, nt, tm, tn);
+    __syncthreads();
 
-    KMajorStager sa;
-    KMajorStager sb;
-    sa.init(P.W, P.H, nullptr, tm * kBM, P.V, tid);
-    sb.init(P.X, P.H, P.kept_idx, tn * kBN, rows, tid);
+    TileSrc A, B;
+    A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
+    B.init(P.Xc + (int64_t)tn * kBN * P.H, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(sa, sb, nk, lds_a, lds_b, acc);
+    mainloop(A, B, nk, ring, acc);
 
     const int vbase = tm * kBM + wm * 128;
     const bool full = vbase + 128 <= P.V;
@@ -238,20 +356,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
           if (ok) mx = fmaxf(mx, acc[i][j][r]);
         }
       float s = 0.f, b = 0.f;
-      const float m2 = mx * kLog2e;
       if (mx != -INFINITY) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const bool ok = full || (vbase + acc_row(i, r, lane) < P.V);
-            const float y = fmaf(acc[i][j][r], kLog2e, -m2);
+            const float y = (acc[i][j][r] - mx) * kLog2e;
             const float e = ok ? __builtin_amdgcn_exp2f(y) : 0.f;
             s += e;
-            b = fmaf(e, ok ? y : 0.f, b);
+            b = fmaf(e, y, b);
           }
       }
-      float m = (mx == -INFINITY) ? -INFINITY : m2;
+      float m = (mx == -INFINITY) ? -INFINITY : mx * kLog2e;
       // the other half of the wave holds the other 64 rows of the same token
       const float mo = __shfl_xor(m, 32);
       const float so = __shfl_xor(s, 32);
@@ -292,7 +409,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
         P.pb[o] = b;
       }
     }
-    __syncthreads();
   }
 }
 
@@ -361,39 +477,27 @@ __global__ void k_zero_rows(const int32_t* __restrict__ pos, int N, int H, float
   for (int k = threadIdx.x; k < H / 4; k += blockDim.x) row[k] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-__global__ void k_gather(const uint16_t* __restrict__ X, const SavedHeader* __restrict__ hdr,
-                         const int32_t* __restrict__ kept_idx, int H, uint16_t* __restrict__ Xc) {
-  const int c = blockIdx.x;
-  if (c >= hdr->n_kept) return;
-  const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)kept_idx[c] * H);
-  uint4* dst = reinterpret_cast<uint4*>(Xc + (int64_t)c * H);
-  for (int k = threadIdx.x; k < H / 8; k += blockDim.x) dst[k] = src[k];
-}
-
 struct DzParams {
   const uint16_t* W;
-  const uint16_t* X;
+  const uint16_t* Xc;
   const int32_t* targets;
   const float* g_lp;
   const float* g_h;  // null when the entropy term is off
   SavedView sv;
   int H, V, n_vt;
-  int c0, C;  // chunk start (compact rows) and capacity
-  int64_t ldz;
-  uint16_t* dZ;  // [C, ldz] bf16
+  int c0, C;     // chunk start (compact rows) and chunk capacity (multiple of 256)
+  int64_t ldz;   // dZ row pitch (V rounded up to 256)
+  uint16_t* dZ;  // [C][ldz]   token-major: the A operand of dX = dZ W
+  uint16_t* dZT; // [ldz][C]   vocab-major: the A operand of dW = dZ^T Xc
 };
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  // round to nearest even (values are finite)
-  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-  a = (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;
-  b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
-  return a | b;
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t a = __float_as_uint(x);
+  return (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;  // finite inputs
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
-  __shared__ uint4 lds_a[2 * kStageChunks];
-  __shared__ uint4 lds_b[2 * kStageChunks];
+  __shared__ __attribute__((aligned(1024))) char ring[kLdsBytes];
 
   const int n_kept = P.sv.hdr->n_kept;
   const int rows = min(P.C, n_kept - P.c0);
@@ -407,53 +511,57 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = P.H / kBK;
   const int32_t* kidx = P.sv.kept_idx + P.c0;
+  const uint16_t* xc = P.Xc + (int64_t)P.c0 * P.H;
 
   for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
     const int t = xcd_logical(round, gridDim.x);
     if (t >= ntiles) continue;
     int tm, tn;
     tile_coords(t, mt, nt, tm, tn);
+    __syncthreads();
 
-    KMajorStager sa;
-    KMajorStager sb;
-    sa.init(P.W, P.H, nullptr, tm * kBM, P.V, tid);
-    sb.init(P.X, P.H, kidx, tn * kBN, rows, tid);
+    TileSrc A, B;
+    A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
+    B.init(xc + (int64_t)tn * kBN * P.H, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(sa, sb, nk, lds_a, lds_b, acc);
+    mainloop(A, B, nk, ring, acc);
 
     const int vbase = tm * kBM + wm * 128;
     const bool full = vbase + 128 <= P.V;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = tn * kBN + wn * 128 + j * 32 + (lane & 31);  // chunk row
-      if (c >= rows) continue;
-      const int cc = P.c0 + c;
-      const int row = kidx[c];
-      const float lse = P.sv.lse[cc];
-      const float glp = P.g_lp[row];
-      const int tt = P.targets[row];
-      // dz = -p * (glp + gh * (lp + ent)) = p * (ca + cb * lp), lp = z - lse
-      float ca = -glp, cb = 0.f;
-      if (P.g_h) {
-        const float gh = P.g_h[row];
-        ca = -(glp + gh * P.sv.ent[cc]);
-        cb = -gh;
+      const bool crow = c < rows;
+      float lse = 0.f, ent = 0.f, glp = 0.f, gh = 0.f;
+      int tt = -1;
+      if (crow) {
+        const int cc = P.c0 + c;
+        const int row = kidx[c];
+        lse = P.sv.lse[cc];
+        glp = P.g_lp[row];
+        tt = P.targets[row];
+        if (P.g_h) {
+          gh = P.g_h[row];
+          ent = P.sv.ent[cc];
+        }
       }
+      // dz = -p (glp + gh (lp + ent)) = p (ca + cb lp), lp = z - lse
+      const float ca = -(glp + gh * ent);
+      const float cb = -gh;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float z = acc[i][j][r];
           // subtract before scaling: z - lse is exact near the row maximum
-          const float lp = z - lse;
+          const float lp = acc[i][j][r] - lse;
           const float p = __builtin_amdgcn_exp2f(lp * kLog2e);
-          float d = p * fmaf(cb, lp, ca);
-          const bool ok = full || (vbase + acc_row(i, r, lane) < P.V);
+          const float d = p * fmaf(cb, lp, ca);
+          const bool ok = crow && (full || (vbase + acc_row(i, r, lane) < P.V));
           acc[i][j][r] = ok ? d : 0.f;
         }
       const int local = tt - vbase;
       const int w = local & 31;
-      const bool hit = local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
+      const bool hit = crow && local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
       if (hit) {
         const int want = (local >> 5) * 16 + ((w >> 3) << 2) + (w & 3);
 #pragma unroll
@@ -462,35 +570,43 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           for (int r = 0; r < 16; ++r)
             if (want == i * 16 + r) acc[i][j][r] += glp;
       }
-      uint16_t* drow = P.dZ + (int64_t)c * P.ldz;
+      // dZ[c][v]: four consecutive v per register group (8 bytes)
+      uint16_t* zrow = P.dZ + (int64_t)c * P.ldz;
+      // dZT[v][c]: one element per register
+      uint16_t* tcol = P.dZT + c;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int v0 = vbase + i * 32 + 8 * g + 4 * (lane >> 5);
-          uint2 pk;
-          pk.x = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-          pk.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          *reinterpret_cast<uint2*>(drow + v0) = pk;
+          const uint32_t h0 = bf16_rne(acc[i][j][4 * g + 0]);
+          const uint32_t h1 = bf16_rne(acc[i][j][4 * g + 1]);
+          const uint32_t h2 = bf16_rne(acc[i][j][4 * g + 2]);
+          const uint32_t h3 = bf16_rne(acc[i][j][4 * g + 3]);
+          *reinterpret_cast<uint2*>(zrow + v0) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+          tcol[(int64_t)(v0 + 0) * P.C] = (uint16_t)h0;
+          tcol[(int64_t)(v0 + 1) * P.C] = (uint16_t)h1;
+          tcol[(int64_t)(v0 + 2) * P.C] = (uint16_t)h2;
+          tcol[(int64_t)(v0 + 3) * P.C] = (uint16_t)h3;
         }
     }
   }
 }
 
+// dX[kept rows] = dZ W: M = chunk rows (A = dZ), N = H (B = WT rows), K = vocab.
 struct DxParams {
-  const uint16_t* dZ;  // [C, ldz]
-  const uint16_t* W;   // [V, H]
+  const uint16_t* dZ;  // [C][ldz]
+  const uint16_t* WT;  // [H][ldv]
   SavedView sv;
   int H, V;
   int c0, C;
-  int64_t ldz;
-  int kpad;  // K extent: V rounded up to 64 (dZ pad columns are zero)
+  int64_t ldz, ldv;
+  int kv;  // K extent: V rounded up to kBK (dZ and WT are zero past V)
   float* dX;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
-  __shared__ uint4 lds_a[2 * kStageChunks];
-  __shared__ uint4 lds_b[2 * kStageChunks];
+  __shared__ __attribute__((aligned(1024))) char ring[kLdsBytes];
 
   const int n_kept = P.sv.hdr->n_kept;
   const int rows = min(P.C, n_kept - P.c0);
@@ -502,7 +618,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nk = P.kpad / kBK;
+  const int nk = P.kv / kBK;
   const int32_t* kidx = P.sv.kept_idx + P.c0;
 
   for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
@@ -510,13 +626,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     if (t >= ntiles) continue;
     int tm, tn;
     tile_coords(t, mt, nt, tm, tn);
+    __syncthreads();
 
-    KMajorStager sa;   // dZ rows (chunk tokens), k = vocab
-    MNMajorStager sb;  // W: element (k = v, n = h) at W[v * H + h]
-    sa.init(P.dZ, P.ldz, nullptr, tm * kBM, rows, tid);
-    sb.init(P.W, P.H, P.V, tn * kBN, P.H, tid);
+    TileSrc A, B;
+    A.init(P.dZ + (int64_t)tm * kBM * P.ldz, P.ldz, rows - tm * kBM);
+    B.init(P.WT + (int64_t)tn * kBN * P.ldv, P.ldv, P.H - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(sa, sb, nk, lds_a, lds_b, acc);
+    mainloop(A, B, nk, ring, acc);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -534,20 +650,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   }
 }
 
+// dW (+)= dZ^T Xc: M = vocab (A = dZT rows), N = H (B = XcT rows), K = chunk rows.
 struct DwParams {
-  const uint16_t* dZ;  // [C, ldz]: element (k = c, m = v) at dZ[c * ldz + v]
-  const uint16_t* Xc;  // [n_kept, H] gathered rows: element (k = c, n = h)
+  const uint16_t* dZT;  // [ldz][C]
+  const uint16_t* XcT;  // [H][ldc], this chunk starts at column c0
   const SavedHeader* hdr;
   int H, V;
   int c0, C;
-  int64_t ldz;
+  int64_t ldc;
   int accumulate;
   float* dW;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
-  __shared__ uint4 lds_a[2 * kStageChunks];
-  __shared__ uint4 lds_b[2 * kStageChunks];
+  __shared__ __attribute__((aligned(1024))) char ring[kLdsBytes];
 
   const int n_kept = P.hdr->n_kept;
   int rows = min(P.C, n_kept - P.c0);
@@ -562,21 +678,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nk = (rows + kBK - 1) / kBK;
-  const uint16_t* xc = P.Xc + (int64_t)P.c0 * P.H;
+  const int nk = (rows + kBK - 1) / kBK;  // dZT is zero past `rows`
 
   for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
     const int t = xcd_logical(round, gridDim.x);
     if (t >= ntiles) continue;
     int tm, tn;
     tile_coords(t, mt, nt, tm, tn);
+    __syncthreads();
 
-    MNMajorStager sa;  // dZ^T: k = chunk row, m = vocab
-    MNMajorStager sb;  // X_c: k = chunk row, n = hidden
-    sa.init(P.dZ, P.ldz, rows, tm * kBM, (int)P.ldz, tid);
-    sb.init(xc, P.H, rows, tn * kBN, P.H, tid);
+    TileSrc A, B;
+    A.init(P.dZT + (int64_t)tm * kBM * P.C, P.C, P.V - tm * kBM);
+    B.init(P.XcT + (int64_t)tn * kBN * P.ldc + P.c0, P.ldc, P.H - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(sa, sb, nk, lds_a, lds_b, acc);
+    mainloop(A, B, nk, ring, acc);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -631,20 +746,21 @@ static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t
 static int check_sizes(int64_t N, int64_t H, int64_t V) {
   if (N < 0 || H <= 0 || V <= 0) return LMHEAD_ERR_INVALID_ARG;
   if (H % 64 != 0) return LMHEAD_ERR_UNSUPPORTED;
-  // int32 indexing of rows, columns and per-tile partial offsets
-  if (N > INT32_MAX / 4 || H > (1 << 20) || V > (INT32_MAX / 4)) return LMHEAD_ERR_UNSUPPORTED;
+  // int32 indexing of rows and partial offsets; a 256-row operand tile must
+  // fit one buffer descriptor (2^31 bytes)
+  if (N > (1 << 28) || H > (1 << 20) || V > (1 << 22)) return LMHEAD_ERR_UNSUPPORTED;
   return LMHEAD_OK;
 }
 
 // Optional per-kernel timing (benchmarks only): hipEvent pairs recorded on
 // the launch stream around every launch while profiling is on.
 enum KernelKind {
-  KK_COMPACT = 0, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS, KK_GATHER, KK_DZ, KK_DX,
-  KK_DW, KK_COUNT
+  KK_COMPACT = 0, KK_GATHER_ROWS, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS,
+  KK_GATHER_COLS, KK_TRANSPOSE_W, KK_DZ, KK_DX, KK_DW, KK_COUNT
 };
 static const char* const kKernelNames[KK_COUNT] = {
-    "compact", "fwd_tiles", "merge", "zero_skipped", "zero_rows",
-    "gather",  "dz_tiles",  "dx_tiles", "dw_tiles"};
+    "compact",     "gather_rows", "fwd_tiles", "merge",    "zero_skipped", "zero_rows",
+    "gather_cols", "transpose_w", "dz_tiles",  "dx_tiles", "dw_tiles"};
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -706,12 +822,12 @@ LMH_API size_t lmhead_saved_bytes(int64_t N) {
 
 LMH_API size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V) {
   if (check_sizes(N, H, V) != LMHEAD_OK) return 0;
-  return fwd_ws_bytes(N, V);
+  return fwd_ws(N, H, V).total;
 }
 
 LMH_API size_t lmhead_bwd_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
   if (check_sizes(N, H, V) != LMHEAD_OK) return 0;
-  return bwd_ws_bytes(N, H, V, token_chunk);
+  return bwd_ws(N, H, V, token_chunk).total;
 }
 
 LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
@@ -730,8 +846,8 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
   if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace))
     return LMHEAD_ERR_INVALID_ARG;
   if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
-  const size_t ws_need = fwd_ws_bytes(N, V);
-  if (workspace_bytes < ws_need || (ws_need > 0 && !workspace)) return LMHEAD_ERR_WORKSPACE;
+  const FwdWs L = fwd_ws(N, H, V);
+  if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return LMHEAD_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   SavedView sv = saved_view(saved, N);
@@ -743,9 +859,14 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
 
   const int nv = n_vtiles(V);
   char* w = static_cast<char*>(workspace);
+  uint16_t* Xc = reinterpret_cast<uint16_t*>(w + L.xc);
+  LMH_TRY(launch(KK_GATHER_ROWS, k_gather_rows, dim3((unsigned)N), dim3(256), s,
+                 static_cast<const uint16_t*>(hidden), (const SavedHeader*)sv.hdr,
+                 (const int32_t*)sv.kept_idx, (int)H, Xc));
+
   FwdParams P;
   P.W = static_cast<const uint16_t*>(weight);
-  P.X = static_cast<const uint16_t*>(hidden);
+  P.Xc = Xc;
   P.targets = targets;
   P.kept_idx = sv.kept_idx;
   P.hdr = sv.hdr;
@@ -753,12 +874,10 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
   P.V = (int)V;
   P.n_vt = nv;
   P.ldp = N;
-  P.zt = reinterpret_cast<float*>(w);
-  const size_t a = align256((size_t)N * 4);
-  const size_t pa = align256((size_t)nv * (size_t)N * 4);
-  P.pm = reinterpret_cast<float*>(w + a);
-  P.ps = reinterpret_cast<float*>(w + a + pa);
-  P.pb = reinterpret_cast<float*>(w + a + 2 * pa);
+  P.zt = reinterpret_cast<float*>(w + L.zt);
+  P.pm = reinterpret_cast<float*>(w + L.pm);
+  P.ps = reinterpret_cast<float*>(w + L.ps);
+  P.pb = reinterpret_cast<float*>(w + L.pb);
   const int64_t max_tiles = (int64_t)nv * ((N + kBN - 1) / kBN);
   LMH_TRY(launch(KK_FWD, k_fwd_tiles, dim3(persistent_grid(max_tiles)), dim3(kThreads), s, P));
 
@@ -785,34 +904,43 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       !aligned16(grad_hidden) || !aligned16(grad_weight))
     return LMHEAD_ERR_INVALID_ARG;
   if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
-  const size_t ws_need = bwd_ws_bytes(N, H, V, token_chunk);
-  if (workspace_bytes < ws_need || (ws_need > 0 && !workspace)) return LMHEAD_ERR_WORKSPACE;
-  const int64_t C = chunk_rows(N, token_chunk);
-  const int64_t ldz = dz_ld(V);
-  if (C * ldz > ((int64_t)1 << 40)) return LMHEAD_ERR_UNSUPPORTED;
+  const BwdWs L = bwd_ws(N, H, V, token_chunk);
+  if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return LMHEAD_ERR_WORKSPACE;
+  const BwdGeom G = bwd_geom(N, V, token_chunk);
+  if (G.C > (1 << 22)) return LMHEAD_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   SavedView sv = saved_view(const_cast<void*>(saved), N);
   char* w = static_cast<char*>(workspace);
-  uint16_t* Xc = reinterpret_cast<uint16_t*>(w);
-  uint16_t* dZ = reinterpret_cast<uint16_t*>(w + align256((size_t)N * (size_t)H * 2));
+  uint16_t* Xc = reinterpret_cast<uint16_t*>(w + L.xc);
+  uint16_t* XcT = reinterpret_cast<uint16_t*>(w + L.xct);
+  uint16_t* WT = reinterpret_cast<uint16_t*>(w + L.wt);
+  uint16_t* dZ = reinterpret_cast<uint16_t*>(w + L.dz);
+  uint16_t* dZT = reinterpret_cast<uint16_t*>(w + L.dzt);
+  const uint16_t* X = static_cast<const uint16_t*>(hidden);
+  const uint16_t* Wt = static_cast<const uint16_t*>(weight);
 
   if (N > 0) {
     LMH_TRY(launch(KK_ZERO_ROWS, k_zero_rows, dim3((unsigned)N), dim3(256), s,
                    (const int32_t*)sv.pos, (int)N, (int)H, grad_hidden));
-    LMH_TRY(launch(KK_GATHER, k_gather, dim3((unsigned)N), dim3(256), s,
-                   static_cast<const uint16_t*>(hidden), (const SavedHeader*)sv.hdr,
-                   (const int32_t*)sv.kept_idx, (int)H, Xc));
+    LMH_TRY(launch(KK_GATHER_ROWS, k_gather_rows, dim3((unsigned)N), dim3(256), s, X,
+                   (const SavedHeader*)sv.hdr, (const int32_t*)sv.kept_idx, (int)H, Xc));
+    LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(G.ldc / kTp), (unsigned)(H / kTp)),
+                   dim3(256), s, X, (const SavedHeader*)sv.hdr, (const int32_t*)sv.kept_idx,
+                   (int)H, XcT, G.ldc));
+    LMH_TRY(launch(KK_TRANSPOSE_W, k_transpose_w,
+                   dim3((unsigned)(G.ldv / kTp), (unsigned)(H / kTp)), dim3(256), s, Wt, (int)V,
+                   (int)H, WT, G.ldv));
   }
 
   const int nv = n_vtiles(V);
-  const int64_t nchunks = N > 0 ? (N + C - 1) / C : 1;
+  const int64_t nchunks = N > 0 ? (N + G.C - 1) / G.C : 1;
   for (int64_t ch = 0; ch < nchunks; ++ch) {
-    const int c0 = (int)(ch * C);
+    const int c0 = (int)(ch * G.C);
     if (N > 0) {
       DzParams D;
-      D.W = static_cast<const uint16_t*>(weight);
-      D.X = static_cast<const uint16_t*>(hidden);
+      D.W = Wt;
+      D.Xc = Xc;
       D.targets = targets;
       D.g_lp = grad_logp;
       D.g_h = entropy_requires_grad ? grad_entropy : nullptr;
@@ -821,35 +949,37 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       D.V = (int)V;
       D.n_vt = nv;
       D.c0 = c0;
-      D.C = (int)C;
-      D.ldz = ldz;
+      D.C = (int)G.C;
+      D.ldz = G.ldz;
       D.dZ = dZ;
-      const int64_t dz_tiles = (int64_t)nv * ((C + kBN - 1) / kBN);
+      D.dZT = dZT;
+      const int64_t dz_tiles = (int64_t)nv * (G.C / kBN);
       LMH_TRY(launch(KK_DZ, k_dz_tiles, dim3(persistent_grid(dz_tiles)), dim3(kThreads), s, D));
 
-      DxParams X;
-      X.dZ = dZ;
-      X.W = static_cast<const uint16_t*>(weight);
-      X.sv = sv;
-      X.H = (int)H;
-      X.V = (int)V;
-      X.c0 = c0;
-      X.C = (int)C;
-      X.ldz = ldz;
-      X.kpad = (int)((V + 63) / 64 * 64);
-      X.dX = grad_hidden;
-      const int64_t dx_tiles = ((C + kBM - 1) / kBM) * ((H + kBN - 1) / kBN);
-      LMH_TRY(launch(KK_DX, k_dx_tiles, dim3(persistent_grid(dx_tiles)), dim3(kThreads), s, X));
+      DxParams X2;
+      X2.dZ = dZ;
+      X2.WT = WT;
+      X2.sv = sv;
+      X2.H = (int)H;
+      X2.V = (int)V;
+      X2.c0 = c0;
+      X2.C = (int)G.C;
+      X2.ldz = G.ldz;
+      X2.ldv = G.ldv;
+      X2.kv = (int)round_up(V, kBK);
+      X2.dX = grad_hidden;
+      const int64_t dx_tiles = (G.C / kBM) * ((H + kBN - 1) / kBN);
+      LMH_TRY(launch(KK_DX, k_dx_tiles, dim3(persistent_grid(dx_tiles)), dim3(kThreads), s, X2));
     }
     DwParams Wp;
-    Wp.dZ = dZ;
-    Wp.Xc = Xc;
+    Wp.dZT = dZT;
+    Wp.XcT = XcT;
     Wp.hdr = sv.hdr;
     Wp.H = (int)H;
     Wp.V = (int)V;
     Wp.c0 = c0;
-    Wp.C = (int)C;
-    Wp.ldz = ldz;
+    Wp.C = (int)G.C;
+    Wp.ldc = G.ldc;
     Wp.accumulate = ch > 0;
     Wp.dW = grad_weight;
     const int64_t dw_tiles = (int64_t)nv * ((H + kBN - 1) / kBN);

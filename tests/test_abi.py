@@ -78,19 +78,34 @@ def test_saved_state_is_far_below_one_full_vocab_activation(lib):
     assert lib.lmhead_saved_bytes(N) < full_bf16 / 10000
 
 
+def _fwd_ws(N, H, V):
+    nv = (V + 255) // 256
+    return _align(4 * N) + 3 * _align(nv * N * 4) + _align(N * H * 2)
+
+
+def _bwd_ws(N, H, V, chunk):
+    up = lambda x, m: (x + m - 1) // m * m
+    want = chunk if chunk > 0 else 8192
+    C = min(up(want, 256), up(N, 256)) if N > 0 else 0
+    ldz, ldv, ldc = up(V, 256), up(V, 64), up(N + 64, 64)
+    return (_align(N * H * 2) + _align(H * ldc * 2) + _align(H * ldv * 2)
+            + _align(C * ldz * 2) + _align(ldz * C * 2))
+
+
 def test_workspace_sizes(lib):
+    for (N, H, V) in ((16384, 4096, 131072), (128, 512, 8192), (10, 64, 1000), (0, 64, 5),
+                      (262144, 5120, 152064)):
+        assert lib.lmhead_fwd_workspace_bytes(N, H, V) == _fwd_ws(N, H, V)
+        for chunk in (0, 100, 256, 8192, 1 << 20):
+            assert lib.lmhead_bwd_workspace_bytes(N, H, V, chunk) == _bwd_ws(N, H, V, chunk)
+    # default chunk is 8192 rows: dZ in two layouts, 2 GiB each at V = 131072
     N, H, V = 16384, 4096, 131072
-    nv = V // 256
-    assert lib.lmhead_fwd_workspace_bytes(N, H, V) == _align(4 * N) + 3 * _align(nv * N * 4)
-    # default chunk 8192 rows of bf16 dZ, plus the gathered kept rows
-    assert lib.lmhead_bwd_workspace_bytes(N, H, V, 0) == _align(N * H * 2) + _align(8192 * V * 2)
-    assert lib.lmhead_bwd_workspace_bytes(N, H, V, 100) == _align(N * H * 2) + _align(100 * V * 2)
-    # V not a multiple of 256: dZ rows are padded to 256 columns
-    assert lib.lmhead_bwd_workspace_bytes(10, 64, 1000, 0) == _align(10 * 64 * 2) + _align(10 * 1024 * 2)
+    assert _bwd_ws(N, H, V, 0) - _bwd_ws(N, H, V, 4096) == 2 * (8192 - 4096) * V * 2
     # invalid sizes
     assert lib.lmhead_fwd_workspace_bytes(10, 100, 1000) == 0
     assert lib.lmhead_fwd_workspace_bytes(-1, 64, 1000) == 0
     assert lib.lmhead_bwd_workspace_bytes(10, 64, 0, 0) == 0
+    assert lib.lmhead_fwd_workspace_bytes(10, 64, (1 << 22) + 1) == 0
 
 
 FAKE = ctypes.c_void_p(0x10000)   # 16-byte aligned, never dereferenced
