@@ -6,10 +6,10 @@
 // op is arranged that way, using transposed copies where needed. Each wave
 // owns a 128 x 128 sub-tile held as 4 x 4 MFMA accumulator blocks (256 AGPRs).
 //
-// K advances in stages of 32 through a ring of 4 LDS stages. Stages are loaded
+// K advances in stages of 32 through a ring of 5 LDS stages (160 KiB). Stages are loaded
 // straight from global memory into LDS with buffer_load_dwordx4 ... lds (no
 // VGPR staging); the buffer descriptor's record count zero-fills rows past
-// the end of the matrix. Loads run 4 stages ahead; one barrier per stage both
+// the end of the matrix. Loads run kStages stages ahead; one barrier per stage both
 // publishes stage k+1 and frees the buffer of stage k for stage k+4. MFMA
 // fragments are double-buffered in registers: the fragments of the next
 // 16-wide k step are read from LDS while the current step's 16 MFMAs issue.
@@ -38,22 +38,25 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBK = 32;
-constexpr int kStages = 4;
+constexpr int kBK = 64;                                      // k per stage
+constexpr int kChunks = kBK / 8;                             // 16-byte chunks per row
+constexpr int kRowBytes = kBK * 2;                           // 128: one L2 line per row
+constexpr int kStages = 2;
 constexpr int kThreads = 256;
-constexpr int kOperandStageBytes = kBM * kBK * 2;            // 16 KiB
+constexpr int kOperandStageBytes = kBM * kRowBytes;          // 32 KiB
 constexpr int kStageBytes = 2 * kOperandStageBytes;          // A then B
 constexpr int kRingBytes = kStages * kStageBytes;            // 128 KiB
-constexpr int kLdsBytes = kRingBytes;
-constexpr int kLoadsPerWaveStage = 2 * (kOperandStageBytes / 4 / 1024);  // 8
+constexpr int kRowsPerLoad = 1024 / kRowBytes;               // rows per 1 KiB LDS-DMA load
+constexpr int kLoadsPerWaveOperand = (kBM / 4) / kRowsPerLoad;  // 8
+constexpr int kLoadsPerWaveStage = 2 * kLoadsPerWaveOperand;    // 16
 constexpr uint32_t kOOB = 0x80000000u;  // voffset beyond every record count
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-__device__ __forceinline__ int lds_swz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & (kChunks - 1); }
 
 // Byte offset of (row, 16-byte chunk) inside one operand stage.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return (row * 4 + (chunk ^ lds_swz(row))) * 16;
+  return (row * kChunks + (chunk ^ lds_swz(row))) * 16;
 }
 
 // s_waitcnt with the given vmcnt and no wait on the other counters (gfx9
@@ -71,7 +74,8 @@ __device__ __forceinline__ void wait_lgkm0() {
 // bf16 matrix; rows at or past `rows_valid` read as zero.
 struct TileSrc {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off[4];  // per load instruction: byte offset of this lane's chunk at k = 0
+  __amdgpu_buffer_rsrc_t none;          // zero records: every load reads zeros
+  uint32_t off[kLoadsPerWaveOperand];  // per load: byte offset of this lane's chunk at k = 0
 
   // tile_base: element pointer of the tile's first row; ld: row pitch
   // (elements, multiple of 8); rows: rows of this tile inside the matrix.
@@ -85,23 +89,30 @@ struct TileSrc {
     const int bytes = __builtin_amdgcn_readfirstlane((int)((int64_t)rows * ld * 2));
     void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
     rsrc = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, kRsrcWord3);
+    none = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0, kRsrcWord3);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wave * 64 + j * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ lds_swz(row);
+    for (int j = 0; j < kLoadsPerWaveOperand; ++j) {
+      const int row = wave * (kBM / 4) + j * kRowsPerLoad + lane / kChunks;
+      const int c = (lane % kChunks) ^ lds_swz(row);
       off[j] = row < rows ? (uint32_t)(row * ld * 2 + c * 16) : kOOB;
     }
   }
-  // Issue this wave's 4 loads of stage kt into the operand stage at `dst`.
-  __device__ __forceinline__ void issue(int kt, char* dst) const {
+  // Issue this wave's loads of stage kt into the operand stage at `dst`;
+  // stages at or past nk read as zeros (zero-record descriptor).
+  __device__ __forceinline__ void issue(int kt, int nk, char* dst) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    char* base = dst + wave * 4096;
+    char* base = dst + wave * (kBM / 4) * kRowBytes;
+    // the k offset rides in the scalar soffset field; rows past the end keep
+    // voffset >= the record count whether or not soffset enters the check
+    const bool live = kt < nk;
+    const int koff = __builtin_amdgcn_readfirstlane(live ? kt * kRowBytes : 0);
+    const __amdgpu_buffer_rsrc_t r = live ? rsrc : none;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(base + j * 1024), 16,
-                                               off[j] + (uint32_t)(kt * kBK * 2), 0, 0, 0);
+    for (int j = 0; j < kLoadsPerWaveOperand; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + j * 1024), 16, off[j], koff,
+                                               0, 0);
   }
 };
 
@@ -145,14 +156,14 @@ __device__ __forceinline__ void read_frags(const char* stage, int kk, int lane, 
   const int r = lane & 31;
   const int c = kk * 2 + (lane >> 5);
   const int o = lds_off(r, c);  // swizzle depends only on lane & 31 (see header)
-  const char* a = stage + wm * 128 * 64 + o;
-  const char* b = stage + kOperandStageBytes + wn * 128 * 64 + o;
+  const char* a = stage + wm * 128 * kRowBytes + o;
+  const char* b = stage + kOperandStageBytes + wn * 128 * kRowBytes + o;
   // first-use order of mfma_step: a0 with b0..b3, then a1, a2, a3
   f.a[0] = *reinterpret_cast<const bf16x8_t*>(a);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t*>(b + j * 32 * 64);
+  for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t*>(b + j * 32 * kRowBytes);
 #pragma unroll
-  for (int i = 1; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(a + i * 32 * 64);
+  for (int i = 1; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(a + i * 32 * kRowBytes);
 }
 
 __device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][4]) {
@@ -163,18 +174,16 @@ __device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][4])
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-__device__ __forceinline__ void issue_stage(const TileSrc& A, const TileSrc& B, int kt,
-                                            char* ring) {
-  char* st = ring + (kt % kStages) * kStageBytes;
-  A.issue(kt, st);
-  B.issue(kt, st + kOperandStageBytes);
+__device__ __forceinline__ void issue_stage(const TileSrc& A, const TileSrc& B, int kt, int nk,
+                                            char* st) {
+  A.issue(kt, nk, st);
+  B.issue(kt, nk, st + kOperandStageBytes);
 }
 
 // Waits until at most `ahead` stages of this wave's loads are in flight.
 __device__ __forceinline__ void wait_stages_ahead(int ahead) {
-  if (ahead >= 3)
-    wait_vmcnt<3 * kLoadsPerWaveStage>();
-  else if (ahead == 2)
+  static_assert(kStages <= 3, "extend the cases below");
+  if (ahead >= 2)
     wait_vmcnt<2 * kLoadsPerWaveStage>();
   else if (ahead == 1)
     wait_vmcnt<kLoadsPerWaveStage>();
@@ -182,76 +191,78 @@ __device__ __forceinline__ void wait_stages_ahead(int ahead) {
     wait_vmcnt<0>();
 }
 
-// One k step of kBK: the fragments of kk = 0 (f0) are in registers; read
-// kk = 1 (f1), run f0's MFMAs, publish stage kt + 1 (wait + barrier), start the
-// loads of stage kt + kStages into the buffer stage kt used, read the next
-// stage's kk = 0 fragments, run f1's MFMAs. STEADY: every condition is known
-// true (kt + kStages < nk), so the body is straight-line code.
 // sched_group_barrier masks
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
 
-template <bool STEADY>
-__device__ __forceinline__ void k_step(const TileSrc& A, const TileSrc& B, int kt, int nk,
-                                       char* ring, int lane, int wm, int wn, Frags& f0, Frags& f1,
-                                       f32x16_t (&acc)[4][4]) {
-  const char* st = ring + (kt % kStages) * kStageBytes;
-  // sched_barrier(0) fences keep the phases in this order: the compiler would
-  // otherwise interleave them to shorten live ranges, which serialises LDS
-  // latency against the MFMAs.
-  read_frags(st, 1, lane, wm, wn, f1);
-  mfma_step(f0, acc);
-  // one LDS read between consecutive MFMAs, so MFMA issue never waits on them
+// Runs one 16-wide MFMA k step from `cur` while reading the fragments of k
+// step `kk` of `stage` into `nxt`, one LDS read between consecutive MFMAs.
+template <int ID>
+__device__ __forceinline__ void step_and_read(const char* stage, int kk, int lane, int wm, int wn,
+                                              const Frags& cur, Frags& nxt,
+                                              f32x16_t (&acc)[4][4]) {
+  read_frags(stage, kk, lane, wm, wn, nxt);
+  mfma_step(cur, acc);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, ID);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, ID);
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, ID);
   __builtin_amdgcn_sched_barrier(0);
-  if (STEADY) {
-    wait_vmcnt<2 * kLoadsPerWaveStage>();  // stage kt + 1 landed (kt + 2, kt + 3 may fly)
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_stage(A, B, kt + kStages, ring);
-    read_frags(ring + ((kt + 1) % kStages) * kStageBytes, 0, lane, wm, wn, f0);
-    mfma_step(f1, acc);
-    // loads and next-stage fragment reads threaded between f1's MFMAs
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 1);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    return;
-  } else if (kt + 1 < nk) {
-    // stages issued so far: 0 .. min(nk - 1, kt + kStages - 1)
-    const int last = (nk - 1 < kt + kStages - 1) ? nk - 1 : kt + kStages - 1;
-    wait_stages_ahead(last - (kt + 1));
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    if (kt + kStages < nk) issue_stage(A, B, kt + kStages, ring);
-    read_frags(ring + ((kt + 1) % kStages) * kStageBytes, 0, lane, wm, wn, f0);
-  } else {
-    wait_lgkm0();
-  }
+}
+
+// The two LDS ring slots are separate __shared__ objects (slot0, slot1) and
+// the loop is unrolled by two, so every LDS access names a fixed slot: the
+// compiler can then see that a stage's fragment reads never alias the
+// direct-to-LDS loads in flight into the other slot, and inserts no waits.
+struct Ring {
+  char* slot[kStages];
+};
+
+// One stage of kBK = 4 MFMA k steps from slot `cur`. On entry f0 holds the
+// stage's kk = 0 fragments. kk = 1..3 are read from LDS while the previous k
+// step's MFMAs issue; before the last k step every wave publishes stage kt + 1
+// (wait + barrier), the loads of stage kt + 2 go into `cur`, and the next
+// stage's kk = 0 fragments are read from `nxt` during the last 16 MFMAs.
+// Every stage runs this same straight-line body: stages past the end of K are
+// zeros, so the loop can run in pairs over an even number of stages.
+__device__ __forceinline__ void k_step(const TileSrc& A, const TileSrc& B, int kt, int nk,
+                                       char* cur, char* nxt, int lane, int wm, int wn, Frags& f0,
+                                       Frags& f1, f32x16_t (&acc)[4][4]) {
   __builtin_amdgcn_sched_barrier(0);
+  step_and_read<0>(cur, 1, lane, wm, wn, f0, f1, acc);
+  step_and_read<1>(cur, 2, lane, wm, wn, f1, f0, acc);
+  step_and_read<2>(cur, 3, lane, wm, wn, f0, f1, acc);
+  // stage kt + 1 must have landed; with two stages nothing newer is in flight
+  wait_vmcnt<0>();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  issue_stage(A, B, kt + kStages, nk, cur);
+  read_frags(nxt, 0, lane, wm, wn, f0);
   mfma_step(f1, acc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 3);
+    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 3);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 3);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 3);
+    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 3);
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Accumulates the tile over nk stages of kBK. The caller must have made the
 // LDS ring free (barrier) before the call; on return every wave has finished
 // its LDS reads and no load is in flight.
-__device__ __forceinline__ void mainloop(const TileSrc& A, const TileSrc& B, int nk, char* ring,
-                                         f32x16_t (&acc)[4][4]) {
+__device__ __forceinline__ void mainloop(const TileSrc& A, const TileSrc& B, int nk, char* slot0,
+                                         char* slot1, f32x16_t (&acc)[4][4]) {
+  static_assert(kStages == 2, "the loop below is unrolled for a two-slot ring");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1;
@@ -265,16 +276,19 @@ __device__ __forceinline__ void mainloop(const TileSrc& A, const TileSrc& B, int
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   if (nk <= 0) return;
 
-  const int pro = nk < kStages ? nk : kStages;
-  for (int s = 0; s < pro; ++s) issue_stage(A, B, s, ring);
-  wait_stages_ahead(pro - 1);
+  issue_stage(A, B, 0, nk, slot0);
+  issue_stage(A, B, 1, nk, slot1);
+  wait_vmcnt<kLoadsPerWaveStage>();
   __builtin_amdgcn_s_barrier();
 
   Frags f0, f1;
-  read_frags(ring, 0, lane, wm, wn, f0);
-  int kt = 0;
-  for (; kt + kStages < nk; ++kt) k_step<true>(A, B, kt, nk, ring, lane, wm, wn, f0, f1, acc);
-  for (; kt < nk; ++kt) k_step<false>(A, B, kt, nk, ring, lane, wm, wn, f0, f1, acc);
+  read_frags(slot0, 0, lane, wm, wn, f0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    k_step(A, B, kt, nk, slot0, slot1, lane, wm, wn, f0, f1, acc);
+    k_step(A, B, kt + 1, nk, slot1, slot0, lane, wm, wn, f0, f1, acc);
+  }
+  // the last pair issued two zero stages that nobody reads; let them land
+  wait_vmcnt<0>();
   wait_lgkm0();
 }
 

@@ -315,8 +315,10 @@ struct FwdParams {
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
-  __shared__ __attribute__((aligned(1024))) char ring[kLdsBytes];
-  __shared__ float red[2][3][kBN];
+  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
+  // per-token partials of the two wave rows; reuses ring slot 0 after the main loop
+  float (*red)[3][kBN] = reinterpret_cast<float (*)[3][kBN]>(slot0);
 
   const int rows = P.hdr->n_kept;
   const int mt = P.n_vt;
@@ -339,10 +341,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
     B.init(P.Xc + (int64_t)tn * kBN * P.H, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, ring, acc);
+    mainloop(A, B, nk, slot0, slot1, acc);
 
     const int vbase = tm * kBM + wm * 128;
     const bool full = vbase + 128 <= P.V;
+    __syncthreads();  // every wave is done reading the ring
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cl = wn * 128 + j * 32 + (lane & 31);  // token inside the tile
@@ -497,7 +500,8 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
-  __shared__ __attribute__((aligned(1024))) char ring[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
 
   const int n_kept = P.sv.hdr->n_kept;
   const int rows = min(P.C, n_kept - P.c0);
@@ -524,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
     B.init(xc + (int64_t)tn * kBN * P.H, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, ring, acc);
+    mainloop(A, B, nk, slot0, slot1, acc);
 
     const int vbase = tm * kBM + wm * 128;
     const bool full = vbase + 128 <= P.V;
@@ -606,7 +610,8 @@ struct DxParams {
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
-  __shared__ __attribute__((aligned(1024))) char ring[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
 
   const int n_kept = P.sv.hdr->n_kept;
   const int rows = min(P.C, n_kept - P.c0);
@@ -632,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     A.init(P.dZ + (int64_t)tm * kBM * P.ldz, P.ldz, rows - tm * kBM);
     B.init(P.WT + (int64_t)tn * kBN * P.ldv, P.ldv, P.H - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, ring, acc);
+    mainloop(A, B, nk, slot0, slot1, acc);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -663,7 +668,8 @@ struct DwParams {
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
-  __shared__ __attribute__((aligned(1024))) char ring[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
 
   const int n_kept = P.hdr->n_kept;
   int rows = min(P.C, n_kept - P.c0);
@@ -691,7 +697,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     A.init(P.dZT + (int64_t)tm * kBM * P.C, P.C, P.V - tm * kBM);
     B.init(P.XcT + (int64_t)tn * kBN * P.ldc + P.c0, P.ldc, P.H - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, ring, acc);
+    mainloop(A, B, nk, slot0, slot1, acc);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
