@@ -27,6 +27,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 KERNELS_GEMM = ("fwd_tiles", "dz_tiles", "dx_tiles", "dw_tiles")
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic_dense_rl_N16384_H4096_V131072.json")
+KERNEL_SOURCES = ("lm_head_log_amd/csrc/lmhead.hip", "lm_head_log_amd/csrc/gemm_core.h")
 
 
 def log(msg):
@@ -40,6 +42,31 @@ def make_workload(cfg: int, keep: float):
     if cfg == 2:
         return wl.config2(keep)
     return wl.CONFIGS[cfg]()
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload_name: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    table (FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB copy), or None when the
+    table is absent, covers another workload, or predates the current kernel
+    sources."""
+    try:
+        with open(TRAFFIC_TABLE) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tab.get("source_sha256") != kernel_source_hash() or tab.get("workload") != workload_name:
+        return None
+    k = tab.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(w, rows_n: int):
@@ -78,7 +105,9 @@ def main():
     ap.add_argument("--keep", type=float, default=1.0)
     ap.add_argument("--token-chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device copy first (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -131,6 +160,13 @@ def main():
         if do_bwd:
             lmh.lmhead_bwd(X, W, t, saved, glp, gh, erg, args.token_chunk, grad_hidden=gX,
                            grad_weight=gW, workspace=ws_b, stream=stream)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         step()
@@ -206,7 +242,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dom, w.name),
         },
         "cpu_baseline": cpu,
     }

@@ -121,12 +121,26 @@ struct TileSrc {
 // Workgroups are dispatched round-robin over the 8 XCDs (chiplets), so block
 // b runs on XCD b % 8. Slot b of round `r` is remapped so that the blocks of
 // one XCD take consecutive logical tiles; logical tiles run in groups of
-// kGroupM m-tiles by all n-tiles (m fastest inside a group), so the 32
-// concurrent tiles of an XCD form a 4 x 8 block sharing A and B panels in
-// that XCD's L2.
+// GM m-tiles by all n-tiles (m fastest inside a group), so the 32
+// concurrent tiles of an XCD form a GM x (32 / GM) block sharing A and B
+// panels in that XCD's L2.
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;
-constexpr int kGroupM = 4;
+// Group widths (m-tiles per group) of each GEMM, chosen by a timing sweep
+// over 1..32 at N=16384 H=4096 V=131072; a group is swept with m
+// fastest, so an XCD's 32 concurrent tiles cover gm m-tiles by 32 / gm n-tiles.
+#ifndef LMH_GM_FWD
+#define LMH_GM_FWD 8
+#endif
+#ifndef LMH_GM_DZ
+#define LMH_GM_DZ 8
+#endif
+#ifndef LMH_GM_DX
+#define LMH_GM_DX 16
+#endif
+#ifndef LMH_GM_DW
+#define LMH_GM_DW 16
+#endif
 
 __device__ __forceinline__ int xcd_logical(int round, int grid) {
   const int b = blockIdx.x;
@@ -134,11 +148,12 @@ __device__ __forceinline__ int xcd_logical(int round, int grid) {
   return round * grid + (b % kXcds) * per + (b / kXcds);
 }
 
+template <int GM>
 __device__ __forceinline__ void tile_coords(int t, int mt, int nt, int& tm, int& tn) {
-  const int per_group = kGroupM * nt;
+  const int per_group = GM * nt;
   const int g = t / per_group;
-  const int first = g * kGroupM;
-  const int gm = min(mt - first, kGroupM);
+  const int first = g * GM;
+  const int gm = min(mt - first, GM);
   const int r = t - g * per_group;
   tm = first + r % gm;
   tn = r / gm;

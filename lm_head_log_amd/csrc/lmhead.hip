@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     const int t = xcd_logical(round, gridDim.x);
     if (t >= ntiles) continue;
     int tm, tn;
-    tile_coords(t, mt, nt, tm, tn);
+    tile_coords<LMH_GM_FWD>(t, mt, nt, tm, tn);
     __syncthreads();
 
     TileSrc A, B;
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     const int t = xcd_logical(round, gridDim.x);
     if (t >= ntiles) continue;
     int tm, tn;
-    tile_coords(t, mt, nt, tm, tn);
+    tile_coords<LMH_GM_DZ>(t, mt, nt, tm, tn);
     __syncthreads();
 
     TileSrc A, B;
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     const int t = xcd_logical(round, gridDim.x);
     if (t >= ntiles) continue;
     int tm, tn;
-    tile_coords(t, mt, nt, tm, tn);
+    tile_coords<LMH_GM_DX>(t, mt, nt, tm, tn);
     __syncthreads();
 
     TileSrc A, B;
@@ -690,7 +690,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     const int t = xcd_logical(round, gridDim.x);
     if (t >= ntiles) continue;
     int tm, tn;
-    tile_coords(t, mt, nt, tm, tn);
+    tile_coords<LMH_GM_DW>(t, mt, nt, tm, tn);
     __syncthreads();
 
     TileSrc A, B;
