@@ -12,8 +12,8 @@
  *    tokens no loss com...": author comment (the vocab matmul is where the
  *    FLOPs are; tokens no loss reads are skipped) and Overview (a keep mask
  *    selects positions; compact -> chunked log-prob/entropy -> expand back,
- *    with zero log-prob and entropy at skipped positions; default token chunk
- *    8192).
+ *    with zero log-prob and entropy at skipped positions; the token chunk
+ *    bounds memory).
  *  - SkyRL PR #2374, "feat(megatron): fuse LM-head entropy for RL": "How it
  *    works" and "Usage" (one projection gives selected-token log-probs and
  *    entropy; metric-only entropy adds no gradient work; entropy-loss mode
@@ -88,7 +88,9 @@ size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V);
  * and column-major) and of W^T, plus dZ for one chunk of C rows in both
  * token-major and vocab-major order, where C = token_chunk rounded up to a
  * multiple of 256 (at most N rounded up to 256). token_chunk <= 0 selects the
- * default 8192 (prime-rl PR #3326, Overview). Returns 0 on invalid sizes. */
+ * largest chunk whose two dZ buffers fit 16 GiB (prime-rl PR #3326, Overview,
+ * uses the chunk to bound memory; its default of 8192 rows was set for a
+ * smaller memory). Returns 0 on invalid sizes. */
 size_t lmhead_bwd_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t token_chunk);
 
 /* Forward: compaction of the kept rows, the fused projection with per-row
@@ -131,7 +133,8 @@ int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
  *  grad_entropy fp32 [N]; must be NULL iff !entropy_requires_grad (N > 0)
  *  grad_hidden fp32 [N, H] out, fully overwritten (+0.0 rows where skipped)
  *  grad_weight fp32 [V, H] out, fully overwritten
- *  token_chunk rows per chunk, rounded up to a multiple of 256; <= 0 selects 8192
+ *  token_chunk rows per chunk, rounded up to a multiple of 256; <= 0 selects
+ *             the default described at lmhead_bwd_workspace_bytes
  *  workspace  >= lmhead_bwd_workspace_bytes(N, H, V, token_chunk) bytes
  */
 int lmhead_bwd(const void* hidden, const void* weight, const int32_t* targets,

@@ -9,8 +9,8 @@ provides device memory and the current stream only.
 argument set of the pages' fused head: ``keep_mask`` (prime-rl PR #3326,
 Overview), ``return_entropy`` / ``entropy_requires_grad`` (SkyRL PR #2374,
 "How it works" and "Usage"), float32 outputs for bf16 inputs (twinkle PR #283,
-section 1), and a token chunk that defaults to 8192 (prime-rl PR #3326,
-Overview).
+section 1), and a token chunk that bounds backward memory (prime-rl PR #3326,
+Overview); 0 selects the library's memory-budget default.
 """
 
 from __future__ import annotations
@@ -29,7 +29,7 @@ __all__ = [
     "DEFAULT_TOKEN_CHUNK", "lmhead_kernel_name", "lmhead_profile_begin", "lmhead_profile_end",
 ]
 
-DEFAULT_TOKEN_CHUNK = 8192
+DEFAULT_TOKEN_CHUNK = 0  # library default: largest chunk whose dZ buffers fit 16 GiB
 
 
 def _L():

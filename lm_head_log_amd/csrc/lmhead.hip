@@ -38,7 +38,12 @@ namespace lmh {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kDefaultChunk = 8192;
+// Default token chunk: the largest multiple of 256 rows whose two bf16 dZ
+// buffers (token-major and vocab-major) fit this budget. The pages' fused head
+// defaults to 8192 rows to bound memory on an 80 GB part; with 288 GB of HBM
+// the budget admits a whole 16K-token batch at V = 131072, which saves the
+// read-modify-write of dW between chunks.
+constexpr int64_t kDefaultDzBudget = int64_t(16) << 30;
 constexpr int kVersion = 100;  // 0.1.0
 
 // ---------------------------------------------------------------------------
@@ -105,7 +110,11 @@ struct BwdGeom {
 };
 static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
   BwdGeom g;
-  const int64_t want = token_chunk > 0 ? token_chunk : kDefaultChunk;
+  int64_t want = token_chunk;
+  if (want <= 0) {
+    want = kDefaultDzBudget / (4 * round_up(V, 256)) / 256 * 256;
+    if (want < 256) want = 256;
+  }
   g.C = N > 0 ? std::min(round_up(want, 256), round_up(N, 256)) : 0;
   g.ldz = round_up(V, 256);
   g.ldv = round_up(V, 64);
@@ -494,10 +503,8 @@ struct DzParams {
   uint16_t* dZT; // [ldz][C]   vocab-major: the A operand of dW = dZ^T Xc
 };
 
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t a = __float_as_uint(x);
-  return (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;  // finite inputs
-}
+// bf16 pairs: (__bf16)x rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
   __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
@@ -531,7 +538,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     mainloop(A, B, nk, slot0, slot1, acc);
 
     const int vbase = tm * kBM + wm * 128;
-    const bool full = vbase + 128 <= P.V;
+    // full: every vocab row of this wave and every token of the tile is valid
+    const bool full = vbase + 128 <= P.V && tn * kBN + kBN <= rows;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = tn * kBN + wn * 128 + j * 32 + (lane & 31);  // chunk row
@@ -559,10 +567,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           // subtract before scaling: z - lse is exact near the row maximum
           const float lp = acc[i][j][r] - lse;
           const float p = __builtin_amdgcn_exp2f(lp * kLog2e);
-          const float d = p * fmaf(cb, lp, ca);
-          const bool ok = crow && (full || (vbase + acc_row(i, r, lane) < P.V));
-          acc[i][j][r] = ok ? d : 0.f;
+          acc[i][j][r] = p * fmaf(cb, lp, ca);
         }
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = crow && (vbase + acc_row(i, r, lane) < P.V);
+            acc[i][j][r] = ok ? acc[i][j][r] : 0.f;
+          }
+      }
       const int local = tt - vbase;
       const int w = local & 31;
       const bool hit = crow && local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
@@ -574,24 +589,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           for (int r = 0; r < 16; ++r)
             if (want == i * 16 + r) acc[i][j][r] += glp;
       }
-      // dZ[c][v]: four consecutive v per register group (8 bytes)
+      // dZ[c][v]: four consecutive v per register group (8 bytes);
+      // dZT[v][c]: one element per register, 32 lanes give 64 contiguous bytes
       uint16_t* zrow = P.dZ + (int64_t)c * P.ldz;
-      // dZT[v][c]: one element per register
       uint16_t* tcol = P.dZT + c;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int v0 = vbase + i * 32 + 8 * g + 4 * (lane >> 5);
-          const uint32_t h0 = bf16_rne(acc[i][j][4 * g + 0]);
-          const uint32_t h1 = bf16_rne(acc[i][j][4 * g + 1]);
-          const uint32_t h2 = bf16_rne(acc[i][j][4 * g + 2]);
-          const uint32_t h3 = bf16_rne(acc[i][j][4 * g + 3]);
-          *reinterpret_cast<uint2*>(zrow + v0) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-          tcol[(int64_t)(v0 + 0) * P.C] = (uint16_t)h0;
-          tcol[(int64_t)(v0 + 1) * P.C] = (uint16_t)h1;
-          tcol[(int64_t)(v0 + 2) * P.C] = (uint16_t)h2;
-          tcol[(int64_t)(v0 + 3) * P.C] = (uint16_t)h3;
+          const bf16x2_t lo = {(__bf16)acc[i][j][4 * g + 0], (__bf16)acc[i][j][4 * g + 1]};
+          const bf16x2_t hi = {(__bf16)acc[i][j][4 * g + 2], (__bf16)acc[i][j][4 * g + 3]};
+          const uint32_t plo = __builtin_bit_cast(uint32_t, lo);
+          const uint32_t phi = __builtin_bit_cast(uint32_t, hi);
+          *reinterpret_cast<uint2*>(zrow + v0) = make_uint2(plo, phi);
+          tcol[(int64_t)(v0 + 0) * P.C] = (uint16_t)plo;
+          tcol[(int64_t)(v0 + 1) * P.C] = (uint16_t)(plo >> 16);
+          tcol[(int64_t)(v0 + 2) * P.C] = (uint16_t)phi;
+          tcol[(int64_t)(v0 + 3) * P.C] = (uint16_t)(phi >> 16);
         }
     }
   }

@@ -85,7 +85,7 @@ def _fwd_ws(N, H, V):
 
 def _bwd_ws(N, H, V, chunk):
     up = lambda x, m: (x + m - 1) // m * m
-    want = chunk if chunk > 0 else 8192
+    want = chunk if chunk > 0 else max(256, (16 << 30) // (4 * up(V, 256)) // 256 * 256)
     C = min(up(want, 256), up(N, 256)) if N > 0 else 0
     ldz, ldv, ldc = up(V, 256), up(V, 64), up(N + 64, 64)
     return (_align(N * H * 2) + _align(H * ldc * 2) + _align(H * ldv * 2)
@@ -98,9 +98,12 @@ def test_workspace_sizes(lib):
         assert lib.lmhead_fwd_workspace_bytes(N, H, V) == _fwd_ws(N, H, V)
         for chunk in (0, 100, 256, 8192, 1 << 20):
             assert lib.lmhead_bwd_workspace_bytes(N, H, V, chunk) == _bwd_ws(N, H, V, chunk)
-    # default chunk is 8192 rows: dZ in two layouts, 2 GiB each at V = 131072
+    # default chunk: two bf16 dZ layouts within 16 GiB, i.e. the whole 16K batch
+    # at V = 131072 (4 GiB each)
     N, H, V = 16384, 4096, 131072
-    assert _bwd_ws(N, H, V, 0) - _bwd_ws(N, H, V, 4096) == 2 * (8192 - 4096) * V * 2
+    assert _bwd_ws(N, H, V, 0) == _bwd_ws(N, H, V, 16384)
+    assert _bwd_ws(N, H, V, 0) - _bwd_ws(N, H, V, 4096) == 2 * (16384 - 4096) * V * 2
+    assert _bwd_ws(262144, 4096, 152064, 0) == _bwd_ws(262144, 4096, 152064, 28160)
     # invalid sizes
     assert lib.lmhead_fwd_workspace_bytes(10, 100, 1000) == 0
     assert lib.lmhead_fwd_workspace_bytes(-1, 64, 1000) == 0
