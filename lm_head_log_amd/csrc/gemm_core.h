@@ -2,24 +2,42 @@
 //
 // One workgroup of 256 threads (4 wave64s arranged 2 x 2) computes a 256 x 256
 // fp32 tile C[m][n] = sum_k A[m][k] * B[n][k] with v_mfma_f32_32x32x16_bf16.
-// Both operands are K-major (row-major with k contiguous): every GEMM of the
-// op is arranged that way, using transposed copies where needed. Each wave
-// owns a 128 x 128 sub-tile held as 4 x 4 MFMA accumulator blocks (256 AGPRs).
+// Each wave owns a 128 x 128 sub-tile held as 4 x 4 MFMA accumulator blocks
+// (256 AGPRs).
 //
-// K advances in stages of 32 through a ring of 5 LDS stages (160 KiB). Stages are loaded
-// straight from global memory into LDS with buffer_load_dwordx4 ... lds (no
-// VGPR staging); the buffer descriptor's record count zero-fills rows past
-// the end of the matrix. Loads run kStages stages ahead; one barrier per stage both
-// publishes stage k+1 and frees the buffer of stage k for stage k+4. MFMA
-// fragments are double-buffered in registers: the fragments of the next
-// 16-wide k step are read from LDS while the current step's 16 MFMAs issue.
+// An operand is read from global memory in one of two layouts, chosen per GEMM
+// so that no operand ever needs a transposed copy:
+//   KSrc  : K-major, [mn][ld] with k contiguous (e.g. W[v][h] as the A of
+//           Z = W X^T, K = h);
+//   MNSrc : MN-major, [k][ld] with mn contiguous (e.g. W[v][h] as the B of
+//           dX = dZ W, K = v, n = h).
 //
-// LDS stage layout: a tile row (an m of A or an n of B) holds its 32 k values
-// as four 16-byte chunks; the chunk index is XOR-swizzled with (row >> 2) & 3.
-// With that swizzle the MFMA fragment reads (lane l reads row l % 32, chunk
-// 2 kk + l / 32) showed zero LDS bank-conflict cycles on gfx950 in a counter
-// measurement of ds_read_b128 address patterns, and each direct-to-LDS load
-// still writes 1 KiB contiguously.
+// K advances in stages of kBK = 64 through a ring of two LDS stages (128 KiB).
+// Stages are loaded straight from global memory into LDS with
+// buffer_load_dwordx4 ... lds (no VGPR staging); the buffer descriptor's
+// record count zero-fills rows past the end of the matrix. One barrier per
+// stage both publishes stage k + 1 and frees the slot of stage k for stage
+// k + 2. MFMA fragments are double-buffered in registers: the fragments of the
+// next 16-wide k step are read from LDS while the current step's 16 MFMAs
+// issue.
+//
+// LDS stage layouts (32 KiB per operand, 256 mn x 64 k bf16):
+//   K-major : 256 rows (one per m or n) of 128 bytes (64 k); the 16-byte chunk
+//             index is XOR-swizzled with (row >> 1) & 7. Fragments are read
+//             with ds_read_b128 (lane l: row l % 32, chunk 2 kk + l / 32).
+//   MN-major: 16 groups of 4 consecutive k rows, 2 KiB each. Inside a group
+//             the 64-byte piece (32 mn values) of k row e in 32-wide mn block
+//             s sits at byte (4 s + e) * 64, i.e. the four k rows are
+//             interleaved piece by piece. Fragments are read with
+//             ds_read_b64_tr_b16, which hands lane i of each 16-lane group
+//             element i % 4 of the 8 bytes addressed by lane 4 e + i / 4 as its
+//             element e: pointing lane 4 e + q at k row k0 + e, mn n0 + 4 q
+//             gives lane i the values (mn n0 + i, k k0 .. k0 + 3), which is the
+//             MFMA fragment shape; two such reads give the 8 k of a fragment.
+//             A half wave reads 4 whole pieces that are adjacent in LDS
+//             (256 contiguous bytes), so the reads are free of bank conflicts,
+//             and one direct-to-LDS load (1 KiB) fills half a group from
+//             4 rows x 256 contiguous global bytes.
 //
 // MFMA 32x32x16 bf16 register layout (lane l of 64):
 //   A fragment: row  l % 32, k = 8 * (l / 32) + [0..7]
@@ -33,13 +51,15 @@
 namespace lmh {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 64;                                      // k per stage
-constexpr int kChunks = kBK / 8;                             // 16-byte chunks per row
+constexpr int kChunks = kBK / 8;                             // 16-byte chunks per K-major row
 constexpr int kRowBytes = kBK * 2;                           // 128: one L2 line per row
 constexpr int kStages = 2;
 constexpr int kThreads = 256;
@@ -52,9 +72,15 @@ constexpr int kLoadsPerWaveStage = 2 * kLoadsPerWaveOperand;    // 16
 constexpr uint32_t kOOB = 0x80000000u;  // voffset beyond every record count
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
+// MN-major stage geometry
+constexpr int kMnRowBytes = kBM * 2;                // 512: one k row of 256 mn values
+constexpr int kMnGroupBytes = 4 * kMnRowBytes;      // 2 KiB: 4 interleaved k rows
+constexpr int kMnPieceBytes = 64;                   // 32 mn values of one k row
+static_assert(kBK / 4 * kMnGroupBytes == kOperandStageBytes, "MN-major stage size");
+
 __device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & (kChunks - 1); }
 
-// Byte offset of (row, 16-byte chunk) inside one operand stage.
+// Byte offset of (row, 16-byte chunk) inside one K-major operand stage.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return (row * kChunks + (chunk ^ lds_swz(row))) * 16;
 }
@@ -70,9 +96,17 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
+// A buffer descriptor must live in SGPRs: its inputs go through readfirstlane
+// so the compiler sees them as wave-uniform (they are uniform by design).
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // A K-major operand tile source: rows row0 .. row0 + 255 of a [rows][ld]
 // bf16 matrix; rows at or past `rows_valid` read as zero.
-struct TileSrc {
+struct KSrc {
   __amdgpu_buffer_rsrc_t rsrc;
   __amdgpu_buffer_rsrc_t none;          // zero records: every load reads zeros
   uint32_t off[kLoadsPerWaveOperand];  // per load: byte offset of this lane's chunk at k = 0
@@ -81,13 +115,8 @@ struct TileSrc {
   // (elements, multiple of 8); rows: rows of this tile inside the matrix.
   __device__ __forceinline__ void init(const uint16_t* tile_base, int64_t ld, int rows) {
     rows = rows < 0 ? 0 : (rows > kBM ? kBM : rows);
-    // The descriptor must live in SGPRs: pass its inputs through readfirstlane
-    // so the compiler sees them as wave-uniform (they are uniform by design).
-    const uint64_t p = reinterpret_cast<uint64_t>(tile_base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
     const int bytes = __builtin_amdgcn_readfirstlane((int)((int64_t)rows * ld * 2));
-    void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    void* base = reinterpret_cast<void*>(uniform_u64(reinterpret_cast<uint64_t>(tile_base)));
     rsrc = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, kRsrcWord3);
     none = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0, kRsrcWord3);
     const int lane = threadIdx.x & 63;
@@ -114,6 +143,76 @@ struct TileSrc {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + j * 1024), 16, off[j], koff,
                                                0, 0);
   }
+  // Fragment of k step kk, 32-row block i of the wave's 128-row half `half`.
+  static __device__ __forceinline__ bf16x8_t frag(const char* op, int kk, int lane, int half,
+                                                  int i) {
+    const int o = lds_off(lane & 31, kk * 2 + (lane >> 5));  // swizzle depends on lane & 31 only
+    return *reinterpret_cast<const bf16x8_t*>(op + (half * 128 + i * 32) * kRowBytes + o);
+  }
+  static constexpr int kReadsPerFrag = 1;
+};
+
+// An MN-major operand tile source: columns mn0 .. mn0 + 255 of the k rows of a
+// [k_rows][ld] bf16 matrix (mn contiguous); k rows at or past k_rows and
+// columns at or past mn_valid (counted from mn0) read as zero.
+struct MNSrc {
+  uint64_t base;                        // byte address of (k 0, mn0); wave-uniform
+  int64_t pitch;                        // bytes per k row; wave-uniform
+  int k_valid;                          // wave-uniform
+  uint32_t off[kLoadsPerWaveOperand];  // per load: byte offset of this lane's chunk in a stage
+
+  __device__ __forceinline__ void init(const uint16_t* col_base, int64_t ld, int k_rows,
+                                       int mn_valid) {
+    base = uniform_u64(reinterpret_cast<uint64_t>(col_base));
+    pitch = (int64_t)uniform_u64((uint64_t)(ld * 2));
+    k_valid = __builtin_amdgcn_readfirstlane(k_rows < 0 ? 0 : k_rows);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int e = (lane >> 2) & 3;     // k row inside the group
+    const int blk = lane >> 4;         // 32-wide mn block inside the half
+    const int cq = lane & 3;           // 16-byte chunk inside the piece
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWaveOperand; ++j) {
+      // load j fills half (j & 1) of group 4 wave + j / 2 of the stage
+      const int row = (wave * 4 + (j >> 1)) * 4 + e;
+      const int col = ((j & 1) * 4 + blk) * 32 + cq * 8;
+      off[j] = col < mn_valid ? (uint32_t)(row * pitch + col * 2) : kOOB;
+    }
+  }
+  // Issue this wave's loads of stage kt into the operand stage at `dst`. The
+  // descriptor is rebased to the stage's first k row, and its record count
+  // covers only the valid rows of the stage (none at or past k_valid).
+  __device__ __forceinline__ void issue(int kt, int /*nk*/, char* dst) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    char* ldsb = dst + wave * 4 * kMnGroupBytes;
+    int rows = k_valid - kt * kBK;
+    rows = rows < 0 ? 0 : (rows > kBK ? kBK : rows);
+    void* p = reinterpret_cast<void*>(uniform_u64(base + (uint64_t)((int64_t)kt * kBK * pitch)));
+    const int bytes = __builtin_amdgcn_readfirstlane((int)(rows * pitch));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p, (short)0, bytes,
+                                                                       kRsrcWord3);
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWaveOperand; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_ptr_t)(ldsb + (j >> 1) * kMnGroupBytes + (j & 1) * 1024), 16, off[j], 0, 0, 0);
+  }
+  static __device__ __forceinline__ bf16x4_t tr_read(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(lds_ptr_t)(p));
+  }
+  // Fragment of k step kk, 32-wide mn block i of the wave's 128 half `half`.
+  static __device__ __forceinline__ bf16x8_t frag(const char* op, int kk, int lane, int half,
+                                                  int i) {
+    // lane 16 g + 4 e + q reads k row 16 kk + 8 (g >> 1) + 4 h + e at mn
+    // 128 half + 32 i + 16 (g & 1) + 4 q, for the two halves h of the fragment
+    const int g = lane >> 4;
+    const int lane_part = (g >> 1) * 2 * kMnGroupBytes + ((lane >> 2) & 3) * kMnPieceBytes +
+                          (g & 1) * 32 + (lane & 3) * 8;
+    const char* p = op + kk * 4 * kMnGroupBytes + (half * 4 + i) * 4 * kMnPieceBytes + lane_part;
+    const bf16x4_t lo = tr_read(p);
+    const bf16x4_t hi = tr_read(p + kMnGroupBytes);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  static constexpr int kReadsPerFrag = 2;
 };
 
 // ---------------------------------------------------------------------------
@@ -166,19 +265,17 @@ struct Frags {
   bf16x8_t a[4], b[4];
 };
 
+template <class SA, class SB>
 __device__ __forceinline__ void read_frags(const char* stage, int kk, int lane, int wm, int wn,
                                            Frags& f) {
-  const int r = lane & 31;
-  const int c = kk * 2 + (lane >> 5);
-  const int o = lds_off(r, c);  // swizzle depends only on lane & 31 (see header)
-  const char* a = stage + wm * 128 * kRowBytes + o;
-  const char* b = stage + kOperandStageBytes + wn * 128 * kRowBytes + o;
+  const char* a = stage;
+  const char* b = stage + kOperandStageBytes;
   // first-use order of mfma_step: a0 with b0..b3, then a1, a2, a3
-  f.a[0] = *reinterpret_cast<const bf16x8_t*>(a);
+  f.a[0] = SA::frag(a, kk, lane, wm, 0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t*>(b + j * 32 * kRowBytes);
+  for (int j = 0; j < 4; ++j) f.b[j] = SB::frag(b, kk, lane, wn, j);
 #pragma unroll
-  for (int i = 1; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(a + i * 32 * kRowBytes);
+  for (int i = 1; i < 4; ++i) f.a[i] = SA::frag(a, kk, lane, wm, i);
 }
 
 __device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][4]) {
@@ -189,21 +286,10 @@ __device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][4])
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-__device__ __forceinline__ void issue_stage(const TileSrc& A, const TileSrc& B, int kt, int nk,
-                                            char* st) {
+template <class SA, class SB>
+__device__ __forceinline__ void issue_stage(const SA& A, const SB& B, int kt, int nk, char* st) {
   A.issue(kt, nk, st);
   B.issue(kt, nk, st + kOperandStageBytes);
-}
-
-// Waits until at most `ahead` stages of this wave's loads are in flight.
-__device__ __forceinline__ void wait_stages_ahead(int ahead) {
-  static_assert(kStages <= 3, "extend the cases below");
-  if (ahead >= 2)
-    wait_vmcnt<2 * kLoadsPerWaveStage>();
-  else if (ahead == 1)
-    wait_vmcnt<kLoadsPerWaveStage>();
-  else
-    wait_vmcnt<0>();
 }
 
 // sched_group_barrier masks
@@ -211,30 +297,28 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
 
+// LDS read instructions per 16-wide k step for operand layouts SA, SB (8..16).
+template <class SA, class SB>
+constexpr int reads_per_step() {
+  return 4 * (SA::kReadsPerFrag + SB::kReadsPerFrag);
+}
+
 // Runs one 16-wide MFMA k step from `cur` while reading the fragments of k
 // step `kk` of `stage` into `nxt`, one LDS read between consecutive MFMAs.
-template <int ID>
+template <class SA, class SB, int ID>
 __device__ __forceinline__ void step_and_read(const char* stage, int kk, int lane, int wm, int wn,
                                               const Frags& cur, Frags& nxt,
                                               f32x16_t (&acc)[4][4]) {
-  read_frags(stage, kk, lane, wm, wn, nxt);
+  constexpr int nr = reads_per_step<SA, SB>();
+  read_frags<SA, SB>(stage, kk, lane, wm, wn, nxt);
   mfma_step(cur, acc);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, ID);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, ID);
+    if (i < nr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, ID);
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, ID);
   __builtin_amdgcn_sched_barrier(0);
 }
-
-// The two LDS ring slots are separate __shared__ objects (slot0, slot1) and
-// the loop is unrolled by two, so every LDS access names a fixed slot: the
-// compiler can then see that a stage's fragment reads never alias the
-// direct-to-LDS loads in flight into the other slot, and inserts no waits.
-struct Ring {
-  char* slot[kStages];
-};
 
 // One stage of kBK = 4 MFMA k steps from slot `cur`. On entry f0 holds the
 // stage's kk = 0 fragments. kk = 1..3 are read from LDS while the previous k
@@ -243,31 +327,28 @@ struct Ring {
 // stage's kk = 0 fragments are read from `nxt` during the last 16 MFMAs.
 // Every stage runs this same straight-line body: stages past the end of K are
 // zeros, so the loop can run in pairs over an even number of stages.
-__device__ __forceinline__ void k_step(const TileSrc& A, const TileSrc& B, int kt, int nk,
-                                       char* cur, char* nxt, int lane, int wm, int wn, Frags& f0,
-                                       Frags& f1, f32x16_t (&acc)[4][4]) {
+template <class SA, class SB>
+__device__ __forceinline__ void k_step(const SA& A, const SB& B, int kt, int nk, char* cur,
+                                       char* nxt, int lane, int wm, int wn, Frags& f0, Frags& f1,
+                                       f32x16_t (&acc)[4][4]) {
+  constexpr int nr = reads_per_step<SA, SB>();
   __builtin_amdgcn_sched_barrier(0);
-  step_and_read<0>(cur, 1, lane, wm, wn, f0, f1, acc);
-  step_and_read<1>(cur, 2, lane, wm, wn, f1, f0, acc);
-  step_and_read<2>(cur, 3, lane, wm, wn, f0, f1, acc);
+  step_and_read<SA, SB, 0>(cur, 1, lane, wm, wn, f0, f1, acc);
+  step_and_read<SA, SB, 1>(cur, 2, lane, wm, wn, f1, f0, acc);
+  step_and_read<SA, SB, 2>(cur, 3, lane, wm, wn, f0, f1, acc);
   // stage kt + 1 must have landed; with two stages nothing newer is in flight
   wait_vmcnt<0>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   issue_stage(A, B, kt + kStages, nk, cur);
-  read_frags(nxt, 0, lane, wm, wn, f0);
+  read_frags<SA, SB>(nxt, 0, lane, wm, wn, f0);
   mfma_step(f1, acc);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 3);
     __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 3);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 3);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 3);
-    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 3);
+    if (i < nr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 3);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -275,7 +356,8 @@ __device__ __forceinline__ void k_step(const TileSrc& A, const TileSrc& B, int k
 // Accumulates the tile over nk stages of kBK. The caller must have made the
 // LDS ring free (barrier) before the call; on return every wave has finished
 // its LDS reads and no load is in flight.
-__device__ __forceinline__ void mainloop(const TileSrc& A, const TileSrc& B, int nk, char* slot0,
+template <class SA, class SB>
+__device__ __forceinline__ void mainloop(const SA& A, const SB& B, int nk, char* slot0,
                                          char* slot1, f32x16_t (&acc)[4][4]) {
   static_assert(kStages == 2, "the loop below is unrolled for a two-slot ring");
   const int lane = threadIdx.x & 63;
@@ -297,7 +379,7 @@ __device__ __forceinline__ void mainloop(const TileSrc& A, const TileSrc& B, int
   __builtin_amdgcn_s_barrier();
 
   Frags f0, f1;
-  read_frags(slot0, 0, lane, wm, wn, f0);
+  read_frags<SA, SB>(slot0, 0, lane, wm, wn, f0);
   for (int kt = 0; kt < nk; kt += 2) {
     k_step(A, B, kt, nk, slot0, slot1, lane, wm, wn, f0, f1, acc);
     k_step(A, B, kt + 1, nk, slot1, slot0, lane, wm, wn, f0, f1, acc);

@@ -14,12 +14,14 @@
 // Backward (twinkle PR #283 section 1: recompute the softmax from saved inputs;
 // SkyRL PR #2374 review: entropy is saved by the forward, not recomputed):
 //   1. k_zero_rows   +0.0 dX rows at skipped positions
-//   2. k_gather      X_c = X[kept] (bf16), the k-operand of dW
+//   2. k_gather_rows X_c = X[kept] (bf16)
 //   3. per chunk of kept rows:
 //      k_dz_tiles    recompute Z^T tile, p = exp(z - LSE),
-//                    dZ = g_lp (onehot - p) - g_H p (z - LSE + H), bf16
-//      k_dx_tiles    dX[kept rows] = dZ W             (K = vocab)
-//      k_dw_tiles    dW (+)= dZ^T X_c                 (K = chunk rows)
+//                    dZ = g_lp (onehot - p) - g_H p (z - LSE + H), bf16,
+//                    stored token-major [c][v]
+//      k_dx_tiles    dX[kept rows] = dZ W    (K = vocab; W read MN-major)
+//      k_dw_tiles    dW (+)= dZ^T X_c        (K = chunk rows; dZ and X_c read
+//                                             MN-major, no transposed copies)
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -38,12 +40,12 @@ namespace lmh {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Default token chunk: the largest multiple of 256 rows whose two bf16 dZ
-// buffers (token-major and vocab-major) fit this budget. The pages' fused head
-// defaults to 8192 rows to bound memory on an 80 GB part; with 288 GB of HBM
-// the budget admits a whole 16K-token batch at V = 131072, which saves the
+// Default token chunk: the largest multiple of 256 rows whose bf16 dZ buffer
+// fits this budget. The pages' fused head defaults to 8192 rows to bound
+// memory on an 80 GB part; with 288 GB of HBM the budget admits a whole
+// 16K-token batch at V = 131072 (4 GiB of dZ), which saves the
 // read-modify-write of dW between chunks.
-constexpr int64_t kDefaultDzBudget = int64_t(16) << 30;
+constexpr int64_t kDefaultDzBudget = int64_t(8) << 30;
 constexpr int kVersion = 100;  // 0.1.0
 
 // ---------------------------------------------------------------------------
@@ -103,39 +105,33 @@ static inline FwdWs fwd_ws(int64_t N, int64_t H, int64_t V) {
   return w;
 }
 
-// Backward geometry: chunk capacity C (rows, multiple of 256), dZ pitch ldz
-// (V rounded up to 256), WT pitch ldv (V rounded up to 64), XcT pitch ldc.
+// Backward geometry: chunk capacity C (rows, multiple of 256) and dZ pitch
+// ldz (V rounded up to 256).
 struct BwdGeom {
-  int64_t C, ldz, ldv, ldc;
+  int64_t C, ldz;
 };
 static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
   BwdGeom g;
   int64_t want = token_chunk;
   if (want <= 0) {
-    want = kDefaultDzBudget / (4 * round_up(V, 256)) / 256 * 256;
+    want = kDefaultDzBudget / (2 * round_up(V, 256)) / 256 * 256;
     if (want < 256) want = 256;
   }
   g.C = N > 0 ? std::min(round_up(want, 256), round_up(N, 256)) : 0;
   g.ldz = round_up(V, 256);
-  g.ldv = round_up(V, 64);
-  g.ldc = round_up(N + 64, 64);
   return g;
 }
 
-// Backward workspace: Xc [N][H] | XcT [H][ldc] | WT [H][ldv] | dZ [C][ldz] |
-// dZT [ldz][C], all bf16.
+// Backward workspace: Xc [N][H] | dZ [C][ldz], both bf16.
 struct BwdWs {
-  size_t xc, xct, wt, dz, dzt, total;
+  size_t xc, dz, total;
 };
 static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
   const BwdGeom g = bwd_geom(N, V, token_chunk);
   BwdWs w;
   w.xc = 0;
-  w.xct = w.xc + align256((size_t)N * (size_t)H * 2);
-  w.wt = w.xct + align256((size_t)H * (size_t)g.ldc * 2);
-  w.dz = w.wt + align256((size_t)H * (size_t)g.ldv * 2);
-  w.dzt = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
-  w.total = w.dzt + align256((size_t)g.ldz * (size_t)g.C * 2);
+  w.dz = w.xc + align256((size_t)N * (size_t)H * 2);
+  w.total = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
   return w;
 }
 
@@ -234,78 +230,6 @@ __global__ void k_gather_rows(const uint16_t* __restrict__ X, const SavedHeader*
 }
 
 // ---------------------------------------------------------------------------
-// 64 x 64 tile transposes through LDS (bf16).
-//   k_transpose_w : WT[h][v] = W[v][h]           (v < V; zero for V <= v < ldv)
-//   k_gather_cols : XcT[h][c] = X[kept_idx[c]][h] (c < n_kept; zero up to ldc)
-// ---------------------------------------------------------------------------
-constexpr int kTp = 64;
-constexpr int kTpPitch = kTp + 8;
-
-__device__ __forceinline__ void transpose_tile(uint16_t (*t)[kTpPitch], uint16_t* __restrict__ out,
-                                               int64_t ld_out) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int r = tid / 8 + 32 * it;  // output row (h)
-    const int ch = tid % 8;           // 8 consecutive output columns
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)t[ch * 8 + 2 * e][r] | ((uint32_t)t[ch * 8 + 2 * e + 1][r] << 16);
-    *reinterpret_cast<uint4*>(out + (int64_t)r * ld_out + ch * 8) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-__global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict__ W, int V, int H,
-                                                     uint16_t* __restrict__ WT, int64_t ldv) {
-  __shared__ uint16_t t[kTp][kTpPitch];
-  const int v0 = blockIdx.x * kTp, h0 = blockIdx.y * kTp;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int r = tid / 8 + 32 * it;
-    const int ch = tid % 8;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (v0 + r < V) x = *reinterpret_cast<const uint4*>(W + (int64_t)(v0 + r) * H + h0 + ch * 8);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      t[r][ch * 8 + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
-      t[r][ch * 8 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
-    }
-  }
-  __syncthreads();
-  transpose_tile(t, WT + (int64_t)h0 * ldv + v0, ldv);
-}
-
-__global__ __launch_bounds__(256) void k_gather_cols(const uint16_t* __restrict__ X,
-                                                     const SavedHeader* __restrict__ hdr,
-                                                     const int32_t* __restrict__ kept_idx, int H,
-                                                     uint16_t* __restrict__ XcT, int64_t ldc) {
-  __shared__ uint16_t t[kTp][kTpPitch];
-  const int n_kept = hdr->n_kept;
-  const int c0 = blockIdx.x * kTp, h0 = blockIdx.y * kTp;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int r = tid / 8 + 32 * it;
-    const int ch = tid % 8;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (c0 + r < n_kept)
-      x = *reinterpret_cast<const uint4*>(X + (int64_t)kept_idx[c0 + r] * H + h0 + ch * 8);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      t[r][ch * 8 + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
-      t[r][ch * 8 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
-    }
-  }
-  __syncthreads();
-  transpose_tile(t, XcT + (int64_t)h0 * ldc + c0, ldc);
-}
-
-// ---------------------------------------------------------------------------
 // Forward tiles: M = vocab (A = W rows), N = kept tokens (B = Xc rows), K = H.
 // The epilogue reduces over the tile's 256 vocab rows per token.
 // ---------------------------------------------------------------------------
@@ -346,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     tile_coords<LMH_GM_FWD>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    TileSrc A, B;
+    KSrc A, B;
     A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
     B.init(P.Xc + (int64_t)tn * kBN * P.H, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
@@ -499,8 +423,7 @@ struct DzParams {
   int H, V, n_vt;
   int c0, C;     // chunk start (compact rows) and chunk capacity (multiple of 256)
   int64_t ldz;   // dZ row pitch (V rounded up to 256)
-  uint16_t* dZ;  // [C][ldz]   token-major: the A operand of dX = dZ W
-  uint16_t* dZT; // [ldz][C]   vocab-major: the A operand of dW = dZ^T Xc
+  uint16_t* dZ;  // [C][ldz] token-major: A of dX = dZ W and of dW = dZ^T Xc
 };
 
 // bf16 pairs: (__bf16)x rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950)
@@ -531,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     tile_coords<LMH_GM_DZ>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    TileSrc A, B;
+    KSrc A, B;
     A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
     B.init(xc + (int64_t)tn * kBN * P.H, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
@@ -589,10 +512,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           for (int r = 0; r < 16; ++r)
             if (want == i * 16 + r) acc[i][j][r] += glp;
       }
-      // dZ[c][v]: four consecutive v per register group (8 bytes);
-      // dZT[v][c]: one element per register, 32 lanes give 64 contiguous bytes
+      // dZ[c][v]: four consecutive v per register group (8 bytes)
       uint16_t* zrow = P.dZ + (int64_t)c * P.ldz;
-      uint16_t* tcol = P.dZT + c;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -603,24 +524,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           const uint32_t plo = __builtin_bit_cast(uint32_t, lo);
           const uint32_t phi = __builtin_bit_cast(uint32_t, hi);
           *reinterpret_cast<uint2*>(zrow + v0) = make_uint2(plo, phi);
-          tcol[(int64_t)(v0 + 0) * P.C] = (uint16_t)plo;
-          tcol[(int64_t)(v0 + 1) * P.C] = (uint16_t)(plo >> 16);
-          tcol[(int64_t)(v0 + 2) * P.C] = (uint16_t)phi;
-          tcol[(int64_t)(v0 + 3) * P.C] = (uint16_t)(phi >> 16);
         }
     }
   }
 }
 
-// dX[kept rows] = dZ W: M = chunk rows (A = dZ), N = H (B = WT rows), K = vocab.
+// dX[kept rows] = dZ W: M = chunk rows (A = dZ rows, K-major), N = H (B = W,
+// MN-major: k = v rows, n = h contiguous), K = vocab.
 struct DxParams {
   const uint16_t* dZ;  // [C][ldz]
-  const uint16_t* WT;  // [H][ldv]
+  const uint16_t* W;   // [V][H]
   SavedView sv;
   int H, V;
   int c0, C;
-  int64_t ldz, ldv;
-  int kv;  // K extent: V rounded up to kBK (dZ and WT are zero past V)
+  int64_t ldz;
   float* dX;
 };
 
@@ -638,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nk = P.kv / kBK;
+  const int nk = (P.V + kBK - 1) / kBK;  // W reads zero past V
   const int32_t* kidx = P.sv.kept_idx + P.c0;
 
   for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
@@ -648,9 +565,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     tile_coords<LMH_GM_DX>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    TileSrc A, B;
+    KSrc A;
+    MNSrc B;
     A.init(P.dZ + (int64_t)tm * kBM * P.ldz, P.ldz, rows - tm * kBM);
-    B.init(P.WT + (int64_t)tn * kBN * P.ldv, P.ldv, P.H - tn * kBN);
+    B.init(P.W + (int64_t)tn * kBN, P.H, P.V, P.H - tn * kBN);
     f32x16_t acc[4][4];
     mainloop(A, B, nk, slot0, slot1, acc);
 
@@ -670,14 +588,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   }
 }
 
-// dW (+)= dZ^T Xc: M = vocab (A = dZT rows), N = H (B = XcT rows), K = chunk rows.
+// dW (+)= dZ^T Xc: M = vocab, N = H, K = chunk rows; both operands MN-major
+// (A = dZ [c][v], B = Xc [c][h]).
 struct DwParams {
-  const uint16_t* dZT;  // [ldz][C]
-  const uint16_t* XcT;  // [H][ldc], this chunk starts at column c0
+  const uint16_t* dZ;  // [C][ldz]
+  const uint16_t* Xc;  // [n_kept][H]; this chunk starts at row c0
   const SavedHeader* hdr;
   int H, V;
   int c0, C;
-  int64_t ldc;
+  int64_t ldz;
   int accumulate;
   float* dW;
 };
@@ -699,7 +618,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nk = (rows + kBK - 1) / kBK;  // dZT is zero past `rows`
+  const int nk = (rows + kBK - 1) / kBK;  // rows past `rows` read as zero
+  const uint16_t* xc = P.Xc + (int64_t)P.c0 * P.H;
 
   for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
     const int t = xcd_logical(round, gridDim.x);
@@ -708,9 +628,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     tile_coords<LMH_GM_DW>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    TileSrc A, B;
-    A.init(P.dZT + (int64_t)tm * kBM * P.C, P.C, P.V - tm * kBM);
-    B.init(P.XcT + (int64_t)tn * kBN * P.ldc + P.c0, P.ldc, P.H - tn * kBN);
+    MNSrc A, B;
+    A.init(P.dZ + (int64_t)tm * kBM, P.ldz, rows, kBM);  // ldz covers every m of the tile
+    B.init(xc + (int64_t)tn * kBN, P.H, rows, P.H - tn * kBN);
     f32x16_t acc[4][4];
     mainloop(A, B, nk, slot0, slot1, acc);
 
@@ -777,11 +697,11 @@ static int check_sizes(int64_t N, int64_t H, int64_t V) {
 // the launch stream around every launch while profiling is on.
 enum KernelKind {
   KK_COMPACT = 0, KK_GATHER_ROWS, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS,
-  KK_GATHER_COLS, KK_TRANSPOSE_W, KK_DZ, KK_DX, KK_DW, KK_COUNT
+  KK_DZ, KK_DX, KK_DW, KK_COUNT
 };
 static const char* const kKernelNames[KK_COUNT] = {
-    "compact",     "gather_rows", "fwd_tiles", "merge",    "zero_skipped", "zero_rows",
-    "gather_cols", "transpose_w", "dz_tiles",  "dx_tiles", "dw_tiles"};
+    "compact",   "gather_rows", "fwd_tiles", "merge",   "zero_skipped",
+    "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles"};
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -934,10 +854,7 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
   SavedView sv = saved_view(const_cast<void*>(saved), N);
   char* w = static_cast<char*>(workspace);
   uint16_t* Xc = reinterpret_cast<uint16_t*>(w + L.xc);
-  uint16_t* XcT = reinterpret_cast<uint16_t*>(w + L.xct);
-  uint16_t* WT = reinterpret_cast<uint16_t*>(w + L.wt);
   uint16_t* dZ = reinterpret_cast<uint16_t*>(w + L.dz);
-  uint16_t* dZT = reinterpret_cast<uint16_t*>(w + L.dzt);
   const uint16_t* X = static_cast<const uint16_t*>(hidden);
   const uint16_t* Wt = static_cast<const uint16_t*>(weight);
 
@@ -946,12 +863,6 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
                    (const int32_t*)sv.pos, (int)N, (int)H, grad_hidden));
     LMH_TRY(launch(KK_GATHER_ROWS, k_gather_rows, dim3((unsigned)N), dim3(256), s, X,
                    (const SavedHeader*)sv.hdr, (const int32_t*)sv.kept_idx, (int)H, Xc));
-    LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(G.ldc / kTp), (unsigned)(H / kTp)),
-                   dim3(256), s, X, (const SavedHeader*)sv.hdr, (const int32_t*)sv.kept_idx,
-                   (int)H, XcT, G.ldc));
-    LMH_TRY(launch(KK_TRANSPOSE_W, k_transpose_w,
-                   dim3((unsigned)(G.ldv / kTp), (unsigned)(H / kTp)), dim3(256), s, Wt, (int)V,
-                   (int)H, WT, G.ldv));
   }
 
   const int nv = n_vtiles(V);
@@ -973,34 +884,31 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       D.C = (int)G.C;
       D.ldz = G.ldz;
       D.dZ = dZ;
-      D.dZT = dZT;
       const int64_t dz_tiles = (int64_t)nv * (G.C / kBN);
       LMH_TRY(launch(KK_DZ, k_dz_tiles, dim3(persistent_grid(dz_tiles)), dim3(kThreads), s, D));
 
       DxParams X2;
       X2.dZ = dZ;
-      X2.WT = WT;
+      X2.W = Wt;
       X2.sv = sv;
       X2.H = (int)H;
       X2.V = (int)V;
       X2.c0 = c0;
       X2.C = (int)G.C;
       X2.ldz = G.ldz;
-      X2.ldv = G.ldv;
-      X2.kv = (int)round_up(V, kBK);
       X2.dX = grad_hidden;
       const int64_t dx_tiles = (G.C / kBM) * ((H + kBN - 1) / kBN);
       LMH_TRY(launch(KK_DX, k_dx_tiles, dim3(persistent_grid(dx_tiles)), dim3(kThreads), s, X2));
     }
     DwParams Wp;
-    Wp.dZT = dZT;
-    Wp.XcT = XcT;
+    Wp.dZ = dZ;
+    Wp.Xc = Xc;
     Wp.hdr = sv.hdr;
     Wp.H = (int)H;
     Wp.V = (int)V;
     Wp.c0 = c0;
     Wp.C = (int)G.C;
-    Wp.ldc = G.ldc;
+    Wp.ldz = G.ldz;
     Wp.accumulate = ch > 0;
     Wp.dW = grad_weight;
     const int64_t dw_tiles = (int64_t)nv * ((H + kBN - 1) / kBN);
