@@ -12,20 +12,24 @@
 //   MNSrc : MN-major, [k][ld] with mn contiguous (e.g. W[v][h] as the B of
 //           dX = dZ W, K = v, n = h).
 //
-// K advances in stages of kBK = 64 through a ring of two LDS stages (128 KiB).
-// Stages are loaded straight from global memory into LDS with
+// K advances in stages of kBK = 32 through a ring of four LDS stages (4 x
+// 32 KiB). Stages are loaded straight from global memory into LDS with
 // buffer_load_dwordx4 ... lds (no VGPR staging); the buffer descriptor's
-// record count zero-fills rows past the end of the matrix. One barrier per
-// stage both publishes stage k + 1 and frees the slot of stage k for stage
-// k + 2. MFMA fragments are double-buffered in registers: the fragments of the
-// next 16-wide k step are read from LDS while the current step's 16 MFMAs
-// issue.
+// record count zero-fills rows past the end of the matrix. The loads of stage
+// k + 3 go into the slot that stage k - 1 released and are spread over the
+// whole of stage k, one load per four MFMAs: a CU moves about 150 GB/s through
+// these loads, twice what the MFMAs consume on average, so loads bunched into
+// a fraction of a stage would stall the issuing wave. One barrier per stage
+// publishes stage k + 1 and releases the slot of stage k. MFMA fragments are
+// double-buffered in registers: the fragments of the next 16-wide k step are
+// read from LDS while the current step's 16 MFMAs issue.
 //
-// LDS stage layouts (32 KiB per operand, 256 mn x 64 k bf16):
-//   K-major : 256 rows (one per m or n) of 128 bytes (64 k); the 16-byte chunk
-//             index is XOR-swizzled with (row >> 1) & 7. Fragments are read
-//             with ds_read_b128 (lane l: row l % 32, chunk 2 kk + l / 32).
-//   MN-major: 16 groups of 4 consecutive k rows, 2 KiB each. Inside a group
+// LDS stage layouts (16 KiB per operand, 256 mn x 32 k bf16):
+//   K-major : 256 rows (one per m or n) of 64 bytes (32 k); the 16-byte chunk
+//             index is XOR-swizzled with (row >> 2) & 3, which keeps the
+//             fragment reads (ds_read_b128, lane l: row l % 32, chunk
+//             2 kk + l / 32) free of bank conflicts.
+//   MN-major: 8 groups of 4 consecutive k rows, 2 KiB each. Inside a group
 //             the 64-byte piece (32 mn values) of k row e in 32-wide mn block
 //             s sits at byte (4 s + e) * 64, i.e. the four k rows are
 //             interleaved piece by piece. Fragments are read with
@@ -58,17 +62,17 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBK = 64;                                      // k per stage
+constexpr int kBK = 32;                                      // k per stage
 constexpr int kChunks = kBK / 8;                             // 16-byte chunks per K-major row
-constexpr int kRowBytes = kBK * 2;                           // 128: one L2 line per row
-constexpr int kStages = 2;
+constexpr int kRowBytes = kBK * 2;                           // 64: half an L2 line per row
+constexpr int kStages = 4;
 constexpr int kThreads = 256;
-constexpr int kOperandStageBytes = kBM * kRowBytes;          // 32 KiB
+constexpr int kOperandStageBytes = kBM * kRowBytes;          // 16 KiB
 constexpr int kStageBytes = 2 * kOperandStageBytes;          // A then B
 constexpr int kRingBytes = kStages * kStageBytes;            // 128 KiB
 constexpr int kRowsPerLoad = 1024 / kRowBytes;               // rows per 1 KiB LDS-DMA load
-constexpr int kLoadsPerWaveOperand = (kBM / 4) / kRowsPerLoad;  // 8
-constexpr int kLoadsPerWaveStage = 2 * kLoadsPerWaveOperand;    // 16
+constexpr int kLoadsPerWaveOperand = (kBM / 4) / kRowsPerLoad;  // 4
+constexpr int kLoadsPerWaveStage = 2 * kLoadsPerWaveOperand;    // 8
 constexpr uint32_t kOOB = 0x80000000u;  // voffset beyond every record count
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
@@ -78,7 +82,7 @@ constexpr int kMnGroupBytes = 4 * kMnRowBytes;      // 2 KiB: 4 interleaved k ro
 constexpr int kMnPieceBytes = 64;                   // 32 mn values of one k row
 static_assert(kBK / 4 * kMnGroupBytes == kOperandStageBytes, "MN-major stage size");
 
-__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & (kChunks - 1); }
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 2) & (kChunks - 1); }
 
 // Byte offset of (row, 16-byte chunk) inside one K-major operand stage.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
@@ -173,8 +177,8 @@ struct MNSrc {
     const int cq = lane & 3;           // 16-byte chunk inside the piece
 #pragma unroll
     for (int j = 0; j < kLoadsPerWaveOperand; ++j) {
-      // load j fills half (j & 1) of group 4 wave + j / 2 of the stage
-      const int row = (wave * 4 + (j >> 1)) * 4 + e;
+      // load j fills half (j & 1) of group kGroupsPerWave wave + j / 2 of the stage
+      const int row = (wave * kGroupsPerWave + (j >> 1)) * 4 + e;
       const int col = ((j & 1) * 4 + blk) * 32 + cq * 8;
       off[j] = col < mn_valid ? (uint32_t)(row * pitch + col * 2) : kOOB;
     }
@@ -184,7 +188,7 @@ struct MNSrc {
   // covers only the valid rows of the stage (none at or past k_valid).
   __device__ __forceinline__ void issue(int kt, int /*nk*/, char* dst) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    char* ldsb = dst + wave * 4 * kMnGroupBytes;
+    char* ldsb = dst + wave * kGroupsPerWave * kMnGroupBytes;
     int rows = k_valid - kt * kBK;
     rows = rows < 0 ? 0 : (rows > kBK ? kBK : rows);
     void* p = reinterpret_cast<void*>(uniform_u64(base + (uint64_t)((int64_t)kt * kBK * pitch)));
@@ -213,6 +217,7 @@ struct MNSrc {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   static constexpr int kReadsPerFrag = 2;
+  static constexpr int kGroupsPerWave = kBK / 4 / 4;  // 4-row groups each wave loads per stage
 };
 
 // ---------------------------------------------------------------------------
@@ -225,9 +230,10 @@ struct MNSrc {
 // panels in that XCD's L2.
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;
-// Group widths (m-tiles per group) of each GEMM, chosen by a timing sweep
-// over 1..32 at N=16384 H=4096 V=131072; a group is swept with m
-// fastest, so an XCD's 32 concurrent tiles cover gm m-tiles by 32 / gm n-tiles.
+// Group widths (m-tiles per group) of each GEMM; a group is swept with m
+// fastest, so an XCD's 32 concurrent tiles cover gm m-tiles by 32 / gm n-tiles
+// and read gm + 32 / gm operand panels (12 for gm = 8, the fewest). Timed at
+// N=16384 H=4096 V=131072 on random operands, 4 and 8 tie and 16 is slower.
 #ifndef LMH_GM_FWD
 #define LMH_GM_FWD 8
 #endif
@@ -235,10 +241,10 @@ constexpr int kXcds = 8;
 #define LMH_GM_DZ 8
 #endif
 #ifndef LMH_GM_DX
-#define LMH_GM_DX 16
+#define LMH_GM_DX 8
 #endif
 #ifndef LMH_GM_DW
-#define LMH_GM_DW 16
+#define LMH_GM_DW 8
 #endif
 
 __device__ __forceinline__ int xcd_logical(int round, int grid) {
@@ -261,6 +267,13 @@ __device__ __forceinline__ void tile_coords(int t, int mt, int nt, int& tm, int&
 // ---------------------------------------------------------------------------
 // Main loop.
 // ---------------------------------------------------------------------------
+// The ring's slots must be distinct __shared__ objects named at every access
+// (see mainloop); kernels declare them with this macro.
+#define LMH_DECLARE_RING                                                  \
+  __shared__ __attribute__((aligned(1024))) char slot0[lmh::kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char slot1[lmh::kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char slot2[lmh::kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char slot3[lmh::kStageBytes]
 struct Frags {
   bf16x8_t a[4], b[4];
 };
@@ -286,12 +299,6 @@ __device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][4])
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-template <class SA, class SB>
-__device__ __forceinline__ void issue_stage(const SA& A, const SB& B, int kt, int nk, char* st) {
-  A.issue(kt, nk, st);
-  B.issue(kt, nk, st + kOperandStageBytes);
-}
-
 // sched_group_barrier masks
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
@@ -303,63 +310,62 @@ constexpr int reads_per_step() {
   return 4 * (SA::kReadsPerFrag + SB::kReadsPerFrag);
 }
 
-// Runs one 16-wide MFMA k step from `cur` while reading the fragments of k
-// step `kk` of `stage` into `nxt`, one LDS read between consecutive MFMAs.
-template <class SA, class SB, int ID>
-__device__ __forceinline__ void step_and_read(const char* stage, int kk, int lane, int wm, int wn,
-                                              const Frags& cur, Frags& nxt,
-                                              f32x16_t (&acc)[4][4]) {
+// Interleaves the 16 MFMAs of a k step with its LDS reads (one after each
+// MFMA) and, with LOADS, the kLoadsPerWaveOperand loads of one operand (one
+// per four MFMAs).
+template <class SA, class SB, bool LOADS, int ID>
+__device__ __forceinline__ void interleave() {
   constexpr int nr = reads_per_step<SA, SB>();
-  read_frags<SA, SB>(stage, kk, lane, wm, wn, nxt);
-  mfma_step(cur, acc);
+  constexpr int every = 16 / kLoadsPerWaveOperand;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, ID);
+    if (LOADS && i % every == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, ID);
     if (i < nr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, ID);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One stage of kBK = 4 MFMA k steps from slot `cur`. On entry f0 holds the
-// stage's kk = 0 fragments. kk = 1..3 are read from LDS while the previous k
-// step's MFMAs issue; before the last k step every wave publishes stage kt + 1
-// (wait + barrier), the loads of stage kt + 2 go into `cur`, and the next
-// stage's kk = 0 fragments are read from `nxt` during the last 16 MFMAs.
-// Every stage runs this same straight-line body: stages past the end of K are
-// zeros, so the loop can run in pairs over an even number of stages.
+// One stage of kBK = 2 MFMA k steps from slot `cur`. On entry f0 holds the
+// stage's kk = 0 fragments and slot `fre` is free (its stage kt - 1 was
+// released by the previous barrier). Step 1 runs kk = 0 while reading kk = 1
+// into f1 and issuing stage kt + 3's A loads into `fre`. Then every wave
+// waits for its loads of stage kt + 1 (at most the 8 loads of stage kt + 2
+// and the 4 just issued may remain) and for its LDS reads, and the barrier
+// publishes stage kt + 1 and releases `cur`. Step 2 runs kk = 1 while reading
+// stage kt + 1's kk = 0 fragments from `nxt` and issuing stage kt + 3's B loads.
+// Stages past the end of K are zeros, so every stage runs this same body.
 template <class SA, class SB>
-__device__ __forceinline__ void k_step(const SA& A, const SB& B, int kt, int nk, char* cur,
-                                       char* nxt, int lane, int wm, int wn, Frags& f0, Frags& f1,
-                                       f32x16_t (&acc)[4][4]) {
-  constexpr int nr = reads_per_step<SA, SB>();
+__device__ __forceinline__ void k_stage(const SA& A, const SB& B, int kt, int nk, const char* cur,
+                                        const char* nxt, char* fre, int lane, int wm, int wn,
+                                        Frags& f0, Frags& f1, f32x16_t (&acc)[4][4]) {
+  static_assert(kStages == 4 && kLoadsPerWaveOperand == 4, "waits below assume this ring");
   __builtin_amdgcn_sched_barrier(0);
-  step_and_read<SA, SB, 0>(cur, 1, lane, wm, wn, f0, f1, acc);
-  step_and_read<SA, SB, 1>(cur, 2, lane, wm, wn, f1, f0, acc);
-  step_and_read<SA, SB, 2>(cur, 3, lane, wm, wn, f0, f1, acc);
-  // stage kt + 1 must have landed; with two stages nothing newer is in flight
-  wait_vmcnt<0>();
+  read_frags<SA, SB>(cur, 1, lane, wm, wn, f1);
+  A.issue(kt + 3, nk, fre);
+  mfma_step(f0, acc);
+  interleave<SA, SB, true, 0>();
+  wait_vmcnt<kLoadsPerWaveStage + kLoadsPerWaveOperand>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  issue_stage(A, B, kt + kStages, nk, cur);
   read_frags<SA, SB>(nxt, 0, lane, wm, wn, f0);
+  B.issue(kt + 3, nk, fre + kOperandStageBytes);
   mfma_step(f1, acc);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 3);
-    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 3);
-    if (i < nr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 3);
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  interleave<SA, SB, true, 1>();
 }
 
 // Accumulates the tile over nk stages of kBK. The caller must have made the
 // LDS ring free (barrier) before the call; on return every wave has finished
-// its LDS reads and no load is in flight.
+// its LDS reads and no load is in flight. The four slots are distinct
+// __shared__ objects and the loop is unrolled by four, so every LDS access
+// names a fixed slot: the compiler can then see that fragment reads never
+// alias the direct-to-LDS loads in flight into other slots, and inserts no
+// waits of its own.
 template <class SA, class SB>
 __device__ __forceinline__ void mainloop(const SA& A, const SB& B, int nk, char* slot0,
-                                         char* slot1, f32x16_t (&acc)[4][4]) {
-  static_assert(kStages == 2, "the loop below is unrolled for a two-slot ring");
+                                         char* slot1, char* slot2, char* slot3,
+                                         f32x16_t (&acc)[4][4]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1;
@@ -373,18 +379,24 @@ __device__ __forceinline__ void mainloop(const SA& A, const SB& B, int nk, char*
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   if (nk <= 0) return;
 
-  issue_stage(A, B, 0, nk, slot0);
-  issue_stage(A, B, 1, nk, slot1);
-  wait_vmcnt<kLoadsPerWaveStage>();
+  A.issue(0, nk, slot0);
+  B.issue(0, nk, slot0 + kOperandStageBytes);
+  A.issue(1, nk, slot1);
+  B.issue(1, nk, slot1 + kOperandStageBytes);
+  A.issue(2, nk, slot2);
+  B.issue(2, nk, slot2 + kOperandStageBytes);
+  wait_vmcnt<2 * kLoadsPerWaveStage>();
   __builtin_amdgcn_s_barrier();
 
   Frags f0, f1;
   read_frags<SA, SB>(slot0, 0, lane, wm, wn, f0);
-  for (int kt = 0; kt < nk; kt += 2) {
-    k_step(A, B, kt, nk, slot0, slot1, lane, wm, wn, f0, f1, acc);
-    k_step(A, B, kt + 1, nk, slot1, slot0, lane, wm, wn, f0, f1, acc);
+  for (int kt = 0; kt < nk; kt += 4) {
+    k_stage(A, B, kt, nk, slot0, slot1, slot3, lane, wm, wn, f0, f1, acc);
+    k_stage(A, B, kt + 1, nk, slot1, slot2, slot0, lane, wm, wn, f0, f1, acc);
+    k_stage(A, B, kt + 2, nk, slot2, slot3, slot1, lane, wm, wn, f0, f1, acc);
+    k_stage(A, B, kt + 3, nk, slot3, slot0, slot2, lane, wm, wn, f0, f1, acc);
   }
-  // the last pair issued two zero stages that nobody reads; let them land
+  // the last stages issued zero loads that nobody reads; let them land
   wait_vmcnt<0>();
   wait_lgkm0();
 }

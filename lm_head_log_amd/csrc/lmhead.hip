@@ -5,23 +5,25 @@
 // expand back; SkyRL PR #2374 "How it works": one projection gives both the
 // selected-token log-prob and the entropy):
 //   1. k_compact     keep mask -> ascending kept rows, row -> compact position
-//   2. k_fwd_tiles   Z^T tile = W[vtile] X[kept]^T on MFMA, never stored; per
+//   2. k_transpose_w W^T, k_gather_cols X[kept]^T: the MN-major operands of
+//                    the logit GEMM (k = h rows, vocabulary / tokens contiguous)
+//   3. k_fwd_tiles   Z^T tile = W[vtile] X[kept]^T on MFMA, never stored; per
 //                    token: max, sum 2^(y), sum 2^(y) y over the tile's 256
 //                    vocab rows (y = z log2 e - max), and the target logit
-//   3. k_merge       fixed-order merge of the vocab-tile partials ->
+//   4. k_merge       fixed-order merge of the vocab-tile partials ->
 //                    log-sum-exp, entropy, log-prob; scatter to kept rows
-//   4. k_zero_skipped  +0.0 log-prob / entropy at skipped rows
+//   5. k_zero_skipped  +0.0 log-prob / entropy at skipped rows
 // Backward (twinkle PR #283 section 1: recompute the softmax from saved inputs;
 // SkyRL PR #2374 review: entropy is saved by the forward, not recomputed):
 //   1. k_zero_rows   +0.0 dX rows at skipped positions
-//   2. k_gather_rows X_c = X[kept] (bf16)
+//   2. k_gather_rows X_c = X[kept]; k_gather_cols X_c^T; k_transpose_w W^T
 //   3. per chunk of kept rows:
 //      k_dz_tiles    recompute Z^T tile, p = exp(z - LSE),
 //                    dZ = g_lp (onehot - p) - g_H p (z - LSE + H), bf16,
-//                    stored token-major [c][v]
-//      k_dx_tiles    dX[kept rows] = dZ W    (K = vocab; W read MN-major)
-//      k_dw_tiles    dW (+)= dZ^T X_c        (K = chunk rows; dZ and X_c read
-//                                             MN-major, no transposed copies)
+//                    stored token-major [c][v] and vocab-major [v][c]
+//      k_dx_tiles    dX[kept rows] = dZ W    (K = vocab: dZ^T and W)
+//      k_dw_tiles    dW (+)= dZ^T X_c        (K = chunk rows: dZ and X_c)
+// Every GEMM reads both operands MN-major (k rows, m or n contiguous).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -40,12 +42,12 @@ namespace lmh {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Default token chunk: the largest multiple of 256 rows whose bf16 dZ buffer
-// fits this budget. The pages' fused head defaults to 8192 rows to bound
-// memory on an 80 GB part; with 288 GB of HBM the budget admits a whole
-// 16K-token batch at V = 131072 (4 GiB of dZ), which saves the
-// read-modify-write of dW between chunks.
-constexpr int64_t kDefaultDzBudget = int64_t(8) << 30;
+// Default token chunk: the largest multiple of 256 rows whose two bf16 dZ
+// buffers (token-major and vocab-major) fit this budget. The pages' fused
+// head defaults to 8192 rows to bound memory on an 80 GB part; with 288 GB of
+// HBM the budget admits a whole 16K-token batch at V = 131072 (4 GiB per
+// layout), which saves the read-modify-write of dW between chunks.
+constexpr int64_t kDefaultDzBudget = int64_t(16) << 30;
 constexpr int kVersion = 100;  // 0.1.0
 
 // ---------------------------------------------------------------------------
@@ -88,10 +90,14 @@ static inline SavedView saved_view(void* base, int64_t N) {
 static inline int n_vtiles(int64_t V) { return (int)((V + kBM - 1) / kBM); }
 static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Pitches of the transposed operand copies: W^T [H][ldv], X_c^T [H][ldc].
+static inline int64_t ldv_of(int64_t V) { return round_up(V, 64); }
+static inline int64_t ldc_of(int64_t N) { return round_up(N, 64); }
+
 // Forward workspace: target logits [N] | partial m, s, b [n_vt][N] each |
-// gathered kept rows Xc [N][H] (bf16).
+// X_c^T [H][ldc] | W^T [H][ldv] (bf16).
 struct FwdWs {
-  size_t zt, pm, ps, pb, xc, total;
+  size_t zt, pm, ps, pb, xct, wt, total;
 };
 static inline FwdWs fwd_ws(int64_t N, int64_t H, int64_t V) {
   const size_t nv = (size_t)n_vtiles(V);
@@ -100,8 +106,9 @@ static inline FwdWs fwd_ws(int64_t N, int64_t H, int64_t V) {
   w.pm = w.zt + align256((size_t)N * 4);
   w.ps = w.pm + align256(nv * (size_t)N * 4);
   w.pb = w.ps + align256(nv * (size_t)N * 4);
-  w.xc = w.pb + align256(nv * (size_t)N * 4);
-  w.total = w.xc + align256((size_t)N * (size_t)H * 2);
+  w.xct = w.pb + align256(nv * (size_t)N * 4);
+  w.wt = w.xct + align256((size_t)H * (size_t)ldc_of(N) * 2);
+  w.total = w.wt + align256((size_t)H * (size_t)ldv_of(V) * 2);
   return w;
 }
 
@@ -114,7 +121,7 @@ static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
   BwdGeom g;
   int64_t want = token_chunk;
   if (want <= 0) {
-    want = kDefaultDzBudget / (2 * round_up(V, 256)) / 256 * 256;
+    want = kDefaultDzBudget / (4 * round_up(V, 256)) / 256 * 256;
     if (want < 256) want = 256;
   }
   g.C = N > 0 ? std::min(round_up(want, 256), round_up(N, 256)) : 0;
@@ -122,16 +129,20 @@ static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
   return g;
 }
 
-// Backward workspace: Xc [N][H] | dZ [C][ldz], both bf16.
+// Backward workspace: X_c [N][H] | X_c^T [H][ldc] | W^T [H][ldv] |
+// dZ [C][ldz] | dZ^T [ldz][C], all bf16.
 struct BwdWs {
-  size_t xc, dz, total;
+  size_t xc, xct, wt, dz, dzt, total;
 };
 static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
   const BwdGeom g = bwd_geom(N, V, token_chunk);
   BwdWs w;
   w.xc = 0;
-  w.dz = w.xc + align256((size_t)N * (size_t)H * 2);
-  w.total = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
+  w.xct = w.xc + align256((size_t)N * (size_t)H * 2);
+  w.wt = w.xct + align256((size_t)H * (size_t)ldc_of(N) * 2);
+  w.dz = w.wt + align256((size_t)H * (size_t)ldv_of(V) * 2);
+  w.dzt = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
+  w.total = w.dzt + align256((size_t)g.ldz * (size_t)g.C * 2);
   return w;
 }
 
@@ -230,16 +241,83 @@ __global__ void k_gather_rows(const uint16_t* __restrict__ X, const SavedHeader*
 }
 
 // ---------------------------------------------------------------------------
-// Forward tiles: M = vocab (A = W rows), N = kept tokens (B = Xc rows), K = H.
-// The epilogue reduces over the tile's 256 vocab rows per token.
+// 64 x 64 tile transposes through LDS (bf16), zero-filled past the valid
+// columns so that every MN-major tile reads finite values:
+//   k_transpose_w : WT[h][v] = W[v][h]            (zero for V <= v < ldv)
+//   k_gather_cols : XcT[h][c] = X[kept_idx[c]][h] (zero for n_kept <= c < ldc)
+// ---------------------------------------------------------------------------
+constexpr int kTp = 64;
+constexpr int kTpPitch = kTp + 8;  // 144-byte rows: column reads hit distinct banks
+
+// Loads rows r (< 64) of the tile as 8-element chunks: src(r) is the row's
+// first element, or null for a zero row.
+template <class RowPtr>
+__device__ __forceinline__ void tile_load(uint16_t (*t)[kTpPitch], RowPtr src) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int r = tid / 8 + 32 * it;
+    const int ch = tid % 8;
+    const uint16_t* p = src(r);
+    const uint4 x = p ? *reinterpret_cast<const uint4*>(p + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(&t[r][ch * 8]) = x;
+  }
+}
+
+// Writes the transpose of the LDS tile: out row h (< 64) gets t[.][h].
+__device__ __forceinline__ void tile_store_t(uint16_t (*t)[kTpPitch], uint16_t* __restrict__ out,
+                                             int64_t ld_out) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int h = tid / 8 + 32 * it;
+    const int ch = tid % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)t[ch * 8 + 2 * e][h] | ((uint32_t)t[ch * 8 + 2 * e + 1][h] << 16);
+    *reinterpret_cast<uint4*>(out + (int64_t)h * ld_out + ch * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict__ W, int V, int H,
+                                                     uint16_t* __restrict__ WT, int64_t ldv) {
+  __shared__ uint16_t t[kTp][kTpPitch];
+  const int v0 = blockIdx.x * kTp, h0 = blockIdx.y * kTp;
+  tile_load(t, [&](int r) -> const uint16_t* {
+    return v0 + r < V ? W + (int64_t)(v0 + r) * H + h0 : nullptr;
+  });
+  __syncthreads();
+  tile_store_t(t, WT + (int64_t)h0 * ldv + v0, ldv);
+}
+
+__global__ __launch_bounds__(256) void k_gather_cols(const uint16_t* __restrict__ X,
+                                                     const SavedHeader* __restrict__ hdr,
+                                                     const int32_t* __restrict__ kept_idx, int H,
+                                                     uint16_t* __restrict__ XcT, int64_t ldc) {
+  __shared__ uint16_t t[kTp][kTpPitch];
+  const int n_kept = hdr->n_kept;
+  const int c0 = blockIdx.x * kTp, h0 = blockIdx.y * kTp;
+  tile_load(t, [&](int r) -> const uint16_t* {
+    return c0 + r < n_kept ? X + (int64_t)kept_idx[c0 + r] * H + h0 : nullptr;
+  });
+  __syncthreads();
+  tile_store_t(t, XcT + (int64_t)h0 * ldc + c0, ldc);
+}
+
+// ---------------------------------------------------------------------------
+// Forward tiles: M = vocab (A = W^T, MN-major), N = kept tokens (B = X_c^T,
+// MN-major), K = H. The epilogue reduces over the tile's 256 vocab rows per
+// token.
 // ---------------------------------------------------------------------------
 struct FwdParams {
-  const uint16_t* W;
-  const uint16_t* Xc;
+  const uint16_t* WT;   // [H][ldv]
+  const uint16_t* XcT;  // [H][ldc]
   const int32_t* targets;
   const int32_t* kept_idx;
   const SavedHeader* hdr;
   int H, V, n_vt;
+  int64_t ldv, ldc;
   int64_t ldp;  // pitch (elements) between vocab tiles in the partial arrays
   float* pm;
   float* ps;
@@ -248,8 +326,7 @@ struct FwdParams {
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
-  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
+  LMH_DECLARE_RING;
   // per-token partials of the two wave rows; reuses ring slot 0 after the main loop
   float (*red)[3][kBN] = reinterpret_cast<float (*)[3][kBN]>(slot0);
 
@@ -270,11 +347,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     tile_coords<LMH_GM_FWD>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    KSrc A, B;
-    A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
-    B.init(P.Xc + (int64_t)tn * kBN * P.H, P.H, rows - tn * kBN);
+    MNSrc A, B;
+    A.init(P.WT + (int64_t)tm * kBM, P.ldv, P.H, P.V - tm * kBM);
+    B.init(P.XcT + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, slot0, slot1, acc);
+    mainloop(A, B, nk, slot0, slot1, slot2, slot3, acc);
 
     const int vbase = tm * kBM + wm * 128;
     const bool full = vbase + 128 <= P.V;
@@ -414,24 +491,25 @@ __global__ void k_zero_rows(const int32_t* __restrict__ pos, int N, int H, float
 }
 
 struct DzParams {
-  const uint16_t* W;
-  const uint16_t* Xc;
+  const uint16_t* WT;   // [H][ldv]
+  const uint16_t* XcT;  // [H][ldc]
   const int32_t* targets;
   const float* g_lp;
   const float* g_h;  // null when the entropy term is off
   SavedView sv;
   int H, V, n_vt;
   int c0, C;     // chunk start (compact rows) and chunk capacity (multiple of 256)
+  int64_t ldv, ldc;
   int64_t ldz;   // dZ row pitch (V rounded up to 256)
-  uint16_t* dZ;  // [C][ldz] token-major: A of dX = dZ W and of dW = dZ^T Xc
+  uint16_t* dZ;  // [C][ldz] token-major: A of dW = dZ^T Xc
+  uint16_t* dZT; // [ldz][C] vocab-major: A of dX = dZ W
 };
 
 // bf16 pairs: (__bf16)x rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
-  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
+  LMH_DECLARE_RING;
 
   const int n_kept = P.sv.hdr->n_kept;
   const int rows = min(P.C, n_kept - P.c0);
@@ -445,7 +523,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = P.H / kBK;
   const int32_t* kidx = P.sv.kept_idx + P.c0;
-  const uint16_t* xc = P.Xc + (int64_t)P.c0 * P.H;
+  // this wave's 128 x 128 bf16 staging tile for the vocab-major store
+  char* tw = wave == 0 ? slot0 : wave == 1 ? slot1 : wave == 2 ? slot2 : slot3;
+  static_assert(kStageBytes == 128 * 128 * 2, "one ring slot per wave tile");
 
   for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
     const int t = xcd_logical(round, gridDim.x);
@@ -454,13 +534,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     tile_coords<LMH_GM_DZ>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    KSrc A, B;
-    A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
-    B.init(xc + (int64_t)tn * kBN * P.H, P.H, rows - tn * kBN);
+    MNSrc A, B;
+    A.init(P.WT + (int64_t)tm * kBM, P.ldv, P.H, P.V - tm * kBM);
+    B.init(P.XcT + P.c0 + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, slot0, slot1, acc);
+    mainloop(A, B, nk, slot0, slot1, slot2, slot3, acc);
+    __syncthreads();  // every wave is done reading the ring
 
     const int vbase = tm * kBM + wm * 128;
+    const int cbase = tn * kBN + wn * 128;
     // full: every vocab row of this wave and every token of the tile is valid
     const bool full = vbase + 128 <= P.V && tn * kBN + kBN <= rows;
 #pragma unroll
@@ -512,8 +594,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           for (int r = 0; r < 16; ++r)
             if (want == i * 16 + r) acc[i][j][r] += glp;
       }
-      // dZ[c][v]: four consecutive v per register group (8 bytes)
+      // dZ[c][v]: four consecutive v per register group (8 bytes); the
+      // vocab-major copy goes through LDS (element (v, c) at row v, column c)
       uint16_t* zrow = P.dZ + (int64_t)c * P.ldz;
+      char* tcol = tw + (j * 32 + (lane & 31)) * 2;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -524,26 +608,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           const uint32_t plo = __builtin_bit_cast(uint32_t, lo);
           const uint32_t phi = __builtin_bit_cast(uint32_t, hi);
           *reinterpret_cast<uint2*>(zrow + v0) = make_uint2(plo, phi);
+          const int vl = v0 - vbase;
+          *reinterpret_cast<uint16_t*>(tcol + (vl + 0) * 256) = (uint16_t)plo;
+          *reinterpret_cast<uint16_t*>(tcol + (vl + 1) * 256) = (uint16_t)(plo >> 16);
+          *reinterpret_cast<uint16_t*>(tcol + (vl + 2) * 256) = (uint16_t)phi;
+          *reinterpret_cast<uint16_t*>(tcol + (vl + 3) * 256) = (uint16_t)(phi >> 16);
         }
+    }
+    // dZ^T[v][c]: each 256-byte LDS row (one v, 128 tokens) goes out as 16-byte
+    // stores; 16 lanes write one row. Invalid rows and columns hold zeros.
+#pragma unroll 8
+    for (int it = 0; it < 32; ++it) {
+      const int q = it * 64 + lane;
+      const int vl = q >> 4, ch = q & 15;
+      const uint4 x = *reinterpret_cast<const uint4*>(tw + vl * 256 + ch * 16);
+      *reinterpret_cast<uint4*>(P.dZT + (int64_t)(vbase + vl) * P.C + cbase + ch * 8) = x;
     }
   }
 }
 
-// dX[kept rows] = dZ W: M = chunk rows (A = dZ rows, K-major), N = H (B = W,
-// MN-major: k = v rows, n = h contiguous), K = vocab.
+// dX[kept rows] = dZ W: M = chunk rows (A = dZ^T: k = v rows, tokens
+// contiguous), N = H (B = W: k = v rows, h contiguous), K = vocab.
 struct DxParams {
-  const uint16_t* dZ;  // [C][ldz]
-  const uint16_t* W;   // [V][H]
+  const uint16_t* dZT;  // [ldz][C]
+  const uint16_t* W;    // [V][H]
   SavedView sv;
   int H, V;
   int c0, C;
-  int64_t ldz;
   float* dX;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
-  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
+  LMH_DECLARE_RING;
 
   const int n_kept = P.sv.hdr->n_kept;
   const int rows = min(P.C, n_kept - P.c0);
@@ -565,12 +661,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     tile_coords<LMH_GM_DX>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    KSrc A;
-    MNSrc B;
-    A.init(P.dZ + (int64_t)tm * kBM * P.ldz, P.ldz, rows - tm * kBM);
+    MNSrc A, B;
+    A.init(P.dZT + (int64_t)tm * kBM, P.C, P.V, rows - tm * kBM);
     B.init(P.W + (int64_t)tn * kBN, P.H, P.V, P.H - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, slot0, slot1, acc);
+    mainloop(A, B, nk, slot0, slot1, slot2, slot3, acc);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -602,8 +697,7 @@ struct DwParams {
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
-  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
+  LMH_DECLARE_RING;
 
   const int n_kept = P.hdr->n_kept;
   int rows = min(P.C, n_kept - P.c0);
@@ -632,7 +726,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     A.init(P.dZ + (int64_t)tm * kBM, P.ldz, rows, kBM);  // ldz covers every m of the tile
     B.init(xc + (int64_t)tn * kBN, P.H, rows, P.H - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, slot0, slot1, acc);
+    mainloop(A, B, nk, slot0, slot1, slot2, slot3, acc);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -697,11 +791,11 @@ static int check_sizes(int64_t N, int64_t H, int64_t V) {
 // the launch stream around every launch while profiling is on.
 enum KernelKind {
   KK_COMPACT = 0, KK_GATHER_ROWS, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS,
-  KK_DZ, KK_DX, KK_DW, KK_COUNT
+  KK_GATHER_COLS, KK_TRANSPOSE_W, KK_DZ, KK_DX, KK_DW, KK_COUNT
 };
 static const char* const kKernelNames[KK_COUNT] = {
-    "compact",   "gather_rows", "fwd_tiles", "merge",   "zero_skipped",
-    "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles"};
+    "compact",     "gather_rows", "fwd_tiles", "merge",    "zero_skipped", "zero_rows",
+    "gather_cols", "transpose_w", "dz_tiles",  "dx_tiles", "dw_tiles"};
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -800,14 +894,20 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
 
   const int nv = n_vtiles(V);
   char* w = static_cast<char*>(workspace);
-  uint16_t* Xc = reinterpret_cast<uint16_t*>(w + L.xc);
-  LMH_TRY(launch(KK_GATHER_ROWS, k_gather_rows, dim3((unsigned)N), dim3(256), s,
-                 static_cast<const uint16_t*>(hidden), (const SavedHeader*)sv.hdr,
-                 (const int32_t*)sv.kept_idx, (int)H, Xc));
+  const int64_t ldc = ldc_of(N), ldv = ldv_of(V);
+  uint16_t* XcT = reinterpret_cast<uint16_t*>(w + L.xct);
+  uint16_t* WT = reinterpret_cast<uint16_t*>(w + L.wt);
+  LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(ldc / kTp), (unsigned)(H / kTp)),
+                 dim3(256), s, static_cast<const uint16_t*>(hidden), (const SavedHeader*)sv.hdr,
+                 (const int32_t*)sv.kept_idx, (int)H, XcT, ldc));
+  LMH_TRY(launch(KK_TRANSPOSE_W, k_transpose_w, dim3((unsigned)(ldv / kTp), (unsigned)(H / kTp)),
+                 dim3(256), s, static_cast<const uint16_t*>(weight), (int)V, (int)H, WT, ldv));
 
   FwdParams P;
-  P.W = static_cast<const uint16_t*>(weight);
-  P.Xc = Xc;
+  P.WT = WT;
+  P.XcT = XcT;
+  P.ldv = ldv;
+  P.ldc = ldc;
   P.targets = targets;
   P.kept_idx = sv.kept_idx;
   P.hdr = sv.hdr;
@@ -854,15 +954,24 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
   SavedView sv = saved_view(const_cast<void*>(saved), N);
   char* w = static_cast<char*>(workspace);
   uint16_t* Xc = reinterpret_cast<uint16_t*>(w + L.xc);
+  uint16_t* XcT = reinterpret_cast<uint16_t*>(w + L.xct);
+  uint16_t* WT = reinterpret_cast<uint16_t*>(w + L.wt);
   uint16_t* dZ = reinterpret_cast<uint16_t*>(w + L.dz);
+  uint16_t* dZT = reinterpret_cast<uint16_t*>(w + L.dzt);
   const uint16_t* X = static_cast<const uint16_t*>(hidden);
   const uint16_t* Wt = static_cast<const uint16_t*>(weight);
+  const int64_t ldc = ldc_of(N), ldv = ldv_of(V);
 
   if (N > 0) {
     LMH_TRY(launch(KK_ZERO_ROWS, k_zero_rows, dim3((unsigned)N), dim3(256), s,
                    (const int32_t*)sv.pos, (int)N, (int)H, grad_hidden));
     LMH_TRY(launch(KK_GATHER_ROWS, k_gather_rows, dim3((unsigned)N), dim3(256), s, X,
                    (const SavedHeader*)sv.hdr, (const int32_t*)sv.kept_idx, (int)H, Xc));
+    LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(ldc / kTp), (unsigned)(H / kTp)),
+                   dim3(256), s, X, (const SavedHeader*)sv.hdr, (const int32_t*)sv.kept_idx,
+                   (int)H, XcT, ldc));
+    LMH_TRY(launch(KK_TRANSPOSE_W, k_transpose_w, dim3((unsigned)(ldv / kTp), (unsigned)(H / kTp)),
+                   dim3(256), s, Wt, (int)V, (int)H, WT, ldv));
   }
 
   const int nv = n_vtiles(V);
@@ -871,8 +980,10 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
     const int c0 = (int)(ch * G.C);
     if (N > 0) {
       DzParams D;
-      D.W = Wt;
-      D.Xc = Xc;
+      D.WT = WT;
+      D.XcT = XcT;
+      D.ldv = ldv;
+      D.ldc = ldc;
       D.targets = targets;
       D.g_lp = grad_logp;
       D.g_h = entropy_requires_grad ? grad_entropy : nullptr;
@@ -884,18 +995,18 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       D.C = (int)G.C;
       D.ldz = G.ldz;
       D.dZ = dZ;
+      D.dZT = dZT;
       const int64_t dz_tiles = (int64_t)nv * (G.C / kBN);
       LMH_TRY(launch(KK_DZ, k_dz_tiles, dim3(persistent_grid(dz_tiles)), dim3(kThreads), s, D));
 
       DxParams X2;
-      X2.dZ = dZ;
+      X2.dZT = dZT;
       X2.W = Wt;
       X2.sv = sv;
       X2.H = (int)H;
       X2.V = (int)V;
       X2.c0 = c0;
       X2.C = (int)G.C;
-      X2.ldz = G.ldz;
       X2.dX = grad_hidden;
       const int64_t dx_tiles = (G.C / kBM) * ((H + kBN - 1) / kBN);
       LMH_TRY(launch(KK_DX, k_dx_tiles, dim3(persistent_grid(dx_tiles)), dim3(kThreads), s, X2));
