@@ -401,9 +401,13 @@ __device__ __forceinline__ void mainloop(const SA& A, const SB& B, int nk, char*
   wait_lgkm0();
 }
 
-// Row (within the wave's 128-row half) held by accumulator register r of block i.
-__device__ __forceinline__ int acc_row(int i, int r, int lane) {
-  return i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+// Row (within the wave's 128-row half) held by accumulator register r of
+// block i: acc_row_fixed(i, r) + acc_row_lane(lane). Epilogues compare the
+// compile-time part against a per-tile lane bound, so the compiler has no
+// per-register lane values to keep live across the tile loop.
+__host__ __device__ constexpr int acc_row_fixed(int i, int r) {
+  return i * 32 + 8 * (r >> 2) + (r & 3);
 }
+__device__ __forceinline__ int acc_row_lane(int lane) { return 4 * (lane >> 5); }
 
 }  // namespace lmh

@@ -42,6 +42,7 @@ namespace lmh {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kMaskedLogit = -1e30f;  // stands in for the logit of a vocabulary row past V
 // Default token chunk: the largest multiple of 256 rows whose two bf16 dZ
 // buffers (token-major and vocab-major) fit this budget. The pages' fused
 // head defaults to 8192 rows to bound memory on an 80 GB part; with 288 GB of
@@ -355,6 +356,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
 
     const int vbase = tm * kBM + wm * 128;
     const bool full = vbase + 128 <= P.V;
+    const int vlim = P.V - vbase - acc_row_lane(lane);  // rows acc_row_fixed < vlim are valid
+    const bool none = vlim <= 0;                         // this lane's rows are all past V
+    if (!full) {
+      // Rows at or past V get a large finite negative logit: exp2 of it minus
+      // any real maximum is exactly 0 and 0 * y stays finite. Done once for
+      // the four column blocks, so no per-row mask outlives this loop.
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = acc_row_fixed(i, r) < vlim;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j][r] = ok ? acc[i][j][r] : kMaskedLogit;
+        }
+    }
     __syncthreads();  // every wave is done reading the ring
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -364,19 +380,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool ok = full || (vbase + acc_row(i, r, lane) < P.V);
-          if (ok) mx = fmaxf(mx, acc[i][j][r]);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      if (none) mx = -INFINITY;
       float s = 0.f, b = 0.f;
       if (mx != -INFINITY) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const bool ok = full || (vbase + acc_row(i, r, lane) < P.V);
             const float y = (acc[i][j][r] - mx) * kLog2e;
-            const float e = ok ? __builtin_amdgcn_exp2f(y) : 0.f;
+            const float e = __builtin_amdgcn_exp2f(y);
             s += e;
             b = fmaf(e, y, b);
           }
@@ -543,8 +556,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
 
     const int vbase = tm * kBM + wm * 128;
     const int cbase = tn * kBN + wn * 128;
-    // full: every vocab row of this wave and every token of the tile is valid
-    const bool full = vbase + 128 <= P.V && tn * kBN + kBN <= rows;
+    // Tokens past the chunk's rows have ca = cb = 0 and a zero logit, so their
+    // dz is exactly 0. Vocabulary rows at or past V are not masked: those rows
+    // of dZ and dZ^T hold finite values that no consumer reads (dX masks k
+    // rows at or past V; dW never stores output rows at or past V).
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = tn * kBN + wn * 128 + j * 32 + (lane & 31);  // chunk row
@@ -574,15 +589,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           const float p = __builtin_amdgcn_exp2f(lp * kLog2e);
           acc[i][j][r] = p * fmaf(cb, lp, ca);
         }
-      if (!full) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool ok = crow && (vbase + acc_row(i, r, lane) < P.V);
-            acc[i][j][r] = ok ? acc[i][j][r] : 0.f;
-          }
-      }
       const int local = tt - vbase;
       const int w = local & 31;
       const bool hit = crow && local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
@@ -667,13 +673,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     f32x16_t acc[4][4];
     mainloop(A, B, nk, slot0, slot1, slot2, slot3, acc);
 
+    const int mrow = tm * kBM + wm * 128 + acc_row_lane(lane);
+    const int mlim = rows - mrow;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = tm * kBM + wm * 128 + acc_row(i, r, lane);
-        if (m >= rows) continue;
-        float* drow = P.dX + (int64_t)kidx[m] * P.H;
+        if (acc_row_fixed(i, r) >= mlim) continue;
+        float* drow = P.dX + (int64_t)kidx[mrow + acc_row_fixed(i, r)] * P.H;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = tn * kBN + wn * 128 + j * 32 + (lane & 31);
@@ -728,13 +735,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     f32x16_t acc[4][4];
     mainloop(A, B, nk, slot0, slot1, slot2, slot3, acc);
 
+    const int mrow = tm * kBM + wm * 128 + acc_row_lane(lane);
+    const int mlim = P.V - mrow;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = tm * kBM + wm * 128 + acc_row(i, r, lane);
-        if (m >= P.V) continue;
-        float* wrow = P.dW + (int64_t)m * P.H;
+        if (acc_row_fixed(i, r) >= mlim) continue;
+        float* wrow = P.dW + (int64_t)(mrow + acc_row_fixed(i, r)) * P.H;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = tn * kBN + wn * 128 + j * 32 + (lane & 31);
