@@ -228,7 +228,7 @@ def main():
             "N": N, "H": H, "V": V, "n_kept": n_kept,
             "keep_fraction": round(n_kept / max(N, 1), 4),
             "return_entropy": bool(ret), "entropy_requires_grad": bool(erg),
-            "token_chunk": args.token_chunk or "default (dZ budget 16 GiB)",
+            "token_chunk": args.token_chunk or "default (dZ budget 8 GiB)",
         },
         "tflops": round(tflops, 1),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),

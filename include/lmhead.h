@@ -80,19 +80,17 @@ size_t lmhead_saved_bytes(int64_t N);
 
 /* Workspace bytes lmhead_fwd needs for N rows and vocabulary V: per row the
  * target logit and, per 256-wide vocabulary tile, three fp32 partial
- * statistics, plus bf16 transposed copies of the kept rows of X ([H][N
- * rounded up to 64]) and of W ([H][V rounded up to 64]). Returns 0 on invalid
- * sizes. */
+ * statistics, plus a bf16 transposed copy of the kept rows of X ([H][N
+ * rounded up to 64]). Returns 0 on invalid sizes. */
 size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V);
 
-/* Workspace bytes lmhead_bwd needs: bf16 copies of the kept rows of X (row-
- * and column-major) and of W^T, plus the bf16 logit gradient dZ of one chunk
- * of C rows in token-major and vocab-major order ([C][V rounded up to 256]
- * and its transpose), where C = token_chunk rounded up to a multiple of 256
- * (at most N rounded up to 256). token_chunk <= 0 selects the largest chunk
- * whose two dZ buffers fit 16 GiB (prime-rl PR #3326, Overview, uses the chunk
- * to bound memory; its default of 8192 rows was set for a smaller memory).
- * Returns 0 on invalid sizes. */
+/* Workspace bytes lmhead_bwd needs: a bf16 transposed copy of the kept rows
+ * of X ([H][N rounded up to 64]) plus the bf16 logit gradient dZ of one chunk
+ * of C rows ([C][V rounded up to 256], token-major), where C = token_chunk
+ * rounded up to a multiple of 256 (at most N rounded up to 256).
+ * token_chunk <= 0 selects the largest chunk whose dZ fits 8 GiB (prime-rl PR
+ * #3326, Overview, uses the chunk to bound memory; its default of 8192 rows
+ * was set for a smaller memory). Returns 0 on invalid sizes. */
 size_t lmhead_bwd_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t token_chunk);
 
 /* Forward: compaction of the kept rows, the fused projection with per-row
@@ -164,10 +162,9 @@ const char* lmhead_status_string(int status);
 int lmhead_version(void);
 
 /* Per-kernel timing for benchmarks (not needed to use the op).
- * Kernel kinds, in order: compact, gather_rows, fwd_tiles, merge,
- * zero_skipped, zero_rows, gather_cols, transpose_w, dz_tiles, dx_tiles,
- * dw_tiles. */
-#define LMHEAD_NUM_KERNELS 11
+ * Kernel kinds, in order: compact, gather_cols, fwd_tiles, merge,
+ * zero_skipped, zero_rows, dz_tiles, dx_tiles, dw_tiles. */
+#define LMHEAD_NUM_KERNELS 9
 
 /* Static name of kernel kind `kind` (NULL if out of range). */
 const char* lmhead_kernel_name(int kind);

@@ -29,7 +29,7 @@ __all__ = [
     "DEFAULT_TOKEN_CHUNK", "lmhead_kernel_name", "lmhead_profile_begin", "lmhead_profile_end",
 ]
 
-DEFAULT_TOKEN_CHUNK = 0  # library default: largest chunk whose two dZ layouts fit 16 GiB
+DEFAULT_TOKEN_CHUNK = 0  # library default: largest chunk whose dZ fits 8 GiB
 
 
 def _L():

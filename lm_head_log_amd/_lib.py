@@ -31,7 +31,7 @@ SIGNATURES = {
     "lmhead_profile_end": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
 }
 
-NUM_KERNELS = 11
+NUM_KERNELS = 9
 
 _lib = None
 

@@ -5,43 +5,45 @@
 // Each wave owns a 128 x 128 sub-tile held as 4 x 4 MFMA accumulator blocks
 // (256 AGPRs).
 //
-// An operand is read from global memory in one of two layouts, chosen per GEMM
-// so that no operand ever needs a transposed copy:
-//   KSrc  : K-major, [mn][ld] with k contiguous (e.g. W[v][h] as the A of
-//           Z = W X^T, K = h);
-//   MNSrc : MN-major, [k][ld] with mn contiguous (e.g. W[v][h] as the B of
-//           dX = dZ W, K = v, n = h).
+// Operand layouts in global memory, one of each per GEMM:
+//   A : K-major, [m][ld] with k contiguous (e.g. W[v][h] for Z = W X^T);
+//   B : MN-major, [k][ld] with n contiguous (e.g. W[v][h] for dX = dZ W).
+// Every GEMM of the op can be arranged this way without a transposed copy of
+// a large operand.
 //
-// K advances in stages of kBK = 32 through a ring of four LDS stages (4 x
-// 32 KiB). Stages are loaded straight from global memory into LDS with
-// buffer_load_dwordx4 ... lds (no VGPR staging); the buffer descriptor's
-// record count zero-fills rows past the end of the matrix. The loads of stage
-// k + 3 go into the slot that stage k - 1 released and are spread over the
-// whole of stage k, one load per four MFMAs: a CU moves about 150 GB/s through
-// these loads, twice what the MFMAs consume on average, so loads bunched into
-// a fraction of a stage would stall the issuing wave. One barrier per stage
-// publishes stage k + 1 and releases the slot of stage k. MFMA fragments are
-// double-buffered in registers: the fragments of the next 16-wide k step are
-// read from LDS while the current step's 16 MFMAs issue.
+// Both operands are loaded straight from global memory into LDS with
+// buffer_load_dwordx4 ... lds (no VGPR staging); a buffer descriptor's record
+// count zero-fills rows past the end of a matrix. K advances in stages of
+// kBK = 32; each stage issues four loads per wave for each operand, spread
+// over the stage's MFMAs (one load per four MFMAs): a CU moves about 150 GB/s
+// through these loads, twice what its MFMAs consume on average, so loads
+// bunched into part of a stage stall the issuing wave. One barrier per stage
+// publishes stage k + 1 and releases the LDS of stage k - 1. MFMA fragments
+// are double-buffered in registers: the fragments of the next 16-wide k step
+// are read from LDS while the current step's 16 MFMAs issue.
 //
-// LDS stage layouts (16 KiB per operand, 256 mn x 32 k bf16):
-//   K-major : 256 rows (one per m or n) of 64 bytes (32 k); the 16-byte chunk
-//             index is XOR-swizzled with (row >> 2) & 3, which keeps the
-//             fragment reads (ds_read_b128, lane l: row l % 32, chunk
-//             2 kk + l / 32) free of bank conflicts.
-//   MN-major: 8 groups of 4 consecutive k rows, 2 KiB each. Inside a group
-//             the 64-byte piece (32 mn values) of k row e in 32-wide mn block
-//             s sits at byte (4 s + e) * 64, i.e. the four k rows are
-//             interleaved piece by piece. Fragments are read with
-//             ds_read_b64_tr_b16, which hands lane i of each 16-lane group
-//             element i % 4 of the 8 bytes addressed by lane 4 e + i / 4 as its
-//             element e: pointing lane 4 e + q at k row k0 + e, mn n0 + 4 q
-//             gives lane i the values (mn n0 + i, k k0 .. k0 + 3), which is the
-//             MFMA fragment shape; two such reads give the 8 k of a fragment.
-//             A half wave reads 4 whole pieces that are adjacent in LDS
-//             (256 contiguous bytes), so the reads are free of bank conflicts,
-//             and one direct-to-LDS load (1 KiB) fills half a group from
-//             4 rows x 256 contiguous global bytes.
+// LDS (160 KiB, all of it):
+//   A ring: three slots of one k pair (64 k, two stages), 32 KiB each. A row
+//     of the pair is 128 bytes, one whole L2 line: fetching K-major rows 64
+//     bytes at a time would split every line across two requests, and the L2
+//     fetches each 64-byte sector on its own miss. The 16-byte chunk index
+//     is XOR-swizzled with (row >> 1) & 7, which keeps the fragment reads
+//     (ds_read_b128, lane l: row l % 32, chunk 2 kq + l / 32) free of bank
+//     conflicts. The loads of pair p + 2 go into the slot pair p - 1
+//     released, half in each stage of pair p.
+//   B ring: four slots of one stage (32 k rows of 256 n, 512 bytes each:
+//     whole lines), 16 KiB each, laid out as 8 groups of 4 consecutive k rows,
+//     2 KiB per group. Inside a group the 64-byte piece (32 n values) of k row
+//     e in 32-wide n block s sits at byte (4 s + e) * 64. Fragments are read
+//     with ds_read_b64_tr_b16, which hands lane i of each 16-lane group element
+//     i % 4 of the 8 bytes addressed by lane 4 e + i / 4 as its element e:
+//     pointing lane 4 e + q at k row k0 + e, n n0 + 4 q gives lane i the
+//     values (n n0 + i, k k0 .. k0 + 3), the MFMA fragment shape; two such
+//     reads give the 8 k of a fragment. A half wave reads 4 whole pieces that
+//     are adjacent in LDS (256 contiguous bytes): no bank conflicts. The loads
+//     of stage k + 3 go into the slot stage k - 1 released.
+// A transpose read moves half the bytes of a ds_read_b128 in about the same
+// LDS time, so the engine reads one operand (A) with ds_read_b128.
 //
 // MFMA 32x32x16 bf16 register layout (lane l of 64):
 //   A fragment: row  l % 32, k = 8 * (l / 32) + [0..7]
@@ -62,31 +64,35 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBK = 32;                                      // k per stage
-constexpr int kChunks = kBK / 8;                             // 16-byte chunks per K-major row
-constexpr int kRowBytes = kBK * 2;                           // 64: half an L2 line per row
-constexpr int kStages = 4;
+constexpr int kBK = 32;         // k per stage
 constexpr int kThreads = 256;
-constexpr int kOperandStageBytes = kBM * kRowBytes;          // 16 KiB
-constexpr int kStageBytes = 2 * kOperandStageBytes;          // A then B
-constexpr int kRingBytes = kStages * kStageBytes;            // 128 KiB
-constexpr int kRowsPerLoad = 1024 / kRowBytes;               // rows per 1 KiB LDS-DMA load
-constexpr int kLoadsPerWaveOperand = (kBM / 4) / kRowsPerLoad;  // 4
-constexpr int kLoadsPerWaveStage = 2 * kLoadsPerWaveOperand;    // 8
 constexpr uint32_t kOOB = 0x80000000u;  // voffset beyond every record count
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-// MN-major stage geometry
-constexpr int kMnRowBytes = kBM * 2;                // 512: one k row of 256 mn values
-constexpr int kMnGroupBytes = 4 * kMnRowBytes;      // 2 KiB: 4 interleaved k rows
-constexpr int kMnPieceBytes = 64;                   // 32 mn values of one k row
-static_assert(kBK / 4 * kMnGroupBytes == kOperandStageBytes, "MN-major stage size");
+// A ring (K-major pairs)
+constexpr int kPairK = 2 * kBK;                      // 64 k per pair
+constexpr int kARowBytes = kPairK * 2;               // 128
+constexpr int kAChunks = kARowBytes / 16;            // 8
+constexpr int kASlotBytes = kBM * kARowBytes;        // 32 KiB
+constexpr int kARowsPerLoad = 1024 / kARowBytes;     // 8
+constexpr int kALoadsPerWavePair = (kBM / 4) / kARowsPerLoad;  // 8
+constexpr int kASlots = 3;
 
-__device__ __forceinline__ int lds_swz(int row) { return (row >> 2) & (kChunks - 1); }
+// B ring (MN-major stages)
+constexpr int kMnRowBytes = kBN * 2;                 // 512: one k row of 256 n values
+constexpr int kMnGroupBytes = 4 * kMnRowBytes;       // 2 KiB: 4 interleaved k rows
+constexpr int kMnPieceBytes = 64;                    // 32 n values of one k row
+constexpr int kBSlotBytes = kBK * kMnRowBytes;       // 16 KiB
+constexpr int kBLoadsPerWaveStage = kBK / 4 / 4 * 2;  // 4
+constexpr int kBSlots = 4;
 
-// Byte offset of (row, 16-byte chunk) inside one K-major operand stage.
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return (row * kChunks + (chunk ^ lds_swz(row))) * 16;
+constexpr int kLoadsPerWaveStage = kALoadsPerWavePair / 2 + kBLoadsPerWaveStage;  // 8
+constexpr int kLdsBytes = kASlots * kASlotBytes + kBSlots * kBSlotBytes;          // 160 KiB
+static_assert(kLdsBytes == 160 * 1024, "the rings fill the CU's LDS");
+
+// Byte offset of (row, 16-byte chunk) inside one A slot.
+__device__ __forceinline__ int a_lds_off(int row, int chunk) {
+  return (row * kAChunks + (chunk ^ ((row >> 1) & (kAChunks - 1)))) * 16;
 }
 
 // s_waitcnt with the given vmcnt and no wait on the other counters (gfx9
@@ -108,15 +114,15 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// A K-major operand tile source: rows row0 .. row0 + 255 of a [rows][ld]
-// bf16 matrix; rows at or past `rows_valid` read as zero.
-struct KSrc {
+// The K-major A operand of a tile: rows m0 .. m0 + 255 of a [rows][ld] bf16
+// matrix; rows at or past `rows` (counted from m0) read as zero.
+struct ASrc {
   __amdgpu_buffer_rsrc_t rsrc;
-  __amdgpu_buffer_rsrc_t none;          // zero records: every load reads zeros
-  uint32_t off[kLoadsPerWaveOperand];  // per load: byte offset of this lane's chunk at k = 0
+  __amdgpu_buffer_rsrc_t none;         // zero records: every load reads zeros
+  uint32_t off[kALoadsPerWavePair];   // per load: byte offset of this lane's chunk at k = 0
 
   // tile_base: element pointer of the tile's first row; ld: row pitch
-  // (elements, multiple of 8); rows: rows of this tile inside the matrix.
+  // (elements, multiple of 8; every row holds the K range rounded up to 64).
   __device__ __forceinline__ void init(const uint16_t* tile_base, int64_t ld, int rows) {
     rows = rows < 0 ? 0 : (rows > kBM ? kBM : rows);
     const int bytes = __builtin_amdgcn_readfirstlane((int)((int64_t)rows * ld * 2));
@@ -126,69 +132,71 @@ struct KSrc {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < kLoadsPerWaveOperand; ++j) {
-      const int row = wave * (kBM / 4) + j * kRowsPerLoad + lane / kChunks;
-      const int c = (lane % kChunks) ^ lds_swz(row);
+    for (int j = 0; j < kALoadsPerWavePair; ++j) {
+      const int row = wave * (kBM / 4) + j * kARowsPerLoad + lane / kAChunks;
+      const int c = (lane % kAChunks) ^ ((row >> 1) & (kAChunks - 1));
       off[j] = row < rows ? (uint32_t)(row * ld * 2 + c * 16) : kOOB;
     }
   }
-  // Issue this wave's loads of stage kt into the operand stage at `dst`;
-  // stages at or past nk read as zeros (zero-record descriptor).
-  __device__ __forceinline__ void issue(int kt, int nk, char* dst) const {
+  // Issue half h (loads 4 h .. 4 h + 3) of this wave's loads of k pair p into
+  // the A slot at `dst`; pairs at or past np read as zeros.
+  __device__ __forceinline__ void issue_half(int p, int np, int h, char* dst) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    char* base = dst + wave * (kBM / 4) * kRowBytes;
+    char* base = dst + wave * (kBM / 4) * kARowBytes;
     // the k offset rides in the scalar soffset field; rows past the end keep
     // voffset >= the record count whether or not soffset enters the check
-    const bool live = kt < nk;
-    const int koff = __builtin_amdgcn_readfirstlane(live ? kt * kRowBytes : 0);
+    const bool live = p < np;
+    const int koff = __builtin_amdgcn_readfirstlane(live ? p * kARowBytes : 0);
     const __amdgpu_buffer_rsrc_t r = live ? rsrc : none;
 #pragma unroll
-    for (int j = 0; j < kLoadsPerWaveOperand; ++j)
+    for (int jj = 0; jj < kALoadsPerWavePair / 2; ++jj) {
+      const int j = h * (kALoadsPerWavePair / 2) + jj;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + j * 1024), 16, off[j], koff,
                                                0, 0);
+    }
   }
-  // Fragment of k step kk, 32-row block i of the wave's 128-row half `half`.
-  static __device__ __forceinline__ bf16x8_t frag(const char* op, int kk, int lane, int half,
+  // Fragment of 16-wide k step kq (0..3) of the pair, 32-row block i of the
+  // wave's 128-row half `half`.
+  static __device__ __forceinline__ bf16x8_t frag(const char* slot, int kq, int lane, int half,
                                                   int i) {
-    const int o = lds_off(lane & 31, kk * 2 + (lane >> 5));  // swizzle depends on lane & 31 only
-    return *reinterpret_cast<const bf16x8_t*>(op + (half * 128 + i * 32) * kRowBytes + o);
+    const int o = a_lds_off(lane & 31, kq * 2 + (lane >> 5));  // swizzle depends on lane & 31 only
+    return *reinterpret_cast<const bf16x8_t*>(slot + (half * 128 + i * 32) * kARowBytes + o);
   }
-  static constexpr int kReadsPerFrag = 1;
 };
 
-// An MN-major operand tile source: columns mn0 .. mn0 + 255 of the k rows of a
-// [k_rows][ld] bf16 matrix (mn contiguous); k rows at or past k_rows and
-// columns at or past mn_valid (counted from mn0) read as zero.
-struct MNSrc {
-  uint64_t base;                        // byte address of (k 0, mn0); wave-uniform
+// The MN-major B operand of a tile: columns n0 .. n0 + 255 of the k rows of a
+// [k_rows][ld] bf16 matrix (n contiguous); k rows at or past k_rows and
+// columns at or past n_valid (counted from n0) read as zero.
+struct BSrc {
+  uint64_t base;                        // byte address of (k 0, n0); wave-uniform
   int64_t pitch;                        // bytes per k row; wave-uniform
   int k_valid;                          // wave-uniform
-  uint32_t off[kLoadsPerWaveOperand];  // per load: byte offset of this lane's chunk in a stage
+  uint32_t off[kBLoadsPerWaveStage];   // per load: byte offset of this lane's chunk in a stage
 
   __device__ __forceinline__ void init(const uint16_t* col_base, int64_t ld, int k_rows,
-                                       int mn_valid) {
+                                       int n_valid) {
     base = uniform_u64(reinterpret_cast<uint64_t>(col_base));
     pitch = (int64_t)uniform_u64((uint64_t)(ld * 2));
     k_valid = __builtin_amdgcn_readfirstlane(k_rows < 0 ? 0 : k_rows);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int e = (lane >> 2) & 3;     // k row inside the group
-    const int blk = lane >> 4;         // 32-wide mn block inside the half
+    const int blk = lane >> 4;         // 32-wide n block inside the half
     const int cq = lane & 3;           // 16-byte chunk inside the piece
 #pragma unroll
-    for (int j = 0; j < kLoadsPerWaveOperand; ++j) {
-      // load j fills half (j & 1) of group kGroupsPerWave wave + j / 2 of the stage
-      const int row = (wave * kGroupsPerWave + (j >> 1)) * 4 + e;
+    for (int j = 0; j < kBLoadsPerWaveStage; ++j) {
+      // load j fills half (j & 1) of group 2 wave + j / 2 of the stage
+      const int row = (wave * 2 + (j >> 1)) * 4 + e;
       const int col = ((j & 1) * 4 + blk) * 32 + cq * 8;
-      off[j] = col < mn_valid ? (uint32_t)(row * pitch + col * 2) : kOOB;
+      off[j] = col < n_valid ? (uint32_t)(row * pitch + col * 2) : kOOB;
     }
   }
-  // Issue this wave's loads of stage kt into the operand stage at `dst`. The
+  // Issue this wave's loads of stage kt into the B slot at `dst`. The
   // descriptor is rebased to the stage's first k row, and its record count
   // covers only the valid rows of the stage (none at or past k_valid).
-  __device__ __forceinline__ void issue(int kt, int /*nk*/, char* dst) const {
+  __device__ __forceinline__ void issue(int kt, char* dst) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    char* ldsb = dst + wave * kGroupsPerWave * kMnGroupBytes;
+    char* ldsb = dst + wave * 2 * kMnGroupBytes;
     int rows = k_valid - kt * kBK;
     rows = rows < 0 ? 0 : (rows > kBK ? kBK : rows);
     void* p = reinterpret_cast<void*>(uniform_u64(base + (uint64_t)((int64_t)kt * kBK * pitch)));
@@ -196,28 +204,27 @@ struct MNSrc {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p, (short)0, bytes,
                                                                        kRsrcWord3);
 #pragma unroll
-    for (int j = 0; j < kLoadsPerWaveOperand; ++j)
+    for (int j = 0; j < kBLoadsPerWaveStage; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r, (lds_ptr_t)(ldsb + (j >> 1) * kMnGroupBytes + (j & 1) * 1024), 16, off[j], 0, 0, 0);
   }
   static __device__ __forceinline__ bf16x4_t tr_read(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(lds_ptr_t)(p));
   }
-  // Fragment of k step kk, 32-wide mn block i of the wave's 128 half `half`.
-  static __device__ __forceinline__ bf16x8_t frag(const char* op, int kk, int lane, int half,
+  // Fragment of k step kk (0..1) of the stage, 32-wide n block i of the
+  // wave's 128 half `half`.
+  static __device__ __forceinline__ bf16x8_t frag(const char* slot, int kk, int lane, int half,
                                                   int i) {
-    // lane 16 g + 4 e + q reads k row 16 kk + 8 (g >> 1) + 4 h + e at mn
+    // lane 16 g + 4 e + q reads k row 16 kk + 8 (g >> 1) + 4 h + e at n
     // 128 half + 32 i + 16 (g & 1) + 4 q, for the two halves h of the fragment
     const int g = lane >> 4;
     const int lane_part = (g >> 1) * 2 * kMnGroupBytes + ((lane >> 2) & 3) * kMnPieceBytes +
                           (g & 1) * 32 + (lane & 3) * 8;
-    const char* p = op + kk * 4 * kMnGroupBytes + (half * 4 + i) * 4 * kMnPieceBytes + lane_part;
+    const char* p = slot + kk * 4 * kMnGroupBytes + (half * 4 + i) * 4 * kMnPieceBytes + lane_part;
     const bf16x4_t lo = tr_read(p);
     const bf16x4_t hi = tr_read(p + kMnGroupBytes);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  static constexpr int kReadsPerFrag = 2;
-  static constexpr int kGroupsPerWave = kBK / 4 / 4;  // 4-row groups each wave loads per stage
 };
 
 // ---------------------------------------------------------------------------
@@ -267,28 +274,38 @@ __device__ __forceinline__ void tile_coords(int t, int mt, int nt, int& tm, int&
 // ---------------------------------------------------------------------------
 // Main loop.
 // ---------------------------------------------------------------------------
-// The ring's slots must be distinct __shared__ objects named at every access
-// (see mainloop); kernels declare them with this macro.
-#define LMH_DECLARE_RING                                                  \
-  __shared__ __attribute__((aligned(1024))) char slot0[lmh::kStageBytes]; \
-  __shared__ __attribute__((aligned(1024))) char slot1[lmh::kStageBytes]; \
-  __shared__ __attribute__((aligned(1024))) char slot2[lmh::kStageBytes]; \
-  __shared__ __attribute__((aligned(1024))) char slot3[lmh::kStageBytes]
+struct Ring {
+  char* a[3];
+  char* b[4];
+};
+
+// The ring slots must be distinct __shared__ objects named at every access
+// (see mainloop); kernels declare them with this macro, which also defines
+// `ring`.
+#define LMH_DECLARE_RING                                                   \
+  __shared__ __attribute__((aligned(1024))) char ra0[lmh::kASlotBytes];    \
+  __shared__ __attribute__((aligned(1024))) char ra1[lmh::kASlotBytes];    \
+  __shared__ __attribute__((aligned(1024))) char ra2[lmh::kASlotBytes];    \
+  __shared__ __attribute__((aligned(1024))) char rb0[lmh::kBSlotBytes];    \
+  __shared__ __attribute__((aligned(1024))) char rb1[lmh::kBSlotBytes];    \
+  __shared__ __attribute__((aligned(1024))) char rb2[lmh::kBSlotBytes];    \
+  __shared__ __attribute__((aligned(1024))) char rb3[lmh::kBSlotBytes];    \
+  const lmh::Ring ring = {{ra0, ra1, ra2}, {rb0, rb1, rb2, rb3}}
+
 struct Frags {
   bf16x8_t a[4], b[4];
 };
 
-template <class SA, class SB>
-__device__ __forceinline__ void read_frags(const char* stage, int kk, int lane, int wm, int wn,
-                                           Frags& f) {
-  const char* a = stage;
-  const char* b = stage + kOperandStageBytes;
+// Fragments of one 16-wide k step: A data is k step kq (0..3) of the pair in
+// slot `as`, B data is k step kk (0..1) of the stage in slot `bs`.
+__device__ __forceinline__ void read_frags(const char* as, int kq, const char* bs, int kk,
+                                           int lane, int wm, int wn, Frags& f) {
   // first-use order of mfma_step: a0 with b0..b3, then a1, a2, a3
-  f.a[0] = SA::frag(a, kk, lane, wm, 0);
+  f.a[0] = ASrc::frag(as, kq, lane, wm, 0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = SB::frag(b, kk, lane, wn, j);
+  for (int j = 0; j < 4; ++j) f.b[j] = BSrc::frag(bs, kk, lane, wn, j);
 #pragma unroll
-  for (int i = 1; i < 4; ++i) f.a[i] = SA::frag(a, kk, lane, wm, i);
+  for (int i = 1; i < 4; ++i) f.a[i] = ASrc::frag(as, kq, lane, wm, i);
 }
 
 __device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][4]) {
@@ -303,68 +320,62 @@ __device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][4])
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
+constexpr int kReadsPerStep = 4 * 1 + 4 * 2;  // A: one ds_read_b128, B: two transpose reads
 
-// LDS read instructions per 16-wide k step for operand layouts SA, SB (8..16).
-template <class SA, class SB>
-constexpr int reads_per_step() {
-  return 4 * (SA::kReadsPerFrag + SB::kReadsPerFrag);
-}
-
-// Interleaves the 16 MFMAs of a k step with its LDS reads (one after each
-// MFMA) and, with LOADS, the kLoadsPerWaveOperand loads of one operand (one
-// per four MFMAs).
-template <class SA, class SB, bool LOADS, int ID>
+// Interleaves the 16 MFMAs of a k step with its 12 LDS reads (one after each
+// of the first 12 MFMAs) and its 4 loads (one per four MFMAs).
+template <int ID>
 __device__ __forceinline__ void interleave() {
-  constexpr int nr = reads_per_step<SA, SB>();
-  constexpr int every = 16 / kLoadsPerWaveOperand;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, ID);
-    if (LOADS && i % every == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, ID);
-    if (i < nr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, ID);
+    if (i % 4 == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, ID);
+    if (i < kReadsPerStep) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, ID);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One stage of kBK = 2 MFMA k steps from slot `cur`. On entry f0 holds the
-// stage's kk = 0 fragments and slot `fre` is free (its stage kt - 1 was
-// released by the previous barrier). Step 1 runs kk = 0 while reading kk = 1
-// into f1 and issuing stage kt + 3's A loads into `fre`. Then every wave
-// waits for its loads of stage kt + 1 (at most the 8 loads of stage kt + 2
-// and the 4 just issued may remain) and for its LDS reads, and the barrier
-// publishes stage kt + 1 and releases `cur`. Step 2 runs kk = 1 while reading
-// stage kt + 1's kk = 0 fragments from `nxt` and issuing stage kt + 3's B loads.
-// Stages past the end of K are zeros, so every stage runs this same body.
-template <class SA, class SB>
-__device__ __forceinline__ void k_stage(const SA& A, const SB& B, int kt, int nk, const char* cur,
-                                        const char* nxt, char* fre, int lane, int wm, int wn,
-                                        Frags& f0, Frags& f1, f32x16_t (&acc)[4][4]) {
-  static_assert(kStages == 4 && kLoadsPerWaveOperand == 4, "waits below assume this ring");
+// Stage s = s0 + U of the main loop (s0 a multiple of 12, so every slot
+// index below is a compile-time constant). On entry f0 holds stage s's
+// kk = 0 fragments. Step 1 runs kk = 0 while reading kk = 1 into f1 and
+// issuing half of pair s / 2 + 2's A loads (into the slot pair s / 2 - 1
+// released). Then every wave waits for its loads of stage s + 1 (at most the
+// 8 loads of stage s - 1 and the 4 just issued may remain) and for its LDS
+// reads, and the barrier publishes stage s + 1 and releases stage s's B slot
+// and, after the pair's second stage, its A slot. Step 2 runs kk = 1 while
+// reading stage s + 1's kk = 0 fragments and issuing stage s + 3's B loads
+// (into the slot stage s - 1 released).
+template <int U>
+__device__ __forceinline__ void k_stage(const ASrc& A, const BSrc& B, int s, int np,
+                                        const Ring& R, int lane, int wm, int wn, Frags& f0,
+                                        Frags& f1, f32x16_t (&acc)[4][4]) {
+  static_assert(kLoadsPerWaveStage == 8, "the wait below assumes 8 loads per stage");
+  constexpr int a_cur = (U / 2) % 3, a_nxt = ((U + 1) / 2) % 3, a_fre = (U / 2 + 2) % 3;
+  constexpr int b_cur = U % 4, b_nxt = (U + 1) % 4, b_fre = (U + 3) % 4;
+  constexpr int sub = U % 2, sub_nxt = (U + 1) % 2;
   __builtin_amdgcn_sched_barrier(0);
-  read_frags<SA, SB>(cur, 1, lane, wm, wn, f1);
-  A.issue(kt + 3, nk, fre);
+  read_frags(R.a[a_cur], 2 * sub + 1, R.b[b_cur], 1, lane, wm, wn, f1);
+  A.issue_half(s / 2 + 2, np, sub, R.a[a_fre]);
   mfma_step(f0, acc);
-  interleave<SA, SB, true, 0>();
-  wait_vmcnt<kLoadsPerWaveStage + kLoadsPerWaveOperand>();
+  interleave<0>();
+  wait_vmcnt<kLoadsPerWaveStage + kALoadsPerWavePair / 2>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_frags<SA, SB>(nxt, 0, lane, wm, wn, f0);
-  B.issue(kt + 3, nk, fre + kOperandStageBytes);
+  read_frags(R.a[a_nxt], 2 * sub_nxt, R.b[b_nxt], 0, lane, wm, wn, f0);
+  B.issue(s + 3, R.b[b_fre]);
   mfma_step(f1, acc);
-  interleave<SA, SB, true, 1>();
+  interleave<1>();
 }
 
 // Accumulates the tile over nk stages of kBK. The caller must have made the
-// LDS ring free (barrier) before the call; on return every wave has finished
-// its LDS reads and no load is in flight. The four slots are distinct
-// __shared__ objects and the loop is unrolled by four, so every LDS access
-// names a fixed slot: the compiler can then see that fragment reads never
-// alias the direct-to-LDS loads in flight into other slots, and inserts no
-// waits of its own.
-template <class SA, class SB>
-__device__ __forceinline__ void mainloop(const SA& A, const SB& B, int nk, char* slot0,
-                                         char* slot1, char* slot2, char* slot3,
+// LDS free (barrier) before the call; on return every wave has finished its
+// LDS reads and no load is in flight. The slots are distinct __shared__
+// objects and the loop is unrolled by 12 (the periods of the two rings are
+// 6 and 4 stages), so every LDS access names a fixed slot: the compiler can
+// then see that fragment reads never alias the direct-to-LDS loads in flight
+// into other slots, and inserts no waits of its own.
+__device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, const Ring& R,
                                          f32x16_t (&acc)[4][4]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -378,25 +389,35 @@ __device__ __forceinline__ void mainloop(const SA& A, const SB& B, int nk, char*
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   if (nk <= 0) return;
+  const int np = (nk + 1) / 2;
 
-  A.issue(0, nk, slot0);
-  B.issue(0, nk, slot0 + kOperandStageBytes);
-  A.issue(1, nk, slot1);
-  B.issue(1, nk, slot1 + kOperandStageBytes);
-  A.issue(2, nk, slot2);
-  B.issue(2, nk, slot2 + kOperandStageBytes);
-  wait_vmcnt<2 * kLoadsPerWaveStage>();
+  // Issue order matters: each stage's wait counts loads issued after the ones
+  // it needs. At stage 0's wait, B stage 1 must be older than the last 12
+  // loads (A pair 1's second half, B stage 2, pair 2's first half).
+  A.issue_half(0, np, 0, R.a[0]);
+  A.issue_half(0, np, 1, R.a[0]);
+  B.issue(0, R.b[0]);
+  B.issue(1, R.b[1]);
+  A.issue_half(1, np, 0, R.a[1]);
+  A.issue_half(1, np, 1, R.a[1]);
+  B.issue(2, R.b[2]);
+  // pair 0 and stage 0 landed: only stage 1, pair 1 and stage 2 may remain
+  wait_vmcnt<kALoadsPerWavePair + 2 * kBLoadsPerWaveStage>();
   __builtin_amdgcn_s_barrier();
 
   Frags f0, f1;
-  read_frags<SA, SB>(slot0, 0, lane, wm, wn, f0);
-  for (int kt = 0; kt < nk; kt += 4) {
-    k_stage(A, B, kt, nk, slot0, slot1, slot3, lane, wm, wn, f0, f1, acc);
-    k_stage(A, B, kt + 1, nk, slot1, slot2, slot0, lane, wm, wn, f0, f1, acc);
-    k_stage(A, B, kt + 2, nk, slot2, slot3, slot1, lane, wm, wn, f0, f1, acc);
-    k_stage(A, B, kt + 3, nk, slot3, slot0, slot2, lane, wm, wn, f0, f1, acc);
+  read_frags(R.a[0], 0, R.b[0], 0, lane, wm, wn, f0);
+  // Whole periods of 12 stages: stages past nk read zeros and add nothing.
+  // An exit between stages would be cheaper for nk not a multiple of 12, but
+  // any branch out of the unrolled body makes the register allocator spill
+  // fragments inside the loop.
+  for (int s = 0; s < nk; s += 12) {
+#define LMH_STAGE(U) k_stage<U>(A, B, s + U, np, R, lane, wm, wn, f0, f1, acc);
+    LMH_STAGE(0) LMH_STAGE(1) LMH_STAGE(2) LMH_STAGE(3) LMH_STAGE(4) LMH_STAGE(5)
+    LMH_STAGE(6) LMH_STAGE(7) LMH_STAGE(8) LMH_STAGE(9) LMH_STAGE(10) LMH_STAGE(11)
+#undef LMH_STAGE
   }
-  // the last stages issued zero loads that nobody reads; let them land
+  // stages and pairs past the end issued loads that nobody reads; let them land
   wait_vmcnt<0>();
   wait_lgkm0();
 }

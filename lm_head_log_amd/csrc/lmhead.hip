@@ -5,8 +5,8 @@
 // expand back; SkyRL PR #2374 "How it works": one projection gives both the
 // selected-token log-prob and the entropy):
 //   1. k_compact     keep mask -> ascending kept rows, row -> compact position
-//   2. k_transpose_w W^T, k_gather_cols X[kept]^T: the MN-major operands of
-//                    the logit GEMM (k = h rows, vocabulary / tokens contiguous)
+//   2. k_gather_cols X_c^T = X[kept]^T [h][c], the token operand of the logit
+//                    GEMM (k = h rows, tokens contiguous)
 //   3. k_fwd_tiles   Z^T tile = W[vtile] X[kept]^T on MFMA, never stored; per
 //                    token: max, sum 2^(y), sum 2^(y) y over the tile's 256
 //                    vocab rows (y = z log2 e - max), and the target logit
@@ -16,14 +16,15 @@
 // Backward (twinkle PR #283 section 1: recompute the softmax from saved inputs;
 // SkyRL PR #2374 review: entropy is saved by the forward, not recomputed):
 //   1. k_zero_rows   +0.0 dX rows at skipped positions
-//   2. k_gather_rows X_c = X[kept]; k_gather_cols X_c^T; k_transpose_w W^T
+//   2. k_gather_cols X_c^T
 //   3. per chunk of kept rows:
 //      k_dz_tiles    recompute Z^T tile, p = exp(z - LSE),
 //                    dZ = g_lp (onehot - p) - g_H p (z - LSE + H), bf16,
-//                    stored token-major [c][v] and vocab-major [v][c]
-//      k_dx_tiles    dX[kept rows] = dZ W    (K = vocab: dZ^T and W)
-//      k_dw_tiles    dW (+)= dZ^T X_c        (K = chunk rows: dZ and X_c)
-// Every GEMM reads both operands MN-major (k rows, m or n contiguous).
+//                    stored token-major [c][v]
+//      k_dx_tiles    dX[kept rows] = dZ W      (K = vocab)
+//      k_dw_tiles    dW^T (+)= X_c^T dZ        (K = chunk rows), stored as dW
+// Every GEMM reads a K-major A (W, dZ, X_c^T) and an MN-major B (X_c^T, W, dZ)
+// as they are stored.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -43,12 +44,12 @@ namespace lmh {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMaskedLogit = -1e30f;  // stands in for the logit of a vocabulary row past V
-// Default token chunk: the largest multiple of 256 rows whose two bf16 dZ
-// buffers (token-major and vocab-major) fit this budget. The pages' fused
-// head defaults to 8192 rows to bound memory on an 80 GB part; with 288 GB of
-// HBM the budget admits a whole 16K-token batch at V = 131072 (4 GiB per
-// layout), which saves the read-modify-write of dW between chunks.
-constexpr int64_t kDefaultDzBudget = int64_t(16) << 30;
+// Default token chunk: the largest multiple of 256 rows whose bf16 dZ buffer
+// fits this budget. The pages' fused head defaults to 8192 rows to bound
+// memory on an 80 GB part; with 288 GB of HBM the budget admits a whole
+// 16K-token batch at V = 131072 (4 GiB of dZ), which saves the
+// read-modify-write of dW between chunks.
+constexpr int64_t kDefaultDzBudget = int64_t(8) << 30;
 constexpr int kVersion = 100;  // 0.1.0
 
 // ---------------------------------------------------------------------------
@@ -91,14 +92,13 @@ static inline SavedView saved_view(void* base, int64_t N) {
 static inline int n_vtiles(int64_t V) { return (int)((V + kBM - 1) / kBM); }
 static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Pitches of the transposed operand copies: W^T [H][ldv], X_c^T [H][ldc].
-static inline int64_t ldv_of(int64_t V) { return round_up(V, 64); }
+// Pitch of the transposed kept rows X_c^T [H][ldc].
 static inline int64_t ldc_of(int64_t N) { return round_up(N, 64); }
 
 // Forward workspace: target logits [N] | partial m, s, b [n_vt][N] each |
-// X_c^T [H][ldc] | W^T [H][ldv] (bf16).
+// X_c^T [H][ldc] (bf16).
 struct FwdWs {
-  size_t zt, pm, ps, pb, xct, wt, total;
+  size_t zt, pm, ps, pb, xct, total;
 };
 static inline FwdWs fwd_ws(int64_t N, int64_t H, int64_t V) {
   const size_t nv = (size_t)n_vtiles(V);
@@ -108,8 +108,7 @@ static inline FwdWs fwd_ws(int64_t N, int64_t H, int64_t V) {
   w.ps = w.pm + align256(nv * (size_t)N * 4);
   w.pb = w.ps + align256(nv * (size_t)N * 4);
   w.xct = w.pb + align256(nv * (size_t)N * 4);
-  w.wt = w.xct + align256((size_t)H * (size_t)ldc_of(N) * 2);
-  w.total = w.wt + align256((size_t)H * (size_t)ldv_of(V) * 2);
+  w.total = w.xct + align256((size_t)H * (size_t)ldc_of(N) * 2);
   return w;
 }
 
@@ -122,7 +121,7 @@ static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
   BwdGeom g;
   int64_t want = token_chunk;
   if (want <= 0) {
-    want = kDefaultDzBudget / (4 * round_up(V, 256)) / 256 * 256;
+    want = kDefaultDzBudget / (2 * round_up(V, 256)) / 256 * 256;
     if (want < 256) want = 256;
   }
   g.C = N > 0 ? std::min(round_up(want, 256), round_up(N, 256)) : 0;
@@ -130,20 +129,16 @@ static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
   return g;
 }
 
-// Backward workspace: X_c [N][H] | X_c^T [H][ldc] | W^T [H][ldv] |
-// dZ [C][ldz] | dZ^T [ldz][C], all bf16.
+// Backward workspace: X_c^T [H][ldc] | dZ [C][ldz], both bf16.
 struct BwdWs {
-  size_t xc, xct, wt, dz, dzt, total;
+  size_t xct, dz, total;
 };
 static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
   const BwdGeom g = bwd_geom(N, V, token_chunk);
   BwdWs w;
-  w.xc = 0;
-  w.xct = w.xc + align256((size_t)N * (size_t)H * 2);
-  w.wt = w.xct + align256((size_t)H * (size_t)ldc_of(N) * 2);
-  w.dz = w.wt + align256((size_t)H * (size_t)ldv_of(V) * 2);
-  w.dzt = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
-  w.total = w.dzt + align256((size_t)g.ldz * (size_t)g.C * 2);
+  w.xct = 0;
+  w.dz = w.xct + align256((size_t)H * (size_t)ldc_of(N) * 2);
+  w.total = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
   return w;
 }
 
@@ -229,22 +224,8 @@ __device__ __forceinline__ void stat_merge(float& m, float& s, float& b, float m
 }
 
 // ---------------------------------------------------------------------------
-// Row gather: Xc[c] = X[kept_idx[c]] for the kept rows (compact order).
-// ---------------------------------------------------------------------------
-__global__ void k_gather_rows(const uint16_t* __restrict__ X, const SavedHeader* __restrict__ hdr,
-                              const int32_t* __restrict__ kept_idx, int H,
-                              uint16_t* __restrict__ Xc) {
-  const int c = blockIdx.x;
-  if (c >= hdr->n_kept) return;
-  const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)kept_idx[c] * H);
-  uint4* dst = reinterpret_cast<uint4*>(Xc + (int64_t)c * H);
-  for (int k = threadIdx.x; k < H / 8; k += blockDim.x) dst[k] = src[k];
-}
-
-// ---------------------------------------------------------------------------
-// 64 x 64 tile transposes through LDS (bf16), zero-filled past the valid
-// columns so that every MN-major tile reads finite values:
-//   k_transpose_w : WT[h][v] = W[v][h]            (zero for V <= v < ldv)
+// Gathered transpose of the kept rows through LDS in 64 x 64 tiles (bf16),
+// zero-filled past the kept rows so that every tile reads finite values:
 //   k_gather_cols : XcT[h][c] = X[kept_idx[c]][h] (zero for n_kept <= c < ldc)
 // ---------------------------------------------------------------------------
 constexpr int kTp = 64;
@@ -281,17 +262,6 @@ __device__ __forceinline__ void tile_store_t(uint16_t (*t)[kTpPitch], uint16_t* 
   }
 }
 
-__global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict__ W, int V, int H,
-                                                     uint16_t* __restrict__ WT, int64_t ldv) {
-  __shared__ uint16_t t[kTp][kTpPitch];
-  const int v0 = blockIdx.x * kTp, h0 = blockIdx.y * kTp;
-  tile_load(t, [&](int r) -> const uint16_t* {
-    return v0 + r < V ? W + (int64_t)(v0 + r) * H + h0 : nullptr;
-  });
-  __syncthreads();
-  tile_store_t(t, WT + (int64_t)h0 * ldv + v0, ldv);
-}
-
 __global__ __launch_bounds__(256) void k_gather_cols(const uint16_t* __restrict__ X,
                                                      const SavedHeader* __restrict__ hdr,
                                                      const int32_t* __restrict__ kept_idx, int H,
@@ -307,18 +277,17 @@ __global__ __launch_bounds__(256) void k_gather_cols(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Forward tiles: M = vocab (A = W^T, MN-major), N = kept tokens (B = X_c^T,
-// MN-major), K = H. The epilogue reduces over the tile's 256 vocab rows per
-// token.
+// Forward tiles: M = vocab (A = W rows), N = kept tokens (B = X_c^T), K = H.
+// The epilogue reduces over the tile's 256 vocab rows per token.
 // ---------------------------------------------------------------------------
 struct FwdParams {
-  const uint16_t* WT;   // [H][ldv]
+  const uint16_t* W;    // [V][H]
   const uint16_t* XcT;  // [H][ldc]
   const int32_t* targets;
   const int32_t* kept_idx;
   const SavedHeader* hdr;
   int H, V, n_vt;
-  int64_t ldv, ldc;
+  int64_t ldc;
   int64_t ldp;  // pitch (elements) between vocab tiles in the partial arrays
   float* pm;
   float* ps;
@@ -329,7 +298,7 @@ struct FwdParams {
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
   LMH_DECLARE_RING;
   // per-token partials of the two wave rows; reuses ring slot 0 after the main loop
-  float (*red)[3][kBN] = reinterpret_cast<float (*)[3][kBN]>(slot0);
+  float (*red)[3][kBN] = reinterpret_cast<float (*)[3][kBN]>(ra0);
 
   const int rows = P.hdr->n_kept;
   const int mt = P.n_vt;
@@ -348,11 +317,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     tile_coords<LMH_GM_FWD>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    MNSrc A, B;
-    A.init(P.WT + (int64_t)tm * kBM, P.ldv, P.H, P.V - tm * kBM);
+    ASrc A;
+    BSrc B;
+    A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
     B.init(P.XcT + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, slot0, slot1, slot2, slot3, acc);
+    mainloop(A, B, nk, ring, acc);
 
     const int vbase = tm * kBM + wm * 128;
     const bool full = vbase + 128 <= P.V;
@@ -504,7 +474,7 @@ __global__ void k_zero_rows(const int32_t* __restrict__ pos, int N, int H, float
 }
 
 struct DzParams {
-  const uint16_t* WT;   // [H][ldv]
+  const uint16_t* W;    // [V][H]
   const uint16_t* XcT;  // [H][ldc]
   const int32_t* targets;
   const float* g_lp;
@@ -512,10 +482,9 @@ struct DzParams {
   SavedView sv;
   int H, V, n_vt;
   int c0, C;     // chunk start (compact rows) and chunk capacity (multiple of 256)
-  int64_t ldv, ldc;
+  int64_t ldc;
   int64_t ldz;   // dZ row pitch (V rounded up to 256)
-  uint16_t* dZ;  // [C][ldz] token-major: A of dW = dZ^T Xc
-  uint16_t* dZT; // [ldz][C] vocab-major: A of dX = dZ W
+  uint16_t* dZ;  // [C][ldz] token-major: A of dX = dZ W, B of dW^T = X_c^T dZ
 };
 
 // bf16 pairs: (__bf16)x rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950)
@@ -536,9 +505,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = P.H / kBK;
   const int32_t* kidx = P.sv.kept_idx + P.c0;
-  // this wave's 128 x 128 bf16 staging tile for the vocab-major store
-  char* tw = wave == 0 ? slot0 : wave == 1 ? slot1 : wave == 2 ? slot2 : slot3;
-  static_assert(kStageBytes == 128 * 128 * 2, "one ring slot per wave tile");
 
   for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
     const int t = xcd_logical(round, gridDim.x);
@@ -547,19 +513,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     tile_coords<LMH_GM_DZ>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    MNSrc A, B;
-    A.init(P.WT + (int64_t)tm * kBM, P.ldv, P.H, P.V - tm * kBM);
+    ASrc A;
+    BSrc B;
+    A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
     B.init(P.XcT + P.c0 + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, slot0, slot1, slot2, slot3, acc);
-    __syncthreads();  // every wave is done reading the ring
+    mainloop(A, B, nk, ring, acc);
 
     const int vbase = tm * kBM + wm * 128;
-    const int cbase = tn * kBN + wn * 128;
     // Tokens past the chunk's rows have ca = cb = 0 and a zero logit, so their
-    // dz is exactly 0. Vocabulary rows at or past V are not masked: those rows
-    // of dZ and dZ^T hold finite values that no consumer reads (dX masks k
-    // rows at or past V; dW never stores output rows at or past V).
+    // dz is exactly 0. Vocabulary rows at or past V are not masked: those
+    // columns of dZ hold finite values that no consumer uses (dX = dZ W reads
+    // W rows at or past V as zero; dW^T never stores columns at or past V).
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = tn * kBN + wn * 128 + j * 32 + (lane & 31);  // chunk row
@@ -600,10 +565,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           for (int r = 0; r < 16; ++r)
             if (want == i * 16 + r) acc[i][j][r] += glp;
       }
-      // dZ[c][v]: four consecutive v per register group (8 bytes); the
-      // vocab-major copy goes through LDS (element (v, c) at row v, column c)
+      // dZ[c][v]: four consecutive v per register group (8 bytes)
       uint16_t* zrow = P.dZ + (int64_t)c * P.ldz;
-      char* tcol = tw + (j * 32 + (lane & 31)) * 2;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -614,33 +577,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           const uint32_t plo = __builtin_bit_cast(uint32_t, lo);
           const uint32_t phi = __builtin_bit_cast(uint32_t, hi);
           *reinterpret_cast<uint2*>(zrow + v0) = make_uint2(plo, phi);
-          const int vl = v0 - vbase;
-          *reinterpret_cast<uint16_t*>(tcol + (vl + 0) * 256) = (uint16_t)plo;
-          *reinterpret_cast<uint16_t*>(tcol + (vl + 1) * 256) = (uint16_t)(plo >> 16);
-          *reinterpret_cast<uint16_t*>(tcol + (vl + 2) * 256) = (uint16_t)phi;
-          *reinterpret_cast<uint16_t*>(tcol + (vl + 3) * 256) = (uint16_t)(phi >> 16);
         }
-    }
-    // dZ^T[v][c]: each 256-byte LDS row (one v, 128 tokens) goes out as 16-byte
-    // stores; 16 lanes write one row. Invalid rows and columns hold zeros.
-#pragma unroll 8
-    for (int it = 0; it < 32; ++it) {
-      const int q = it * 64 + lane;
-      const int vl = q >> 4, ch = q & 15;
-      const uint4 x = *reinterpret_cast<const uint4*>(tw + vl * 256 + ch * 16);
-      *reinterpret_cast<uint4*>(P.dZT + (int64_t)(vbase + vl) * P.C + cbase + ch * 8) = x;
     }
   }
 }
 
-// dX[kept rows] = dZ W: M = chunk rows (A = dZ^T: k = v rows, tokens
-// contiguous), N = H (B = W: k = v rows, h contiguous), K = vocab.
+// dX[kept rows] = dZ W: M = chunk rows (A = dZ rows), N = H (B = W: k = v
+// rows, h contiguous), K = vocab.
 struct DxParams {
-  const uint16_t* dZT;  // [ldz][C]
-  const uint16_t* W;    // [V][H]
+  const uint16_t* dZ;  // [C][ldz]
+  const uint16_t* W;   // [V][H]
   SavedView sv;
   int H, V;
   int c0, C;
+  int64_t ldz;
   float* dX;
 };
 
@@ -667,11 +617,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     tile_coords<LMH_GM_DX>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    MNSrc A, B;
-    A.init(P.dZT + (int64_t)tm * kBM, P.C, P.V, rows - tm * kBM);
+    ASrc A;
+    BSrc B;
+    A.init(P.dZ + (int64_t)tm * kBM * P.ldz, P.ldz, rows - tm * kBM);
     B.init(P.W + (int64_t)tn * kBN, P.H, P.V, P.H - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, slot0, slot1, slot2, slot3, acc);
+    mainloop(A, B, nk, ring, acc);
 
     const int mrow = tm * kBM + wm * 128 + acc_row_lane(lane);
     const int mlim = rows - mrow;
@@ -690,15 +641,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   }
 }
 
-// dW (+)= dZ^T Xc: M = vocab, N = H, K = chunk rows; both operands MN-major
-// (A = dZ [c][v], B = Xc [c][h]).
+// dW^T (+)= X_c^T dZ: M = H (A = X_c^T rows), N = vocab (B = dZ: k = chunk
+// rows, vocabulary contiguous), K = chunk rows; stored transposed into dW.
 struct DwParams {
-  const uint16_t* dZ;  // [C][ldz]
-  const uint16_t* Xc;  // [n_kept][H]; this chunk starts at row c0
+  const uint16_t* XcT;  // [H][ldc]; this chunk starts at column c0
+  const uint16_t* dZ;   // [C][ldz]
   const SavedHeader* hdr;
   int H, V;
   int c0, C;
-  int64_t ldz;
+  int64_t ldc, ldz;
   int accumulate;
   float* dW;
 };
@@ -712,15 +663,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     if (P.accumulate) return;  // nothing to add
     rows = 0;                  // first chunk with no kept rows: write zeros
   }
-  const int mt = (P.V + kBM - 1) / kBM;
-  const int nt = (P.H + kBN - 1) / kBN;
+  const int mt = (P.H + kBM - 1) / kBM;
+  const int nt = (P.V + kBN - 1) / kBN;
   const int ntiles = mt * nt;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nk = (rows + kBK - 1) / kBK;  // rows past `rows` read as zero
-  const uint16_t* xc = P.Xc + (int64_t)P.c0 * P.H;
+  const int nk = (rows + kBK - 1) / kBK;  // dZ rows past `rows` read as zero
 
   for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
     const int t = xcd_logical(round, gridDim.x);
@@ -729,30 +679,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     tile_coords<LMH_GM_DW>(t, mt, nt, tm, tn);
     __syncthreads();
 
-    MNSrc A, B;
-    A.init(P.dZ + (int64_t)tm * kBM, P.ldz, rows, kBM);  // ldz covers every m of the tile
-    B.init(xc + (int64_t)tn * kBN, P.H, rows, P.H - tn * kBN);
+    ASrc A;
+    BSrc B;
+    A.init(P.XcT + (int64_t)tm * kBM * P.ldc + P.c0, P.ldc, P.H - tm * kBM);
+    B.init(P.dZ + (int64_t)tn * kBN, P.ldz, rows, kBN);  // ldz covers every v of the tile
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, slot0, slot1, slot2, slot3, acc);
+    mainloop(A, B, nk, ring, acc);
 
-    const int mrow = tm * kBM + wm * 128 + acc_row_lane(lane);
-    const int mlim = P.V - mrow;
+    // lane: vocabulary row v (column of the tile) and, per register group,
+    // four consecutive h: one 16-byte store into dW[v][h .. h + 3]
+    const int hrow = tm * kBM + wm * 128 + acc_row_lane(lane);
+    const int hlim = P.H - hrow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int v = tn * kBN + wn * 128 + j * 32 + (lane & 31);
+      if (v >= P.V) continue;
+      float* wrow = P.dW + (int64_t)v * P.H + hrow;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (acc_row_fixed(i, r) >= mlim) continue;
-        float* wrow = P.dW + (int64_t)(mrow + acc_row_fixed(i, r)) * P.H;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = tn * kBN + wn * 128 + j * 32 + (lane & 31);
-          if (n < P.H) {
-            float v = acc[i][j][r];
-            if (P.accumulate) v += wrow[n];
-            wrow[n] = v;
+        for (int g = 0; g < 4; ++g) {
+          const int h = acc_row_fixed(i, 4 * g);
+          if (h >= hlim) continue;  // H is a multiple of 4: the group is whole
+          float4 x = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                 acc[i][j][4 * g + 3]);
+          if (P.accumulate) {
+            const float4 o = *reinterpret_cast<const float4*>(wrow + h);
+            x.x += o.x;
+            x.y += o.y;
+            x.z += o.z;
+            x.w += o.w;
           }
+          *reinterpret_cast<float4*>(wrow + h) = x;
         }
-      }
+    }
   }
 }
 
@@ -798,12 +758,12 @@ static int check_sizes(int64_t N, int64_t H, int64_t V) {
 // Optional per-kernel timing (benchmarks only): hipEvent pairs recorded on
 // the launch stream around every launch while profiling is on.
 enum KernelKind {
-  KK_COMPACT = 0, KK_GATHER_ROWS, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS,
-  KK_GATHER_COLS, KK_TRANSPOSE_W, KK_DZ, KK_DX, KK_DW, KK_COUNT
+  KK_COMPACT = 0, KK_GATHER_COLS, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS,
+  KK_DZ, KK_DX, KK_DW, KK_COUNT
 };
 static const char* const kKernelNames[KK_COUNT] = {
-    "compact",     "gather_rows", "fwd_tiles", "merge",    "zero_skipped", "zero_rows",
-    "gather_cols", "transpose_w", "dz_tiles",  "dx_tiles", "dw_tiles"};
+    "compact",   "gather_cols", "fwd_tiles", "merge",   "zero_skipped",
+    "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles"};
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -902,19 +862,15 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
 
   const int nv = n_vtiles(V);
   char* w = static_cast<char*>(workspace);
-  const int64_t ldc = ldc_of(N), ldv = ldv_of(V);
+  const int64_t ldc = ldc_of(N);
   uint16_t* XcT = reinterpret_cast<uint16_t*>(w + L.xct);
-  uint16_t* WT = reinterpret_cast<uint16_t*>(w + L.wt);
   LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(ldc / kTp), (unsigned)(H / kTp)),
                  dim3(256), s, static_cast<const uint16_t*>(hidden), (const SavedHeader*)sv.hdr,
                  (const int32_t*)sv.kept_idx, (int)H, XcT, ldc));
-  LMH_TRY(launch(KK_TRANSPOSE_W, k_transpose_w, dim3((unsigned)(ldv / kTp), (unsigned)(H / kTp)),
-                 dim3(256), s, static_cast<const uint16_t*>(weight), (int)V, (int)H, WT, ldv));
 
   FwdParams P;
-  P.WT = WT;
+  P.W = static_cast<const uint16_t*>(weight);
   P.XcT = XcT;
-  P.ldv = ldv;
   P.ldc = ldc;
   P.targets = targets;
   P.kept_idx = sv.kept_idx;
@@ -961,25 +917,18 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
   hipStream_t s = static_cast<hipStream_t>(stream);
   SavedView sv = saved_view(const_cast<void*>(saved), N);
   char* w = static_cast<char*>(workspace);
-  uint16_t* Xc = reinterpret_cast<uint16_t*>(w + L.xc);
   uint16_t* XcT = reinterpret_cast<uint16_t*>(w + L.xct);
-  uint16_t* WT = reinterpret_cast<uint16_t*>(w + L.wt);
   uint16_t* dZ = reinterpret_cast<uint16_t*>(w + L.dz);
-  uint16_t* dZT = reinterpret_cast<uint16_t*>(w + L.dzt);
   const uint16_t* X = static_cast<const uint16_t*>(hidden);
   const uint16_t* Wt = static_cast<const uint16_t*>(weight);
-  const int64_t ldc = ldc_of(N), ldv = ldv_of(V);
+  const int64_t ldc = ldc_of(N);
 
   if (N > 0) {
     LMH_TRY(launch(KK_ZERO_ROWS, k_zero_rows, dim3((unsigned)N), dim3(256), s,
                    (const int32_t*)sv.pos, (int)N, (int)H, grad_hidden));
-    LMH_TRY(launch(KK_GATHER_ROWS, k_gather_rows, dim3((unsigned)N), dim3(256), s, X,
-                   (const SavedHeader*)sv.hdr, (const int32_t*)sv.kept_idx, (int)H, Xc));
     LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(ldc / kTp), (unsigned)(H / kTp)),
                    dim3(256), s, X, (const SavedHeader*)sv.hdr, (const int32_t*)sv.kept_idx,
                    (int)H, XcT, ldc));
-    LMH_TRY(launch(KK_TRANSPOSE_W, k_transpose_w, dim3((unsigned)(ldv / kTp), (unsigned)(H / kTp)),
-                   dim3(256), s, Wt, (int)V, (int)H, WT, ldv));
   }
 
   const int nv = n_vtiles(V);
@@ -988,9 +937,8 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
     const int c0 = (int)(ch * G.C);
     if (N > 0) {
       DzParams D;
-      D.WT = WT;
+      D.W = Wt;
       D.XcT = XcT;
-      D.ldv = ldv;
       D.ldc = ldc;
       D.targets = targets;
       D.g_lp = grad_logp;
@@ -1003,12 +951,12 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       D.C = (int)G.C;
       D.ldz = G.ldz;
       D.dZ = dZ;
-      D.dZT = dZT;
       const int64_t dz_tiles = (int64_t)nv * (G.C / kBN);
       LMH_TRY(launch(KK_DZ, k_dz_tiles, dim3(persistent_grid(dz_tiles)), dim3(kThreads), s, D));
 
       DxParams X2;
-      X2.dZT = dZT;
+      X2.dZ = dZ;
+      X2.ldz = G.ldz;
       X2.W = Wt;
       X2.sv = sv;
       X2.H = (int)H;
@@ -1020,13 +968,14 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       LMH_TRY(launch(KK_DX, k_dx_tiles, dim3(persistent_grid(dx_tiles)), dim3(kThreads), s, X2));
     }
     DwParams Wp;
+    Wp.XcT = XcT;
     Wp.dZ = dZ;
-    Wp.Xc = Xc;
     Wp.hdr = sv.hdr;
     Wp.H = (int)H;
     Wp.V = (int)V;
     Wp.c0 = c0;
     Wp.C = (int)G.C;
+    Wp.ldc = ldc;
     Wp.ldz = G.ldz;
     Wp.accumulate = ch > 0;
     Wp.dW = grad_weight;
