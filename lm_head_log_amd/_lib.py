@@ -6,7 +6,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblmhead.so")
+# The in-tree build; LMHEAD_LIB names another build of the same sources (for
+# side-by-side timing of kernel variants).
+LIB_PATH = os.environ.get("LMHEAD_LIB") or os.path.join(_HERE, "liblmhead.so")
 
 # Every symbol include/lmhead.h declares, with its ctypes signature.
 c_size = ctypes.c_size_t
