@@ -4,11 +4,14 @@
 V=131072 (SkyRL PR #2374, Performance), differentiable entropy, every row kept.
 
 One step = lmhead_fwd + lmhead_bwd over one synthetic batch whose inputs are
-already resident in HBM; every buffer is preallocated. Prints ONE JSON line on
-stdout; progress goes to stderr.
+already resident in HBM; every buffer is preallocated. After the timed steps,
+the keep-fraction sweep of the same page (same batch, nested masks) is timed
+and fitted as t = t0 + f * t1. Prints ONE JSON line on stdout; progress goes
+to stderr.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--keep 1.0]
                     [--config 2] [--token-chunk 0] [--no-cpu-baseline]
+                    [--no-keep-sweep]
 """
 
 from __future__ import annotations
@@ -105,7 +108,9 @@ def main():
     ap.add_argument("--keep", type=float, default=1.0)
     ap.add_argument("--token-chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--no-keep-sweep", action="store_true")
+    ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (counter calibration)")
     args = ap.parse_args()
@@ -154,12 +159,32 @@ def main():
         gW = torch.empty(V, H, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        lmh.lmhead_fwd(X, W, t, km, ret, erg, logp=logp, entropy=ent, saved=saved,
+    def fwd(mask):
+        lmh.lmhead_fwd(X, W, t, mask, ret, erg, logp=logp, entropy=ent, saved=saved,
                        workspace=ws_f, stream=stream)
+
+    def bwd():
         if do_bwd:
             lmh.lmhead_bwd(X, W, t, saved, glp, gh, erg, args.token_chunk, grad_hidden=gX,
                            grad_weight=gW, workspace=ws_b, stream=stream)
+
+    def step():
+        fwd(km)
+        bwd()
+
+    def timed_steps(mask, k):
+        """k steps with an event after each forward and each backward."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * k + 1)]
+        ev[0].record(stream)
+        for i in range(k):
+            fwd(mask)
+            ev[2 * i + 1].record(stream)
+            bwd()
+            ev[2 * i + 2].record(stream)
+        torch.cuda.synchronize()
+        f = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(k)]
+        b = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(k)]
+        return ev[0].elapsed_time(ev[2 * k]), f, b
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -176,17 +201,15 @@ def main():
 
     torch.cuda.synchronize()
     lmh.lmhead_profile_begin()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_total, f_ms, b_ms = timed_steps(km, args.steps)
     prof = lmh.lmhead_profile_end()
-    ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
+    step_ms = [a + b for a, b in zip(f_ms, b_ms)]
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step")
+
+    def spread(xs):
+        return {"median": round(float(np.median(xs)), 4), "min": round(min(xs), 4),
+                "max": round(max(xs), 4)}
 
     fl_gemm = 2.0 * n_kept * H * V  # one logit-sized contraction over kept rows
     n_gemm = 4 if do_bwd else 1
@@ -203,6 +226,35 @@ def main():
     for k in KERNELS_GEMM:
         if k in kern:
             kern[k]["tflops"] = round(fl_gemm / (kern[k]["ms_per_step"] * 1e-3) / 1e12, 1)
+
+    sweep = None
+    if not args.no_keep_sweep and args.config == 2:
+        import workloads as wl
+        masks = wl.config2_masks(wl.KEEP_SWEEP, N=N)
+        fr, ms, kept = [], [], []
+        for f in wl.KEEP_SWEEP:
+            m_dev = torch.from_numpy(masks[f]).to(dev)
+            for _ in range(2):
+                fwd(m_dev)
+                bwd()
+            tot, _, _ = timed_steps(m_dev, args.sweep_steps)
+            fr.append(f)
+            kept.append(int(masks[f].sum()))
+            ms.append(tot / args.sweep_steps)
+            log(f"keep {f:.2f}: {ms[-1]:.3f} ms/step ({kept[-1]} kept rows)")
+        kf = np.array(kept, dtype=np.float64) / N
+        A = np.stack([np.ones_like(kf), kf], axis=1)
+        coef, *_ = np.linalg.lstsq(A, np.array(ms), rcond=None)
+        pred = A @ coef
+        ss_res = float(((np.array(ms) - pred) ** 2).sum())
+        ss_tot = float(((np.array(ms) - np.mean(ms)) ** 2).sum())
+        sweep = {
+            "keep_fraction": fr, "kept_rows": kept, "ms_per_step": [round(x, 4) for x in ms],
+            "fit": "ms = t0 + t1 * kept_fraction (least squares)",
+            "t0_ms": round(float(coef[0]), 4), "t1_ms": round(float(coef[1]), 4),
+            "r2": round(1.0 - ss_res / ss_tot, 6) if ss_tot > 0 else None,
+            "steps_each": args.sweep_steps,
+        }
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -232,8 +284,13 @@ def main():
         },
         "tflops": round(tflops, 1),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        # model FLOPs: 6 K_n H V (2 without backward), i.e. without the logit recompute
+        "model_tflops": round((6 if do_bwd else 2) * n_kept * H * V / (ms_step * 1e-3) / 1e12, 1),
         "kept_tokens_per_s": round(n_kept / (ms_step * 1e-3), 1),
         "flops_per_step": flops_step,
+        "step_ms": spread(step_ms),
+        "fwd_ms": spread(f_ms),
+        "bwd_ms": spread(b_ms) if do_bwd else None,
         "kernels": kern,
         "roofline": {
             "kernel": dom,
@@ -245,6 +302,7 @@ def main():
             "traffic": measured_traffic(dom, w.name),
         },
         "cpu_baseline": cpu,
+        "keep_sweep": sweep,
     }
     print(json.dumps(out), flush=True)
 

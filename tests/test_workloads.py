@@ -68,6 +68,12 @@ def test_config2_masks_nested_and_fractions():
     assert wl.config2(1.0, N=64, H=64, V=256, mask=False).keep is None
 
 
+def test_config2_masks_helper_matches_config2():
+    masks = wl.config2_masks(wl.KEEP_SWEEP, N=5000)
+    for f in wl.KEEP_SWEEP:
+        assert np.array_equal(masks[f], wl.config2(f, N=5000, H=64, V=256).keep)
+
+
 def test_packed_grpo_layout_rules():
     rng = np.random.default_rng(1)
     N, V = 4096, 1000

@@ -170,6 +170,13 @@ def config2(keep_fraction: float = 1.0, seed: int = 2, N: int = 16384,
                     meta=dict(config=2, seed=seed, keep_fraction=keep_fraction))
 
 
+def config2_masks(fractions=KEEP_SWEEP, seed: int = 2, N: int = 16384) -> dict:
+    """The keep masks ``config2(f).keep`` for each fraction f, from the same
+    uniform draw, without generating X and W again."""
+    u = _gen(_streams(seed)["keep"]).random(N)
+    return {f: (u < f).astype(np.uint8) for f in fractions}
+
+
 def packed_grpo_layout(N: int, V: int, nseq: int, rng: np.random.Generator):
     """Packed sequences with prompt/completion split and next-token targets.
 
