@@ -106,6 +106,23 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
+// This thread's lane and wave, opaque to the optimiser. Per-tile setup derives
+// many per-lane values (load offsets, epilogue indices) that do not depend on
+// the tile; hoisted out of a persistent tile loop they stay live across the
+// main loop, which needs nearly every register, and get spilled to scratch
+// and reloaded every tile. Reading the lane through an empty asm inside the
+// loop keeps them per tile: a few VALU instructions instead of scratch traffic.
+__device__ __forceinline__ int lane_fresh() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
+__device__ __forceinline__ int wave_fresh() {
+  int w = threadIdx.x >> 6;
+  asm volatile("" : "+v"(w));
+  return w;
+}
+
 // A buffer descriptor must live in SGPRs: its inputs go through readfirstlane
 // so the compiler sees them as wave-uniform (they are uniform by design).
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
@@ -129,8 +146,8 @@ struct ASrc {
     void* base = reinterpret_cast<void*>(uniform_u64(reinterpret_cast<uint64_t>(tile_base)));
     rsrc = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, kRsrcWord3);
     none = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0, kRsrcWord3);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = lane_fresh();
+    const int wave = wave_fresh();
 #pragma unroll
     for (int j = 0; j < kALoadsPerWavePair; ++j) {
       const int row = wave * (kBM / 4) + j * kARowsPerLoad + lane / kAChunks;
@@ -178,8 +195,8 @@ struct BSrc {
     base = uniform_u64(reinterpret_cast<uint64_t>(col_base));
     pitch = (int64_t)uniform_u64((uint64_t)(ld * 2));
     k_valid = __builtin_amdgcn_readfirstlane(k_rows < 0 ? 0 : k_rows);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = lane_fresh();
+    const int wave = wave_fresh();
     const int e = (lane >> 2) & 3;     // k row inside the group
     const int blk = lane >> 4;         // 32-wide n block inside the half
     const int cq = lane & 3;           // 16-byte chunk inside the piece
@@ -229,12 +246,12 @@ struct BSrc {
 
 // ---------------------------------------------------------------------------
 // Tile scheduling: persistent workgroups, XCD-aware grouped order.
-// Workgroups are dispatched round-robin over the 8 XCDs (chiplets), so block
-// b runs on XCD b % 8. Slot b of round `r` is remapped so that the blocks of
-// one XCD take consecutive logical tiles; logical tiles run in groups of
-// GM m-tiles by all n-tiles (m fastest inside a group), so the 32
-// concurrent tiles of an XCD form a GM x (32 / GM) block sharing A and B
-// panels in that XCD's L2.
+// Workgroups are dispatched round-robin over the 8 XCDs (chiplets), 32 per
+// XCD at full occupancy. Each round of `grid` logical tiles is dealt to the
+// XCDs in blocks of grid / 8 consecutive tiles (queue_tile below); logical
+// tiles run in groups of GM m-tiles by all n-tiles (m fastest inside a
+// group), so the 32 concurrent tiles of an XCD form a GM x (32 / GM) block
+// sharing A and B panels in that XCD's L2.
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;
 // Group widths (m-tiles per group) of each GEMM; a group is swept with m
@@ -254,12 +271,6 @@ constexpr int kXcds = 8;
 #define LMH_GM_DW 8
 #endif
 
-__device__ __forceinline__ int xcd_logical(int round, int grid) {
-  const int b = blockIdx.x;
-  const int per = grid / kXcds;  // grid is a multiple of kXcds
-  return round * grid + (b % kXcds) * per + (b / kXcds);
-}
-
 template <int GM>
 __device__ __forceinline__ void tile_coords(int t, int mt, int nt, int& tm, int& tn) {
   const int per_group = GM * nt;
@@ -269,6 +280,53 @@ __device__ __forceinline__ void tile_coords(int t, int mt, int nt, int& tm, int&
   const int r = t - g * per_group;
   tm = first + r % gm;
   tn = r / gm;
+}
+
+// Dynamic tile queues. Logical tiles are dealt to the XCDs as in the static
+// order above (the per = grid / 8 workgroups of an XCD take consecutive
+// logical tiles of each round), but each XCD hands its tiles out from its own
+// counter in device memory, and with `steal` a workgroup whose XCD has none
+// left takes the next tile of another XCD's queue. The XCDs do not run at the
+// same speed under these kernels (measured: up to 4 % apart), so with a fixed
+// assignment the slowest one sets the kernel time; stealing only pays when a
+// tile is a small part of a workgroup's work, so the host enables it for
+// launches with many tiles per workgroup.
+struct TileQueue {
+  int* ctr;    // [kXcds] counters, zero before the launch
+  int ntiles;  // logical tiles of this launch
+  int steal;
+};
+
+__device__ __forceinline__ int xcd_id() {
+  // s_getreg_b32 hwreg(HW_REG_XCC_ID, 0, 4): the XCD this wave runs on
+  return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kXcds - 1);
+}
+
+// The next logical tile for the calling workgroup, or -1 when none is left.
+// One thread takes it with a vector atomic and broadcasts it through the
+// first word of `bcast` (LDS that no load in flight writes; see the kernels);
+// contains a workgroup barrier.
+__device__ __forceinline__ int queue_tile(const TileQueue& q, char* bcast) {
+  volatile int* slot = reinterpret_cast<volatile int*>(bcast);
+  if (threadIdx.x == 0) {
+    const int grid = gridDim.x;
+    const int per = grid / kXcds;
+    const int full = q.ntiles / grid, rem = q.ntiles - full * grid;
+    const int x = xcd_id();
+    int t = -1;
+    for (int d = 0; d < (q.steal ? kXcds : 1); ++d) {
+      const int y = (x + d) & (kXcds - 1);
+      const int count = full * per + min(per, max(0, rem - per * y));
+      const int k = atomicAdd(&q.ctr[y], 1);
+      if (k < count) {
+        t = (k / per) * grid + y * per + k % per;
+        break;
+      }
+    }
+    *slot = t;
+  }
+  __syncthreads();
+  return *slot;
 }
 
 // ---------------------------------------------------------------------------

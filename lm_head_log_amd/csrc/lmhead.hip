@@ -95,15 +95,17 @@ static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * 
 // Pitch of the transposed kept rows X_c^T [H][ldc].
 static inline int64_t ldc_of(int64_t N) { return round_up(N, 64); }
 
-// Forward workspace: target logits [N] | partial m, s, b [n_vt][N] each |
-// X_c^T [H][ldc] (bf16).
+// Forward workspace: tile-queue counters | target logits [N] | partial m, s, b
+// [n_vt][N] each | X_c^T [H][ldc] (bf16).
 struct FwdWs {
-  size_t zt, pm, ps, pb, xct, total;
+  size_t q, zt, pm, ps, pb, xct, total;
 };
+constexpr int kQueueInts = 8;  // one tile-queue counter per XCD
 static inline FwdWs fwd_ws(int64_t N, int64_t H, int64_t V) {
   const size_t nv = (size_t)n_vtiles(V);
   FwdWs w;
-  w.zt = 0;
+  w.q = 0;
+  w.zt = w.q + align256(kQueueInts * 4);
   w.pm = w.zt + align256((size_t)N * 4);
   w.ps = w.pm + align256(nv * (size_t)N * 4);
   w.pb = w.ps + align256(nv * (size_t)N * 4);
@@ -129,14 +131,19 @@ static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
   return g;
 }
 
-// Backward workspace: X_c^T [H][ldc] | dZ [C][ldz], both bf16.
+// Backward workspace: tile-queue counters (three GEMMs per chunk) |
+// X_c^T [H][ldc] | dZ [C][ldz], both bf16.
 struct BwdWs {
-  size_t xct, dz, total;
+  size_t q, xct, dz, total;
+  int64_t nq;  // counters
 };
 static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
   const BwdGeom g = bwd_geom(N, V, token_chunk);
   BwdWs w;
-  w.xct = 0;
+  const int64_t nchunks = N > 0 ? (N + g.C - 1) / g.C : 1;
+  w.nq = nchunks * 3 * kQueueInts;
+  w.q = 0;
+  w.xct = w.q + align256((size_t)w.nq * 4);
   w.dz = w.xct + align256((size_t)H * (size_t)ldc_of(N) * 2);
   w.total = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
   return w;
@@ -293,6 +300,8 @@ struct FwdParams {
   float* ps;
   float* pb;
   float* zt;
+  int* queue;  // tile-queue counters of this launch (zero before it)
+  int steal;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
@@ -305,17 +314,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
   const int nt = (rows + kBN - 1) / kBN;
   const int ntiles = mt * nt;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   const int nk = P.H / kBK;
 
-  for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
-    const int t = xcd_logical(round, gridDim.x);
-    if (t >= ntiles) continue;
+  const TileQueue q = {P.queue, ntiles, P.steal};
+  for (;;) {
+    // B slot 3 is free here (see queue_tile): this wave's loads into it are
+    // done, and the next tile's loads write it only after its first barrier
+    const int t = queue_tile(q, rb3);
+    if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_FWD>(t, mt, nt, tm, tn);
-    __syncthreads();
 
     ASrc A;
     BSrc B;
@@ -323,6 +331,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     B.init(P.XcT + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
     mainloop(A, B, nk, ring, acc);
+    // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
+    // out of the tile loop to be spilled across the main loop
+    const int lane = lane_fresh(), wave = wave_fresh();
+    const int wm = wave >> 1, wn = wave & 1;
 
     const int vbase = tm * kBM + wm * 128;
     const bool full = vbase + 128 <= P.V;
@@ -466,6 +478,11 @@ __global__ void k_zero_skipped(const int32_t* __restrict__ pos, int N, float* __
 // ---------------------------------------------------------------------------
 // Backward kernels.
 // ---------------------------------------------------------------------------
+// Zeroes n ints (the tile-queue counters of the launches that follow).
+__global__ void k_zero_ints(int* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
 __global__ void k_zero_rows(const int32_t* __restrict__ pos, int N, int H, float* __restrict__ dX) {
   const int i = blockIdx.x;
   if (i >= N || pos[i] >= 0) return;
@@ -485,6 +502,8 @@ struct DzParams {
   int64_t ldc;
   int64_t ldz;   // dZ row pitch (V rounded up to 256)
   uint16_t* dZ;  // [C][ldz] token-major: A of dX = dZ W, B of dW^T = X_c^T dZ
+  int* queue;  // tile-queue counters of this launch (zero before it)
+  int steal;
 };
 
 // bf16 pairs: (__bf16)x rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950)
@@ -500,18 +519,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
   const int nt = (rows + kBN - 1) / kBN;
   const int ntiles = mt * nt;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   const int nk = P.H / kBK;
   const int32_t* kidx = P.sv.kept_idx + P.c0;
 
-  for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
-    const int t = xcd_logical(round, gridDim.x);
-    if (t >= ntiles) continue;
+  const TileQueue q = {P.queue, ntiles, P.steal};
+  for (;;) {
+    // B slot 3 is free here (see queue_tile): this wave's loads into it are
+    // done, and the next tile's loads write it only after its first barrier
+    const int t = queue_tile(q, rb3);
+    if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_DZ>(t, mt, nt, tm, tn);
-    __syncthreads();
 
     ASrc A;
     BSrc B;
@@ -519,6 +537,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     B.init(P.XcT + P.c0 + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
     mainloop(A, B, nk, ring, acc);
+    // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
+    // out of the tile loop to be spilled across the main loop
+    const int lane = lane_fresh(), wave = wave_fresh();
+    const int wm = wave >> 1, wn = wave & 1;
 
     const int vbase = tm * kBM + wm * 128;
     // Tokens past the chunk's rows have ca = cb = 0 and a zero logit, so their
@@ -592,6 +614,8 @@ struct DxParams {
   int c0, C;
   int64_t ldz;
   float* dX;
+  int* queue;  // tile-queue counters of this launch (zero before it)
+  int steal;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
@@ -604,18 +628,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   const int nt = (P.H + kBN - 1) / kBN;
   const int ntiles = mt * nt;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   const int nk = (P.V + kBK - 1) / kBK;  // W reads zero past V
   const int32_t* kidx = P.sv.kept_idx + P.c0;
 
-  for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
-    const int t = xcd_logical(round, gridDim.x);
-    if (t >= ntiles) continue;
+  const TileQueue q = {P.queue, ntiles, P.steal};
+  for (;;) {
+    // B slot 3 is free here (see queue_tile): this wave's loads into it are
+    // done, and the next tile's loads write it only after its first barrier
+    const int t = queue_tile(q, rb3);
+    if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_DX>(t, mt, nt, tm, tn);
-    __syncthreads();
 
     ASrc A;
     BSrc B;
@@ -623,6 +646,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     B.init(P.W + (int64_t)tn * kBN, P.H, P.V, P.H - tn * kBN);
     f32x16_t acc[4][4];
     mainloop(A, B, nk, ring, acc);
+    // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
+    // out of the tile loop to be spilled across the main loop
+    const int lane = lane_fresh(), wave = wave_fresh();
+    const int wm = wave >> 1, wn = wave & 1;
 
     const int mrow = tm * kBM + wm * 128 + acc_row_lane(lane);
     const int mlim = rows - mrow;
@@ -652,6 +679,8 @@ struct DwParams {
   int64_t ldc, ldz;
   int accumulate;
   float* dW;
+  int* queue;  // tile-queue counters of this launch (zero before it)
+  int steal;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
@@ -667,17 +696,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
   const int nt = (P.V + kBN - 1) / kBN;
   const int ntiles = mt * nt;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   const int nk = (rows + kBK - 1) / kBK;  // dZ rows past `rows` read as zero
 
-  for (int round = 0; round * (int)gridDim.x < ntiles; ++round) {
-    const int t = xcd_logical(round, gridDim.x);
-    if (t >= ntiles) continue;
+  const TileQueue q = {P.queue, ntiles, P.steal};
+  for (;;) {
+    // B slot 3 is free here (see queue_tile): this wave's loads into it are
+    // done, and the next tile's loads write it only after its first barrier
+    const int t = queue_tile(q, rb3);
+    if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_DW>(t, mt, nt, tm, tn);
-    __syncthreads();
 
     ASrc A;
     BSrc B;
@@ -685,6 +713,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     B.init(P.dZ + (int64_t)tn * kBN, P.ldz, rows, kBN);  // ldz covers every v of the tile
     f32x16_t acc[4][4];
     mainloop(A, B, nk, ring, acc);
+    // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
+    // out of the tile loop to be spilled across the main loop
+    const int lane = lane_fresh(), wave = wave_fresh();
+    const int wm = wave >> 1, wn = wave & 1;
 
     // lane: vocabulary row v (column of the tile) and, per register group,
     // four consecutive h: one 16-byte store into dW[v][h .. h + 3]
@@ -744,6 +776,10 @@ static int persistent_grid(int64_t max_tiles) {
   return (int)(need < g ? need : g);
 }
 
+// Tile stealing between XCDs pays only when a tile is a small part of a
+// workgroup's work.
+static inline int steal_for(int64_t tiles, int grid) { return tiles >= 16 * (int64_t)grid; }
+
 static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 static int check_sizes(int64_t N, int64_t H, int64_t V) {
@@ -759,11 +795,11 @@ static int check_sizes(int64_t N, int64_t H, int64_t V) {
 // the launch stream around every launch while profiling is on.
 enum KernelKind {
   KK_COMPACT = 0, KK_GATHER_COLS, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS,
-  KK_DZ, KK_DX, KK_DW, KK_COUNT
+  KK_DZ, KK_DX, KK_DW, KK_ZERO_QUEUES, KK_COUNT
 };
 static const char* const kKernelNames[KK_COUNT] = {
-    "compact",   "gather_cols", "fwd_tiles", "merge",   "zero_skipped",
-    "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles"};
+    "compact",   "gather_cols", "fwd_tiles", "merge",    "zero_skipped",
+    "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles", "zero_queues"};
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -884,7 +920,11 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
   P.ps = reinterpret_cast<float*>(w + L.ps);
   P.pb = reinterpret_cast<float*>(w + L.pb);
   const int64_t max_tiles = (int64_t)nv * ((N + kBN - 1) / kBN);
-  LMH_TRY(launch(KK_FWD, k_fwd_tiles, dim3(persistent_grid(max_tiles)), dim3(kThreads), s, P));
+  const int grid = persistent_grid(max_tiles);
+  P.queue = reinterpret_cast<int*>(w + L.q);
+  P.steal = steal_for(max_tiles, grid);
+  LMH_TRY(launch(KK_ZERO_QUEUES, k_zero_ints, dim3(1), dim3(64), s, P.queue, kQueueInts));
+  LMH_TRY(launch(KK_FWD, k_fwd_tiles, dim3(grid), dim3(kThreads), s, P));
 
   LMH_TRY(launch(KK_MERGE, k_merge, dim3((unsigned)((N + kMergeRows - 1) / kMergeRows)), dim3(256),
                  s, (const float*)P.pm, (const float*)P.ps, (const float*)P.pb,
@@ -922,6 +962,9 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
   const uint16_t* X = static_cast<const uint16_t*>(hidden);
   const uint16_t* Wt = static_cast<const uint16_t*>(weight);
   const int64_t ldc = ldc_of(N);
+  int* queues = reinterpret_cast<int*>(w + L.q);
+  LMH_TRY(launch(KK_ZERO_QUEUES, k_zero_ints, dim3((unsigned)((L.nq + 255) / 256)), dim3(256), s,
+                 queues, (int)L.nq));
 
   if (N > 0) {
     LMH_TRY(launch(KK_ZERO_ROWS, k_zero_rows, dim3((unsigned)N), dim3(256), s,
@@ -952,7 +995,10 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       D.ldz = G.ldz;
       D.dZ = dZ;
       const int64_t dz_tiles = (int64_t)nv * (G.C / kBN);
-      LMH_TRY(launch(KK_DZ, k_dz_tiles, dim3(persistent_grid(dz_tiles)), dim3(kThreads), s, D));
+      const int dz_grid = persistent_grid(dz_tiles);
+      D.queue = queues + (ch * 3 + 0) * kQueueInts;
+      D.steal = steal_for(dz_tiles, dz_grid);
+      LMH_TRY(launch(KK_DZ, k_dz_tiles, dim3(dz_grid), dim3(kThreads), s, D));
 
       DxParams X2;
       X2.dZ = dZ;
@@ -965,7 +1011,10 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       X2.C = (int)G.C;
       X2.dX = grad_hidden;
       const int64_t dx_tiles = (G.C / kBM) * ((H + kBN - 1) / kBN);
-      LMH_TRY(launch(KK_DX, k_dx_tiles, dim3(persistent_grid(dx_tiles)), dim3(kThreads), s, X2));
+      const int dx_grid = persistent_grid(dx_tiles);
+      X2.queue = queues + (ch * 3 + 1) * kQueueInts;
+      X2.steal = steal_for(dx_tiles, dx_grid);
+      LMH_TRY(launch(KK_DX, k_dx_tiles, dim3(dx_grid), dim3(kThreads), s, X2));
     }
     DwParams Wp;
     Wp.XcT = XcT;
@@ -980,7 +1029,10 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
     Wp.accumulate = ch > 0;
     Wp.dW = grad_weight;
     const int64_t dw_tiles = (int64_t)nv * ((H + kBN - 1) / kBN);
-    LMH_TRY(launch(KK_DW, k_dw_tiles, dim3(persistent_grid(dw_tiles)), dim3(kThreads), s, Wp));
+    const int dw_grid = persistent_grid(dw_tiles);
+    Wp.queue = queues + (ch * 3 + 2) * kQueueInts;
+    Wp.steal = steal_for(dw_tiles, dw_grid);
+    LMH_TRY(launch(KK_DW, k_dw_tiles, dim3(dw_grid), dim3(kThreads), s, Wp));
   }
   return LMHEAD_OK;
 }

@@ -81,14 +81,15 @@ def test_saved_state_is_far_below_one_full_vocab_activation(lib):
 def _fwd_ws(N, H, V):
     nv = (V + 255) // 256
     up64 = lambda x: (x + 63) // 64 * 64
-    return _align(4 * N) + 3 * _align(nv * N * 4) + _align(H * up64(N) * 2)
+    return _align(32) + _align(4 * N) + 3 * _align(nv * N * 4) + _align(H * up64(N) * 2)
 
 
 def _bwd_ws(N, H, V, chunk):
     up = lambda x, m: (x + m - 1) // m * m
     want = chunk if chunk > 0 else max(256, (8 << 30) // (2 * up(V, 256)) // 256 * 256)
     C = min(up(want, 256), up(N, 256)) if N > 0 else 0
-    return _align(H * up(N, 64) * 2) + _align(C * up(V, 256) * 2)
+    nchunks = (N + C - 1) // C if N > 0 else 1
+    return _align(nchunks * 3 * 32) + _align(H * up(N, 64) * 2) + _align(C * up(V, 256) * 2)
 
 
 def test_workspace_sizes(lib):
@@ -101,7 +102,9 @@ def test_workspace_sizes(lib):
     # V = 131072 (4 GiB)
     N, H, V = 16384, 4096, 131072
     assert _bwd_ws(N, H, V, 0) == _bwd_ws(N, H, V, 16384)
-    assert _bwd_ws(N, H, V, 0) - _bwd_ws(N, H, V, 4096) == (16384 - 4096) * V * 2
+    # the 4096-row chunking has four chunks' tile-queue counters instead of one
+    queues = _align(4 * 3 * 32) - _align(1 * 3 * 32)
+    assert _bwd_ws(N, H, V, 0) - _bwd_ws(N, H, V, 4096) == (16384 - 4096) * V * 2 - queues
     assert _bwd_ws(262144, 4096, 152064, 0) == _bwd_ws(262144, 4096, 152064, 28160)
     # invalid sizes
     assert lib.lmhead_fwd_workspace_bytes(10, 100, 1000) == 0
