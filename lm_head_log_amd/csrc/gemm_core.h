@@ -433,8 +433,19 @@ __device__ __forceinline__ void k_stage(const ASrc& A, const BSrc& B, int s, int
 // 6 and 4 stages), so every LDS access names a fixed slot: the compiler can
 // then see that fragment reads never alias the direct-to-LDS loads in flight
 // into other slots, and inserts no waits of its own.
+//
+// SHIFT (even, 0..10) starts the slot rotation at virtual stage SHIFT: the
+// first 12 - SHIFT stages run as straight-line copies of bodies SHIFT..11
+// before the loop, so a stage count with nk + SHIFT a multiple of 12 runs no
+// padding stage. Any other count runs up to 11 stages past nk, which read
+// zeros and add nothing (an early exit instead would be a branch out of the
+// unrolled body, and any such branch makes the register allocator spill
+// fragments inside the loop).
+template <int SHIFT = 0>
 __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, const Ring& R,
                                          f32x16_t (&acc)[4][4]) {
+  static_assert(SHIFT % 2 == 0 && SHIFT >= 0 && SHIFT < 12, "A pairs must stay aligned");
+  constexpr int kPeel = (12 - SHIFT) % 12;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1;
@@ -452,24 +463,29 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
   // Issue order matters: each stage's wait counts loads issued after the ones
   // it needs. At stage 0's wait, B stage 1 must be older than the last 12
   // loads (A pair 1's second half, B stage 2, pair 2's first half).
-  A.issue_half(0, np, 0, R.a[0]);
-  A.issue_half(0, np, 1, R.a[0]);
-  B.issue(0, R.b[0]);
-  B.issue(1, R.b[1]);
-  A.issue_half(1, np, 0, R.a[1]);
-  A.issue_half(1, np, 1, R.a[1]);
-  B.issue(2, R.b[2]);
+  constexpr int a0 = (SHIFT / 2) % 3, a1 = (SHIFT / 2 + 1) % 3;
+  constexpr int b0 = SHIFT % 4, b1 = (SHIFT + 1) % 4, b2 = (SHIFT + 2) % 4;
+  A.issue_half(0, np, 0, R.a[a0]);
+  A.issue_half(0, np, 1, R.a[a0]);
+  B.issue(0, R.b[b0]);
+  B.issue(1, R.b[b1]);
+  A.issue_half(1, np, 0, R.a[a1]);
+  A.issue_half(1, np, 1, R.a[a1]);
+  B.issue(2, R.b[b2]);
   // pair 0 and stage 0 landed: only stage 1, pair 1 and stage 2 may remain
   wait_vmcnt<kALoadsPerWavePair + 2 * kBLoadsPerWaveStage>();
   __builtin_amdgcn_s_barrier();
 
   Frags f0, f1;
-  read_frags(R.a[0], 0, R.b[0], 0, lane, wm, wn, f0);
-  // Whole periods of 12 stages: stages past nk read zeros and add nothing.
-  // An exit between stages would be cheaper for nk not a multiple of 12, but
-  // any branch out of the unrolled body makes the register allocator spill
-  // fragments inside the loop.
-  for (int s = 0; s < nk; s += 12) {
+  read_frags(R.a[a0], 0, R.b[b0], 0, lane, wm, wn, f0);
+  if constexpr (kPeel > 0) {
+#define LMH_PEEL(U) \
+  if constexpr (U >= SHIFT) k_stage<U>(A, B, U - SHIFT, np, R, lane, wm, wn, f0, f1, acc);
+    LMH_PEEL(0) LMH_PEEL(1) LMH_PEEL(2) LMH_PEEL(3) LMH_PEEL(4) LMH_PEEL(5)
+    LMH_PEEL(6) LMH_PEEL(7) LMH_PEEL(8) LMH_PEEL(9) LMH_PEEL(10) LMH_PEEL(11)
+#undef LMH_PEEL
+  }
+  for (int s = kPeel; s < nk; s += 12) {
 #define LMH_STAGE(U) k_stage<U>(A, B, s + U, np, R, lane, wm, wn, f0, f1, acc);
     LMH_STAGE(0) LMH_STAGE(1) LMH_STAGE(2) LMH_STAGE(3) LMH_STAGE(4) LMH_STAGE(5)
     LMH_STAGE(6) LMH_STAGE(7) LMH_STAGE(8) LMH_STAGE(9) LMH_STAGE(10) LMH_STAGE(11)
@@ -479,6 +495,9 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
   wait_vmcnt<0>();
   wait_lgkm0();
 }
+
+// The SHIFT that makes nk (even) stages run without padding.
+__host__ __device__ constexpr int stage_shift(int nk) { return (12 - nk % 12) % 12; }
 
 // Row (within the wave's 128-row half) held by accumulator register r of
 // block i: acc_row_fixed(i, r) + acc_row_lane(lane). Epilogues compare the

@@ -304,6 +304,7 @@ struct FwdParams {
   int steal;
 };
 
+template <int SHIFT>
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
   LMH_DECLARE_RING;
   // per-token partials of the two wave rows; reuses ring slot 0 after the main loop
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
     B.init(P.XcT + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, ring, acc);
+    mainloop<SHIFT>(A, B, nk, ring, acc);
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
     const int lane = lane_fresh(), wave = wave_fresh();
@@ -509,6 +510,7 @@ struct DzParams {
 // bf16 pairs: (__bf16)x rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
+template <int SHIFT>
 __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
   LMH_DECLARE_RING;
 
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
     B.init(P.XcT + P.c0 + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, ring, acc);
+    mainloop<SHIFT>(A, B, nk, ring, acc);
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
     const int lane = lane_fresh(), wave = wave_fresh();
@@ -844,6 +846,17 @@ static int launch(int kind, Kern k, dim3 grid, dim3 block, hipStream_t s, Args..
   return LMHEAD_OK;
 }
 
+// Launches the instance of a GEMM kernel for the stage shift (even, 0..10)
+// that makes its stage count run without padding (mainloop).
+template <class Params, class... Kernels>
+static int launch_shifted(int kind, int shift, dim3 grid, hipStream_t s, const Params& p,
+                          Kernels... k) {
+  void (*table[])(Params) = {k...};
+  static_assert(sizeof...(Kernels) == 6, "one instance per even shift");
+  return launch(kind, table[shift / 2], grid, dim3(kThreads), s, p);
+}
+
+
 #define LMH_TRY(expr)                  \
   do {                                 \
     const int st_ = (expr);            \
@@ -924,7 +937,9 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
   P.queue = reinterpret_cast<int*>(w + L.q);
   P.steal = steal_for(max_tiles, grid);
   LMH_TRY(launch(KK_ZERO_QUEUES, k_zero_ints, dim3(1), dim3(64), s, P.queue, kQueueInts));
-  LMH_TRY(launch(KK_FWD, k_fwd_tiles, dim3(grid), dim3(kThreads), s, P));
+  LMH_TRY(launch_shifted(KK_FWD, stage_shift((int)(H / kBK)), dim3(grid), s, P,
+                         k_fwd_tiles<0>, k_fwd_tiles<2>, k_fwd_tiles<4>, k_fwd_tiles<6>,
+                         k_fwd_tiles<8>, k_fwd_tiles<10>));
 
   LMH_TRY(launch(KK_MERGE, k_merge, dim3((unsigned)((N + kMergeRows - 1) / kMergeRows)), dim3(256),
                  s, (const float*)P.pm, (const float*)P.ps, (const float*)P.pb,
@@ -998,7 +1013,9 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       const int dz_grid = persistent_grid(dz_tiles);
       D.queue = queues + (ch * 3 + 0) * kQueueInts;
       D.steal = steal_for(dz_tiles, dz_grid);
-      LMH_TRY(launch(KK_DZ, k_dz_tiles, dim3(dz_grid), dim3(kThreads), s, D));
+      LMH_TRY(launch_shifted(KK_DZ, stage_shift((int)(H / kBK)), dim3(dz_grid), s, D,
+                             k_dz_tiles<0>, k_dz_tiles<2>, k_dz_tiles<4>, k_dz_tiles<6>,
+                             k_dz_tiles<8>, k_dz_tiles<10>));
 
       DxParams X2;
       X2.dZ = dZ;

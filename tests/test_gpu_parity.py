@@ -68,6 +68,8 @@ def test_config1_full_parity():
     (513, 320, 2049, 13),     # several tiles plus one-element tails
     (77, 128, 50000, 14),     # many vocab tiles, few rows
     (600, 256, 4096, 15),     # exact tiles in H and V
+    (130, 384, 3000, 16),     # H / 32 a multiple of 12: the unshifted main loop
+    (260, 704, 1500, 17),     # H / 32 = 22: shift 2, a peeled period longer than the loop's
 ])
 def test_ragged_shapes(N, H, V, seed):
     say(f"case: ragged N{N} H{H} V{V}")
