@@ -79,13 +79,16 @@ typedef enum {
 size_t lmhead_saved_bytes(int64_t N);
 
 /* Workspace bytes lmhead_fwd needs for N rows and vocabulary V: 8 tile-queue
- * counters, per row the target logit and, per 256-wide vocabulary tile, three
- * fp32 partial statistics, plus a bf16 transposed copy of the kept rows of X
+ * counters, the target of each kept row (N rounded up to 256 entries), per
+ * row the target logit and, per 256-wide vocabulary tile, three fp32 partial
+ * statistics, plus a bf16 transposed copy of the kept rows of X
  * ([H][N rounded up to 64]). Returns 0 on invalid sizes. */
 size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V);
 
-/* Workspace bytes lmhead_bwd needs: 24 tile-queue counters per token chunk, a
- * bf16 transposed copy of the kept rows of X ([H][N rounded up to 64]) and
+/* Workspace bytes lmhead_bwd needs: 24 tile-queue counters per token chunk,
+ * 20 bytes per kept row (N rounded up to 256 entries) of logit-gradient
+ * coefficients and targets, a bf16 transposed copy of the kept rows of X
+ * ([H][N rounded up to 64]) and
  * the bf16 logit gradient dZ of one chunk
  * of C rows ([C][V rounded up to 256], token-major), where C = token_chunk
  * rounded up to a multiple of 256 (at most N rounded up to 256).
@@ -164,8 +167,9 @@ int lmhead_version(void);
 
 /* Per-kernel timing for benchmarks (not needed to use the op).
  * Kernel kinds, in order: compact, gather_cols, fwd_tiles, merge,
- * zero_skipped, zero_rows, dz_tiles, dx_tiles, dw_tiles, zero_queues. */
-#define LMHEAD_NUM_KERNELS 10
+ * zero_skipped, zero_rows, dz_tiles, dx_tiles, dw_tiles, zero_queues,
+ * bwd_rows. */
+#define LMHEAD_NUM_KERNELS 11
 
 /* Static name of kernel kind `kind` (NULL if out of range). */
 const char* lmhead_kernel_name(int kind);

@@ -33,7 +33,7 @@ SIGNATURES = {
     "lmhead_profile_end": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
 }
 
-NUM_KERNELS = 10
+NUM_KERNELS = 11
 
 _lib = None
 

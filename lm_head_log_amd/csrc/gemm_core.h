@@ -117,6 +117,12 @@ __device__ __forceinline__ int lane_fresh() {
   asm volatile("" : "+v"(l));
   return l;
 }
+// A wave-uniform value the compiler cannot see through, so nothing derived
+// from it is computed ahead of the point where it is produced.
+__device__ __forceinline__ int sgpr_fresh(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
 __device__ __forceinline__ int wave_fresh() {
   int w = threadIdx.x >> 6;
   asm volatile("" : "+v"(w));
@@ -446,8 +452,10 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
                                          f32x16_t (&acc)[4][4]) {
   static_assert(SHIFT % 2 == 0 && SHIFT >= 0 && SHIFT < 12, "A pairs must stay aligned");
   constexpr int kPeel = (12 - SHIFT) % 12;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // fresh per call: the fragment addresses derived from them are computed per
+  // tile instead of being kept (and spilled) across the epilogues
+  const int lane = lane_fresh();
+  const int wave = wave_fresh();
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
@@ -480,7 +488,7 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
   read_frags(R.a[a0], 0, R.b[b0], 0, lane, wm, wn, f0);
   if constexpr (kPeel > 0) {
 #define LMH_PEEL(U) \
-  if constexpr (U >= SHIFT) k_stage<U>(A, B, U - SHIFT, np, R, lane, wm, wn, f0, f1, acc);
+  if constexpr (U >= SHIFT) k_stage<U>(A, B, sgpr_fresh(U - SHIFT), np, R, lane, wm, wn, f0, f1, acc);
     LMH_PEEL(0) LMH_PEEL(1) LMH_PEEL(2) LMH_PEEL(3) LMH_PEEL(4) LMH_PEEL(5)
     LMH_PEEL(6) LMH_PEEL(7) LMH_PEEL(8) LMH_PEEL(9) LMH_PEEL(10) LMH_PEEL(11)
 #undef LMH_PEEL
@@ -494,6 +502,24 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
   // stages and pairs past the end issued loads that nobody reads; let them land
   wait_vmcnt<0>();
   wait_lgkm0();
+}
+
+// Epilogue reads of the accumulators. The compiler, left to itself, copies
+// every accumulator block to vector registers right after the main loop (the
+// copies land in the loop's exit block, ahead of the epilogue's branches),
+// which fills the register file and serialises the epilogue. acc_read moves
+// one accumulator register where its value is used. The hardware does not
+// interlock an accumulator read on an MFMA still writing it, and the compiler
+// does not see into the asm, so acc_read_fence (24 wait states, more than the
+// write-to-read distance of even a 16-pass MFMA) must separate the main loop
+// from the first acc_read.
+__device__ __forceinline__ void acc_read_fence() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+__device__ __forceinline__ float acc_read(float x) {
+  float y;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
+  return y;
 }
 
 // The SHIFT that makes nk (even) stages run without padding.

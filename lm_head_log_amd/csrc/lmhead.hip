@@ -4,7 +4,8 @@
 // Forward (prime-rl PR #3326 Overview: compact -> chunked log-prob/entropy ->
 // expand back; SkyRL PR #2374 "How it works": one projection gives both the
 // selected-token log-prob and the entropy):
-//   1. k_compact     keep mask -> ascending kept rows, row -> compact position
+//   1. k_compact     keep mask -> ascending kept rows, row -> compact position,
+//                    target of each compact row
 //   2. k_gather_cols X_c^T = X[kept]^T [h][c], the token operand of the logit
 //                    GEMM (k = h rows, tokens contiguous)
 //   3. k_fwd_tiles   Z^T tile = W[vtile] X[kept]^T on MFMA, never stored; per
@@ -15,9 +16,11 @@
 //   5. k_zero_skipped  +0.0 log-prob / entropy at skipped rows
 // Backward (twinkle PR #283 section 1: recompute the softmax from saved inputs;
 // SkyRL PR #2374 review: entropy is saved by the forward, not recomputed):
-//   1. k_zero_rows   +0.0 dX rows at skipped positions
-//   2. k_gather_cols X_c^T
-//   3. per chunk of kept rows:
+//   1. k_bwd_rows    per kept row: LSE, upstream grads and target folded into
+//                    the coefficients of dz as a function of the logit
+//   2. k_zero_rows   +0.0 dX rows at skipped positions
+//   3. k_gather_cols X_c^T
+//   4. per chunk of kept rows:
 //      k_dz_tiles    recompute Z^T tile, p = exp(z - LSE),
 //                    dZ = g_lp (onehot - p) - g_H p (z - LSE + H), bf16,
 //                    stored token-major [c][v]
@@ -32,6 +35,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/lmhead.h"
@@ -43,7 +47,6 @@ namespace lmh {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kMaskedLogit = -1e30f;  // stands in for the logit of a vocabulary row past V
 // Default token chunk: the largest multiple of 256 rows whose bf16 dZ buffer
 // fits this budget. The pages' fused head defaults to 8192 rows to bound
 // memory on an 80 GB part; with 288 GB of HBM the budget admits a whole
@@ -95,17 +98,21 @@ static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * 
 // Pitch of the transposed kept rows X_c^T [H][ldc].
 static inline int64_t ldc_of(int64_t N) { return round_up(N, 64); }
 
-// Forward workspace: tile-queue counters | target logits [N] | partial m, s, b
-// [n_vt][N] each | X_c^T [H][ldc] (bf16).
+// Rows of the per-token arrays the GEMM epilogues read: whole 256-token tiles.
+static inline int64_t tile_rows(int64_t N) { return round_up(N, 256); }
+
+// Forward workspace: tile-queue counters | compact targets [tile_rows] |
+// target logits [N] | partial m, s, b [n_vt][N] each | X_c^T [H][ldc] (bf16).
 struct FwdWs {
-  size_t q, zt, pm, ps, pb, xct, total;
+  size_t q, tg, zt, pm, ps, pb, xct, total;
 };
 constexpr int kQueueInts = 8;  // one tile-queue counter per XCD
 static inline FwdWs fwd_ws(int64_t N, int64_t H, int64_t V) {
   const size_t nv = (size_t)n_vtiles(V);
   FwdWs w;
   w.q = 0;
-  w.zt = w.q + align256(kQueueInts * 4);
+  w.tg = w.q + align256(kQueueInts * 4);
+  w.zt = w.tg + align256((size_t)tile_rows(N) * 4);
   w.pm = w.zt + align256((size_t)N * 4);
   w.ps = w.pm + align256(nv * (size_t)N * 4);
   w.pb = w.ps + align256(nv * (size_t)N * 4);
@@ -131,10 +138,11 @@ static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
   return g;
 }
 
-// Backward workspace: tile-queue counters (three GEMMs per chunk) |
-// X_c^T [H][ldc] | dZ [C][ldz], both bf16.
+// Backward workspace: tile-queue counters (three GEMMs per chunk) | per-row
+// dZ coefficients (float4) and compact targets [tile_rows] | X_c^T [H][ldc] |
+// dZ [C][ldz], both bf16.
 struct BwdWs {
-  size_t q, xct, dz, total;
+  size_t q, rc, tg, xct, dz, total;
   int64_t nq;  // counters
 };
 static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
@@ -143,7 +151,9 @@ static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk)
   const int64_t nchunks = N > 0 ? (N + g.C - 1) / g.C : 1;
   w.nq = nchunks * 3 * kQueueInts;
   w.q = 0;
-  w.xct = w.q + align256((size_t)w.nq * 4);
+  w.rc = w.q + align256((size_t)w.nq * 4);
+  w.tg = w.rc + align256((size_t)tile_rows(N) * 16);
+  w.xct = w.tg + align256((size_t)tile_rows(N) * 4);
   w.dz = w.xct + align256((size_t)H * (size_t)ldc_of(N) * 2);
   w.total = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
   return w;
@@ -157,7 +167,7 @@ constexpr int kCompactThreads = 1024;
 __global__ __launch_bounds__(kCompactThreads) void k_compact(
     const uint8_t* __restrict__ keep, const int32_t* __restrict__ targets, int N, int H, int V,
     int flags, int32_t* __restrict__ kept_idx, int32_t* __restrict__ pos,
-    SavedHeader* __restrict__ hdr) {
+    SavedHeader* __restrict__ hdr, int32_t* __restrict__ tg, int tg_rows) {
   __shared__ int scan[kCompactThreads];
   const int tid = threadIdx.x;
   const int seg = (N + kCompactThreads - 1) / kCompactThreads;
@@ -179,15 +189,18 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(
   for (int i = beg; i < end; ++i) {
     const bool k = keep ? (keep[i] != 0) : true;
     if (k) {
+      const int t = targets[i];
       kept_idx[o] = i;
       pos[i] = o;
+      tg[o] = t;
       ++o;
-      const int t = targets[i];
       bad |= (t < 0 || t >= V);
     } else {
       pos[i] = -1;
     }
   }
+  // compact targets past the kept rows: -1 matches no vocabulary row
+  for (int c = scan[kCompactThreads - 1] + tid; c < tg_rows; c += kCompactThreads) tg[c] = -1;
   bad = __syncthreads_or(bad);
   if (tid == 0) {
     hdr->n_kept = scan[kCompactThreads - 1];
@@ -290,8 +303,7 @@ __global__ __launch_bounds__(256) void k_gather_cols(const uint16_t* __restrict_
 struct FwdParams {
   const uint16_t* W;    // [V][H]
   const uint16_t* XcT;  // [H][ldc]
-  const int32_t* targets;
-  const int32_t* kept_idx;
+  const int32_t* tg;    // [tile_rows] target of each compact row, -1 past the kept rows
   const SavedHeader* hdr;
   int H, V, n_vt;
   int64_t ldc;
@@ -326,6 +338,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     int tm, tn;
     tile_coords<LMH_GM_FWD>(t, mt, nt, tm, tn);
 
+    // targets of this lane's four tokens, loaded before the main loop so that
+    // their latency is hidden under it
+    int tgt[4];
+    {
+      const int* tp = P.tg + tn * kBN + (wave_fresh() & 1) * 128 + (lane_fresh() & 31);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tgt[j] = tp[j * 32];
+    }
+
     ASrc A;
     BSrc B;
     A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
@@ -340,71 +361,81 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     const int vbase = tm * kBM + wm * 128;
     const bool full = vbase + 128 <= P.V;
     const int vlim = P.V - vbase - acc_row_lane(lane);  // rows acc_row_fixed < vlim are valid
-    const bool none = vlim <= 0;                         // this lane's rows are all past V
-    if (!full) {
-      // Rows at or past V get a large finite negative logit: exp2 of it minus
-      // any real maximum is exactly 0 and 0 * y stays finite. Done once for
-      // the four column blocks, so no per-row mask outlives this loop.
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool ok = acc_row_fixed(i, r) < vlim;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j][r] = ok ? acc[i][j][r] : kMaskedLogit;
-        }
-    }
     __syncthreads();  // every wave is done reading the ring
+    acc_read_fence();
+    // Per token (column j of this lane): m = max y, s = sum 2^(y - m) and
+    // b = sum 2^(y - m) (y - m) over this lane's 64 vocabulary rows, merged
+    // with the other half of the wave (the other 64 rows) and staged in LDS
+    // for the merge of the two wave rows; then the target pick. The masked
+    // form leaves out rows at or past V, which only the last vocabulary tile
+    // has; a lane with no valid row gives the empty partial (-inf, 0, 0).
+    auto columns = [&](auto masked_t) {
+      constexpr bool kMasked = decltype(masked_t)::value;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int cl = wn * 128 + j * 32 + (lane & 31);  // token inside the tile
-      const int c = tn * kBN + cl;                     // compact row
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
-      if (none) mx = -INFINITY;
-      float s = 0.f, b = 0.f;
-      if (mx != -INFINITY) {
+      for (int j = 0; j < 4; ++j) {
+        const int cl = wn * 128 + j * 32 + (lane & 31);  // token inside the tile
+        const int c = tn * kBN + cl;                     // compact row
+        // this lane's 64 logits of the token, each accumulator read once; the
+        // masked form replaces rows at or past V by a large finite negative
+        // logit, whose 2^(y - m) is exactly 0 next to any real maximum while
+        // 0 * y stays finite
+        // (the row limit is made opaque per column so that the 64 row masks
+        // are recomputed, not kept in scalar registers across columns)
+        int vl = vlim;
+        if (kMasked) asm volatile("" : "+v"(vl));
+        float v[64];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float y = (acc[i][j][r] - mx) * kLog2e;
+          for (int r = 0; r < 16; ++r)
+            v[i * 16 + r] =
+                (!kMasked || acc_row_fixed(i, r) < vl) ? acc_read(acc[i][j][r]) : -1e30f;
+        float mx = v[0];
+#pragma unroll
+        for (int k = 1; k < 64; ++k) mx = fmaxf(mx, v[k]);
+        if (kMasked && vlim <= 0) mx = -INFINITY;  // no valid row: the empty partial
+        float m = (mx == -INFINITY) ? -INFINITY : mx * kLog2e;
+        float s = 0.f, b = 0.f;
+        if (mx != -INFINITY) {
+#pragma unroll
+          for (int k = 0; k < 64; ++k) {
+            // y = z log2 e - m: 0 up to the rounding of m at the maximum
+            const float y = fmaf(v[k], kLog2e, -m);
             const float e = __builtin_amdgcn_exp2f(y);
             s += e;
             b = fmaf(e, y, b);
           }
-      }
-      float m = (mx == -INFINITY) ? -INFINITY : mx * kLog2e;
-      // the other half of the wave holds the other 64 rows of the same token
-      const float mo = __shfl_xor(m, 32);
-      const float so = __shfl_xor(s, 32);
-      const float bo = __shfl_xor(b, 32);
-      stat_merge(m, s, b, mo, so, bo);
-      if (lane < 32) {
-        red[wm][0][cl] = m;
-        red[wm][1][cl] = s;
-        red[wm][2][cl] = b;
-      }
-      // target pick: exactly one lane in the grid holds z[t] for this token
-      if (c < rows) {
-        const int tt = P.targets[P.kept_idx[c]];
-        const int local = tt - vbase;
+        }
+        const float mo = __shfl_xor(m, 32);
+        const float so = __shfl_xor(s, 32);
+        const float bo = __shfl_xor(b, 32);
+        stat_merge(m, s, b, mo, so, bo);
+        if (lane < 32) {
+          red[wm][0][cl] = m;
+          red[wm][1][cl] = s;
+          red[wm][2][cl] = b;
+        }
+        // exactly one lane in the grid holds z[t] for a kept token (the
+        // target of a token past the kept rows is -1 and never hits)
+        const int local = tgt[j] - vbase;
         const int w = local & 31;
         const bool hit = local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
         if (hit) {
           const int want = (local >> 5) * 16 + ((w >> 3) << 2) + (w & 3);
           float z = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) z = (want == i * 16 + r) ? acc[i][j][r] : z;
+          for (int k = 0; k < 64; ++k) z = (want == k) ? v[k] : z;
           P.zt[c] = z;
         }
+        // one column at a time: keeps the copies of the accumulators out of
+        // the way of the other columns (no spills)
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    };
+    if (full)
+      columns(std::false_type{});
+    else
+      columns(std::true_type{});
     __syncthreads();
     {
       const int cl = tid;  // one token per thread
@@ -432,7 +463,7 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm,
                                                const float* __restrict__ ps,
                                                const float* __restrict__ pb,
                                                const float* __restrict__ zt, int64_t ldp, int n_vt,
-                                               const int32_t* __restrict__ targets, int V,
+                                               const int32_t* __restrict__ tg, int V,
                                                SavedView sv, float* __restrict__ logp,
                                                float* __restrict__ entropy) {
   __shared__ float sh[3][4][kMergeRows];
@@ -458,7 +489,7 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm,
     const float lse = (m + l2s) * kLn2;
     const float ent = (l2s - b / s) * kLn2;
     const int row = sv.kept_idx[c];
-    const int t = targets[row];
+    const int t = tg[c];
     const float lp = (t >= 0 && t < V) ? zt[c] - lse : __builtin_nanf("");
     sv.lse[c] = lse;
     sv.ent[c] = ent;
@@ -491,12 +522,39 @@ __global__ void k_zero_rows(const int32_t* __restrict__ pos, int N, int H, float
   for (int k = threadIdx.x; k < H / 4; k += blockDim.x) row[k] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// Per compact row c, the coefficients of dz as a function of the logit z:
+//   dz = p (ca + cb (z - LSE)) + g_lp [v = t],  p = 2^(z log2 e - LSE log2 e),
+//   ca = -(g_lp + g_H H),  cb = -g_H,
+// stored as {LSE log2 e, ca - cb LSE, cb, g_lp} with the target t beside it.
+// Rows past the kept ones get zeros and target -1, so their dz is exactly 0.
+__global__ __launch_bounds__(256) void k_bwd_rows(SavedView sv, const int32_t* __restrict__ targets,
+                                                  const float* __restrict__ g_lp,
+                                                  const float* __restrict__ g_h, int n_rows,
+                                                  float4* __restrict__ rc,
+                                                  int32_t* __restrict__ tg) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n_rows) return;
+  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+  int t = -1;
+  if (c < sv.hdr->n_kept) {
+    const int row = sv.kept_idx[c];
+    const float lse = sv.lse[c];
+    const float glp = g_lp[row];
+    const float gh = g_h ? g_h[row] : 0.f;
+    const float ent = g_h ? sv.ent[c] : 0.f;
+    const float ca = -(glp + gh * ent), cb = -gh;
+    r = make_float4(lse * kLog2e, ca - cb * lse, cb, glp);
+    t = targets[row];
+  }
+  rc[c] = r;
+  tg[c] = t;
+}
+
 struct DzParams {
   const uint16_t* W;    // [V][H]
   const uint16_t* XcT;  // [H][ldc]
-  const int32_t* targets;
-  const float* g_lp;
-  const float* g_h;  // null when the entropy term is off
+  const float4* rc;     // [tile_rows] dz coefficients per compact row (k_bwd_rows)
+  const int32_t* tg;    // [tile_rows] target per compact row, -1 past the kept rows
   SavedView sv;
   int H, V, n_vt;
   int c0, C;     // chunk start (compact rows) and chunk capacity (multiple of 256)
@@ -522,7 +580,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
   const int ntiles = mt * nt;
   const int tid = threadIdx.x;
   const int nk = P.H / kBK;
-  const int32_t* kidx = P.sv.kept_idx + P.c0;
 
   const TileQueue q = {P.queue, ntiles, P.steal};
   for (;;) {
@@ -532,6 +589,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_DZ>(t, mt, nt, tm, tn);
+
+    // coefficients and targets of this lane's four tokens, loaded before the
+    // main loop so that their latency is hidden under it
+    float4 rcv[4];
+    int tgt[4];
+    {
+      const int c = P.c0 + tn * kBN + (wave_fresh() & 1) * 128 + (lane_fresh() & 31);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        rcv[j] = P.rc[c + j * 32];
+        tgt[j] = P.tg[c + j * 32];
+      }
+    }
 
     ASrc A;
     BSrc B;
@@ -545,63 +615,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     const int wm = wave >> 1, wn = wave & 1;
 
     const int vbase = tm * kBM + wm * 128;
-    // Tokens past the chunk's rows have ca = cb = 0 and a zero logit, so their
-    // dz is exactly 0. Vocabulary rows at or past V are not masked: those
+    acc_read_fence();
+    // Tokens past the kept rows have zero coefficients and a zero logit, so
+    // their dz is exactly 0. Vocabulary rows at or past V are not masked: those
     // columns of dZ hold finite values that no consumer uses (dX = dZ W reads
     // W rows at or past V as zero; dW^T never stores columns at or past V).
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = tn * kBN + wn * 128 + j * 32 + (lane & 31);  // chunk row
-      const bool crow = c < rows;
-      float lse = 0.f, ent = 0.f, glp = 0.f, gh = 0.f;
-      int tt = -1;
-      if (crow) {
-        const int cc = P.c0 + c;
-        const int row = kidx[c];
-        lse = P.sv.lse[cc];
-        glp = P.g_lp[row];
-        tt = P.targets[row];
-        if (P.g_h) {
-          gh = P.g_h[row];
-          ent = P.sv.ent[cc];
-        }
-      }
-      // dz = -p (glp + gh (lp + ent)) = p (ca + cb lp), lp = z - lse
-      const float ca = -(glp + gh * ent);
-      const float cb = -gh;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // subtract before scaling: z - lse is exact near the row maximum
-          const float lp = acc[i][j][r] - lse;
-          const float p = __builtin_amdgcn_exp2f(lp * kLog2e);
-          acc[i][j][r] = p * fmaf(cb, lp, ca);
-        }
-      const int local = tt - vbase;
+      const float4 k = rcv[j];  // {LSE log2 e, ca - cb LSE, cb, g_lp}
+      const int local = tgt[j] - vbase;
       const int w = local & 31;
-      const bool hit = crow && local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
-      if (hit) {
-        const int want = (local >> 5) * 16 + ((w >> 3) << 2) + (w & 3);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (want == i * 16 + r) acc[i][j][r] += glp;
-      }
-      // dZ[c][v]: four consecutive v per register group (8 bytes)
+      const bool hit = local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
+      const int want = (local >> 5) * 16 + ((w >> 3) << 2) + (w & 3);
       uint16_t* zrow = P.dZ + (int64_t)c * P.ldz;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        float d[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float z = acc_read(acc[i][j][r]);
+          const float p = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -k.x));
+          d[r] = p * fmaf(k.z, z, k.y);
+        }
+        // the one-hot term of the target, in the one lane that holds it
+        if (hit && (want >> 4) == i) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((want & 15) == r) d[r] += k.w;
+        }
+        // dZ[c][v]: four consecutive v per register group (8 bytes)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int v0 = vbase + i * 32 + 8 * g + 4 * (lane >> 5);
-          const bf16x2_t lo = {(__bf16)acc[i][j][4 * g + 0], (__bf16)acc[i][j][4 * g + 1]};
-          const bf16x2_t hi = {(__bf16)acc[i][j][4 * g + 2], (__bf16)acc[i][j][4 * g + 3]};
+          const bf16x2_t lo = {(__bf16)d[4 * g + 0], (__bf16)d[4 * g + 1]};
+          const bf16x2_t hi = {(__bf16)d[4 * g + 2], (__bf16)d[4 * g + 3]};
           const uint32_t plo = __builtin_bit_cast(uint32_t, lo);
           const uint32_t phi = __builtin_bit_cast(uint32_t, hi);
           *reinterpret_cast<uint2*>(zrow + v0) = make_uint2(plo, phi);
         }
+        // one register block at a time (bounds the live copies)
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
@@ -724,6 +779,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     // four consecutive h: one 16-byte store into dW[v][h .. h + 3]
     const int hrow = tm * kBM + wm * 128 + acc_row_lane(lane);
     const int hlim = P.H - hrow;
+    acc_read_fence();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int v = tn * kBN + wn * 128 + j * 32 + (lane & 31);
@@ -735,14 +791,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
         for (int g = 0; g < 4; ++g) {
           const int h = acc_row_fixed(i, 4 * g);
           if (h >= hlim) continue;  // H is a multiple of 4: the group is whole
-          float4 x = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                 acc[i][j][4 * g + 3]);
+          float4 x;
           if (P.accumulate) {
             const float4 o = *reinterpret_cast<const float4*>(wrow + h);
-            x.x += o.x;
-            x.y += o.y;
-            x.z += o.z;
-            x.w += o.w;
+            x.x = acc_read(acc[i][j][4 * g]) + o.x;
+            x.y = acc_read(acc[i][j][4 * g + 1]) + o.y;
+            x.z = acc_read(acc[i][j][4 * g + 2]) + o.z;
+            x.w = acc_read(acc[i][j][4 * g + 3]) + o.w;
+          } else {
+            x = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                            acc[i][j][4 * g + 3]);
           }
           *reinterpret_cast<float4*>(wrow + h) = x;
         }
@@ -797,11 +855,11 @@ static int check_sizes(int64_t N, int64_t H, int64_t V) {
 // the launch stream around every launch while profiling is on.
 enum KernelKind {
   KK_COMPACT = 0, KK_GATHER_COLS, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS,
-  KK_DZ, KK_DX, KK_DW, KK_ZERO_QUEUES, KK_COUNT
+  KK_DZ, KK_DX, KK_DW, KK_ZERO_QUEUES, KK_BWD_ROWS, KK_COUNT
 };
 static const char* const kKernelNames[KK_COUNT] = {
     "compact",   "gather_cols", "fwd_tiles", "merge",    "zero_skipped",
-    "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles", "zero_queues"};
+    "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles", "zero_queues", "bwd_rows"};
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -905,12 +963,14 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
   SavedView sv = saved_view(saved, N);
   const int flags = (return_entropy ? 1 : 0) | (entropy_requires_grad ? 2 : 0);
 
+  char* w = static_cast<char*>(workspace);
+  int32_t* tg = reinterpret_cast<int32_t*>(w + L.tg);
   LMH_TRY(launch(KK_COMPACT, k_compact, dim3(1), dim3(kCompactThreads), s, keep_mask, targets,
-                 (int)N, (int)H, (int)V, flags, sv.kept_idx, sv.pos, sv.hdr));
+                 (int)N, (int)H, (int)V, flags, sv.kept_idx, sv.pos, sv.hdr, tg,
+                 (int)tile_rows(N)));
   if (N == 0) return LMHEAD_OK;
 
   const int nv = n_vtiles(V);
-  char* w = static_cast<char*>(workspace);
   const int64_t ldc = ldc_of(N);
   uint16_t* XcT = reinterpret_cast<uint16_t*>(w + L.xct);
   LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(ldc / kTp), (unsigned)(H / kTp)),
@@ -921,8 +981,7 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
   P.W = static_cast<const uint16_t*>(weight);
   P.XcT = XcT;
   P.ldc = ldc;
-  P.targets = targets;
-  P.kept_idx = sv.kept_idx;
+  P.tg = tg;
   P.hdr = sv.hdr;
   P.H = (int)H;
   P.V = (int)V;
@@ -943,7 +1002,8 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
 
   LMH_TRY(launch(KK_MERGE, k_merge, dim3((unsigned)((N + kMergeRows - 1) / kMergeRows)), dim3(256),
                  s, (const float*)P.pm, (const float*)P.ps, (const float*)P.pb,
-                 (const float*)P.zt, (int64_t)N, nv, targets, (int)V, sv, logp, entropy));
+                 (const float*)P.zt, (int64_t)N, nv, (const int32_t*)tg, (int)V, sv, logp,
+                 entropy));
   LMH_TRY(launch(KK_ZERO_SKIPPED, k_zero_skipped, dim3((unsigned)((N + 255) / 256)), dim3(256), s,
                  (const int32_t*)sv.pos, (int)N, logp, entropy));
   return LMHEAD_OK;
@@ -978,10 +1038,16 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
   const uint16_t* Wt = static_cast<const uint16_t*>(weight);
   const int64_t ldc = ldc_of(N);
   int* queues = reinterpret_cast<int*>(w + L.q);
+  float4* rc = reinterpret_cast<float4*>(w + L.rc);
+  int32_t* tg = reinterpret_cast<int32_t*>(w + L.tg);
   LMH_TRY(launch(KK_ZERO_QUEUES, k_zero_ints, dim3((unsigned)((L.nq + 255) / 256)), dim3(256), s,
                  queues, (int)L.nq));
 
   if (N > 0) {
+    const int nrows = (int)tile_rows(N);
+    LMH_TRY(launch(KK_BWD_ROWS, k_bwd_rows, dim3((unsigned)(nrows / 256)), dim3(256), s, sv,
+                   targets, grad_logp, entropy_requires_grad ? grad_entropy : nullptr, nrows, rc,
+                   tg));
     LMH_TRY(launch(KK_ZERO_ROWS, k_zero_rows, dim3((unsigned)N), dim3(256), s,
                    (const int32_t*)sv.pos, (int)N, (int)H, grad_hidden));
     LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(ldc / kTp), (unsigned)(H / kTp)),
@@ -998,9 +1064,8 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
       D.W = Wt;
       D.XcT = XcT;
       D.ldc = ldc;
-      D.targets = targets;
-      D.g_lp = grad_logp;
-      D.g_h = entropy_requires_grad ? grad_entropy : nullptr;
+      D.rc = rc;
+      D.tg = tg;
       D.sv = sv;
       D.H = (int)H;
       D.V = (int)V;

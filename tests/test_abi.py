@@ -81,7 +81,9 @@ def test_saved_state_is_far_below_one_full_vocab_activation(lib):
 def _fwd_ws(N, H, V):
     nv = (V + 255) // 256
     up64 = lambda x: (x + 63) // 64 * 64
-    return _align(32) + _align(4 * N) + 3 * _align(nv * N * 4) + _align(H * up64(N) * 2)
+    rows = (N + 255) // 256 * 256
+    return (_align(32) + _align(4 * rows) + _align(4 * N) + 3 * _align(nv * N * 4)
+            + _align(H * up64(N) * 2))
 
 
 def _bwd_ws(N, H, V, chunk):
@@ -89,7 +91,9 @@ def _bwd_ws(N, H, V, chunk):
     want = chunk if chunk > 0 else max(256, (8 << 30) // (2 * up(V, 256)) // 256 * 256)
     C = min(up(want, 256), up(N, 256)) if N > 0 else 0
     nchunks = (N + C - 1) // C if N > 0 else 1
-    return _align(nchunks * 3 * 32) + _align(H * up(N, 64) * 2) + _align(C * up(V, 256) * 2)
+    rows = up(N, 256)
+    return (_align(nchunks * 3 * 32) + _align(16 * rows) + _align(4 * rows)
+            + _align(H * up(N, 64) * 2) + _align(C * up(V, 256) * 2))
 
 
 def test_workspace_sizes(lib):
