@@ -510,15 +510,18 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
 // which fills the register file and serialises the epilogue. acc_read moves
 // one accumulator register where its value is used. The hardware does not
 // interlock an accumulator read on an MFMA still writing it, and the compiler
-// does not see into the asm, so acc_read_fence (24 wait states, more than the
-// write-to-read distance of even a 16-pass MFMA) must separate the main loop
-// from the first acc_read.
-__device__ __forceinline__ void acc_read_fence() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+// does not see into the asm, so every acc_read takes the token of an
+// acc_read_fence (24 wait states, more than the write-to-read distance of
+// even a 16-pass MFMA) issued after the main loop: no read is scheduled
+// above it.
+__device__ __forceinline__ int acc_read_fence() {
+  int tok;
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_mov_b32 %0, 0" : "=s"(tok) : : "memory");
+  return tok;
 }
-__device__ __forceinline__ float acc_read(float x) {
+__device__ __forceinline__ float acc_read(float x, int tok) {
   float y;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
+  asm("v_accvgpr_read_b32 %0, %1 ; after fence %2" : "=v"(y) : "a"(x), "s"(tok));
   return y;
 }
 

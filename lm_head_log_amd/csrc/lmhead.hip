@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     const bool full = vbase + 128 <= P.V;
     const int vlim = P.V - vbase - acc_row_lane(lane);  // rows acc_row_fixed < vlim are valid
     __syncthreads();  // every wave is done reading the ring
-    acc_read_fence();
+    const int fence = acc_read_fence();
     // Per token (column j of this lane): m = max y, s = sum 2^(y - m) and
     // b = sum 2^(y - m) (y - m) over this lane's 64 vocabulary rows, merged
     // with the other half of the wave (the other 64 rows) and staged in LDS
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             v[i * 16 + r] =
-                (!kMasked || acc_row_fixed(i, r) < vl) ? acc_read(acc[i][j][r]) : -1e30f;
+                (!kMasked || acc_row_fixed(i, r) < vl) ? acc_read(acc[i][j][r], fence) : -1e30f;
         float mx = v[0];
 #pragma unroll
         for (int k = 1; k < 64; ++k) mx = fmaxf(mx, v[k]);
@@ -615,26 +615,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     const int wm = wave >> 1, wn = wave & 1;
 
     const int vbase = tm * kBM + wm * 128;
-    acc_read_fence();
+    const int fence = acc_read_fence();
     // Tokens past the kept rows have zero coefficients and a zero logit, so
     // their dz is exactly 0. Vocabulary rows at or past V are not masked: those
     // columns of dZ hold finite values that no consumer uses (dX = dZ W reads
     // W rows at or past V as zero; dW^T never stores columns at or past V).
+    //
+    // dZ leaves through LDS, one column block j (64 tokens x 256 vocabulary
+    // entries, 32 KiB) at a time: a lane's registers hold 4 consecutive
+    // entries of 32 different token rows, so direct stores would write 16-byte
+    // pieces of 32 rows per instruction; staged, each store instruction writes
+    // two whole 512-byte row segments. Staging layout: token t (0..63) at
+    // t * 512 bytes, its 16-byte chunk q (8 entries) at chunk q ^ (t & 31), so
+    // both the register-order writes and the row-order reads are free of bank
+    // conflicts.
+    __syncthreads();  // every wave is done reading the ring
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = tn * kBN + wn * 128 + j * 32 + (lane & 31);  // chunk row
-      const float4 k = rcv[j];  // {LSE log2 e, ca - cb LSE, cb, g_lp}
+      char* stage = ring.a[j % 3];  // the barrier of block j - 2 freed it
+      const float4 k = rcv[j];      // {LSE log2 e, ca - cb LSE, cb, g_lp}
       const int local = tgt[j] - vbase;
       const int w = local & 31;
       const bool hit = local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
       const int want = (local >> 5) * 16 + ((w >> 3) << 2) + (w & 3);
-      uint16_t* zrow = P.dZ + (int64_t)c * P.ldz;
+      const int t = wn * 32 + (lane & 31);  // this lane's token in the block
+      char* trow = stage + t * 512 + (lane >> 5) * 8;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float d[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float z = acc_read(acc[i][j][r]);
+          const float z = acc_read(acc[i][j][r], fence);
           const float p = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -k.x));
           d[r] = p * fmaf(k.z, z, k.y);
         }
@@ -644,18 +655,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           for (int r = 0; r < 16; ++r)
             if ((want & 15) == r) d[r] += k.w;
         }
-        // dZ[c][v]: four consecutive v per register group (8 bytes)
+        // register group g: entries wm * 128 + i * 32 + 8 g + 4 (lane >> 5) + 0..3
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int v0 = vbase + i * 32 + 8 * g + 4 * (lane >> 5);
+          const int q = wm * 16 + i * 4 + g;
           const bf16x2_t lo = {(__bf16)d[4 * g + 0], (__bf16)d[4 * g + 1]};
           const bf16x2_t hi = {(__bf16)d[4 * g + 2], (__bf16)d[4 * g + 3]};
-          const uint32_t plo = __builtin_bit_cast(uint32_t, lo);
-          const uint32_t phi = __builtin_bit_cast(uint32_t, hi);
-          *reinterpret_cast<uint2*>(zrow + v0) = make_uint2(plo, phi);
+          *reinterpret_cast<uint2*>(trow + ((q ^ (t & 31)) << 4)) =
+              make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
         }
         // one register block at a time (bounds the live copies)
         __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      // wave w stores tokens 16 w .. 16 w + 15, two rows per instruction
+      const int q = lane & 31;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int tr = wave * 16 + 2 * u + (lane >> 5);
+        const uint4 x = *reinterpret_cast<const uint4*>(stage + tr * 512 + ((q ^ (tr & 31)) << 4));
+        const int c = tn * kBN + (tr >> 5) * 128 + j * 32 + (tr & 31);  // chunk row
+        *reinterpret_cast<uint4*>(P.dZ + (int64_t)c * P.ldz + tm * kBM + q * 8) = x;
       }
     }
   }
@@ -779,7 +799,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     // four consecutive h: one 16-byte store into dW[v][h .. h + 3]
     const int hrow = tm * kBM + wm * 128 + acc_row_lane(lane);
     const int hlim = P.H - hrow;
-    acc_read_fence();
+    const int fence = acc_read_fence();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int v = tn * kBN + wn * 128 + j * 32 + (lane & 31);
@@ -794,10 +814,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
           float4 x;
           if (P.accumulate) {
             const float4 o = *reinterpret_cast<const float4*>(wrow + h);
-            x.x = acc_read(acc[i][j][4 * g]) + o.x;
-            x.y = acc_read(acc[i][j][4 * g + 1]) + o.y;
-            x.z = acc_read(acc[i][j][4 * g + 2]) + o.z;
-            x.w = acc_read(acc[i][j][4 * g + 3]) + o.w;
+            x.x = acc_read(acc[i][j][4 * g], fence) + o.x;
+            x.y = acc_read(acc[i][j][4 * g + 1], fence) + o.y;
+            x.z = acc_read(acc[i][j][4 * g + 2], fence) + o.z;
+            x.w = acc_read(acc[i][j][4 * g + 3], fence) + o.w;
           } else {
             x = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                             acc[i][j][4 * g + 3]);
