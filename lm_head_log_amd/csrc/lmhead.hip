@@ -621,25 +621,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     // columns of dZ hold finite values that no consumer uses (dX = dZ W reads
     // W rows at or past V as zero; dW^T never stores columns at or past V).
     //
-    // dZ leaves through LDS, one column block j (64 tokens x 256 vocabulary
-    // entries, 32 KiB) at a time: a lane's registers hold 4 consecutive
-    // entries of 32 different token rows, so direct stores would write 16-byte
-    // pieces of 32 rows per instruction; staged, each store instruction writes
-    // two whole 512-byte row segments. Staging layout: token t (0..63) at
-    // t * 512 bytes, its 16-byte chunk q (8 entries) at chunk q ^ (t & 31), so
-    // both the register-order writes and the row-order reads are free of bank
-    // conflicts.
+    // dZ leaves through LDS: a lane's registers hold 4 consecutive entries of
+    // 32 different token rows, so direct stores would write 8-byte pieces of
+    // 32 rows per instruction. Each wave stages its 32 tokens x 128 entries
+    // of one column block j (8 KiB, a private quarter of ring slot 0) and
+    // stores them back in row order, four 256-byte row segments per
+    // instruction. Staging layout: token t (0..31) at t * 256 bytes, its
+    // 16-byte chunk q (8 entries) at chunk q ^ (t & 15), so both the
+    // register-order writes and the row-order reads are free of bank
+    // conflicts. A wave's LDS accesses are performed in order, so the region
+    // is reused for every j without a barrier.
     __syncthreads();  // every wave is done reading the ring
+    char* stage = ring.a[0] + wave * 8192;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      char* stage = ring.a[j % 3];  // the barrier of block j - 2 freed it
-      const float4 k = rcv[j];      // {LSE log2 e, ca - cb LSE, cb, g_lp}
+      const float4 k = rcv[j];  // {LSE log2 e, ca - cb LSE, cb, g_lp}
       const int local = tgt[j] - vbase;
       const int w = local & 31;
       const bool hit = local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
       const int want = (local >> 5) * 16 + ((w >> 3) << 2) + (w & 3);
-      const int t = wn * 32 + (lane & 31);  // this lane's token in the block
-      char* trow = stage + t * 512 + (lane >> 5) * 8;
+      const int t = lane & 31;  // this lane's token in the wave's block
+      char* trow = stage + t * 256 + (lane >> 5) * 8;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float d[16];
@@ -655,27 +657,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
           for (int r = 0; r < 16; ++r)
             if ((want & 15) == r) d[r] += k.w;
         }
-        // register group g: entries wm * 128 + i * 32 + 8 g + 4 (lane >> 5) + 0..3
+        // register group g: entries i * 32 + 8 g + 4 (lane >> 5) + 0..3 of the wave's 128
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int q = wm * 16 + i * 4 + g;
+          const int q = i * 4 + g;
           const bf16x2_t lo = {(__bf16)d[4 * g + 0], (__bf16)d[4 * g + 1]};
           const bf16x2_t hi = {(__bf16)d[4 * g + 2], (__bf16)d[4 * g + 3]};
-          *reinterpret_cast<uint2*>(trow + ((q ^ (t & 31)) << 4)) =
+          *reinterpret_cast<uint2*>(trow + ((q ^ (t & 15)) << 4)) =
               make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
         }
         // one register block at a time (bounds the live copies)
         __builtin_amdgcn_sched_barrier(0);
       }
-      __syncthreads();
-      // wave w stores tokens 16 w .. 16 w + 15, two rows per instruction
-      const int q = lane & 31;
+      // rows 4 u .. 4 u + 3 of the block per instruction, 16 lanes a row
+      const int q = lane & 15;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int tr = wave * 16 + 2 * u + (lane >> 5);
-        const uint4 x = *reinterpret_cast<const uint4*>(stage + tr * 512 + ((q ^ (tr & 31)) << 4));
-        const int c = tn * kBN + (tr >> 5) * 128 + j * 32 + (tr & 31);  // chunk row
-        *reinterpret_cast<uint4*>(P.dZ + (int64_t)c * P.ldz + tm * kBM + q * 8) = x;
+        const int tr = 4 * u + (lane >> 4);
+        const uint4 x = *reinterpret_cast<const uint4*>(stage + tr * 256 + ((q ^ (tr & 15)) << 4));
+        const int c = tn * kBN + wn * 128 + j * 32 + tr;  // chunk row
+        *reinterpret_cast<uint4*>(P.dZ + (int64_t)c * P.ldz + vbase + q * 8) = x;
       }
     }
   }
@@ -795,35 +796,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     const int lane = lane_fresh(), wave = wave_fresh();
     const int wm = wave >> 1, wn = wave & 1;
 
-    // lane: vocabulary row v (column of the tile) and, per register group,
-    // four consecutive h: one 16-byte store into dW[v][h .. h + 3]
-    const int hrow = tm * kBM + wm * 128 + acc_row_lane(lane);
-    const int hlim = P.H - hrow;
+    // dW leaves through LDS the way dZ does in k_dz_tiles: each wave stages
+    // its 32 vocabulary rows x 128 h of column block j (16 KiB, a private
+    // half of ring slot 0 or 1; row t at t * 512 bytes, 16-byte chunk q (4 h)
+    // at chunk q ^ t) and stores two 512-byte row segments per instruction.
     const int fence = acc_read_fence();
+    __syncthreads();  // every wave is done reading the ring
+    char* stage = (wave < 2 ? ra0 : ra1) + (wave & 1) * 16384;
+    const int h0 = tm * kBM + wm * 128;  // first h of the wave's rows
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int v = tn * kBN + wn * 128 + j * 32 + (lane & 31);
-      if (v >= P.V) continue;
-      float* wrow = P.dW + (int64_t)v * P.H + hrow;
+      const int t = lane & 31;  // this lane's vocabulary row in the wave's block
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int h = acc_row_fixed(i, 4 * g);
-          if (h >= hlim) continue;  // H is a multiple of 4: the group is whole
-          float4 x;
-          if (P.accumulate) {
-            const float4 o = *reinterpret_cast<const float4*>(wrow + h);
-            x.x = acc_read(acc[i][j][4 * g], fence) + o.x;
-            x.y = acc_read(acc[i][j][4 * g + 1], fence) + o.y;
-            x.z = acc_read(acc[i][j][4 * g + 2], fence) + o.z;
-            x.w = acc_read(acc[i][j][4 * g + 3], fence) + o.w;
-          } else {
-            x = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                            acc[i][j][4 * g + 3]);
-          }
-          *reinterpret_cast<float4*>(wrow + h) = x;
+          // register group g: h = i * 32 + 8 g + 4 (lane >> 5) + 0..3 of the wave's 128
+          const int q = i * 8 + 2 * g + (lane >> 5);
+          const float4 x = make_float4(
+              acc_read(acc[i][j][4 * g], fence), acc_read(acc[i][j][4 * g + 1], fence),
+              acc_read(acc[i][j][4 * g + 2], fence), acc_read(acc[i][j][4 * g + 3], fence));
+          *reinterpret_cast<float4*>(stage + t * 512 + ((q ^ t) << 4)) = x;
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // rows 2 u, 2 u + 1 of the block per instruction, 32 lanes a row
+      const int q = lane & 31;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int tr = 2 * u + (lane >> 5);
+        const int v = tn * kBN + wn * 128 + j * 32 + tr;
+        const int h = h0 + q * 4;
+        if (v < P.V && h < P.H) {  // H is a multiple of 4: a chunk is whole
+          float4 x = *reinterpret_cast<const float4*>(stage + tr * 512 + ((q ^ tr) << 4));
+          float* dst = P.dW + (int64_t)v * P.H + h;
+          if (P.accumulate) {
+            const float4 o = *reinterpret_cast<const float4*>(dst);
+            x.x += o.x;
+            x.y += o.y;
+            x.z += o.z;
+            x.w += o.w;
+          }
+          *reinterpret_cast<float4*>(dst) = x;
+        }
+      }
     }
   }
 }
