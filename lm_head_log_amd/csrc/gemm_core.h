@@ -254,7 +254,7 @@ struct BSrc {
 // Tile scheduling: persistent workgroups, XCD-aware grouped order.
 // Workgroups are dispatched round-robin over the 8 XCDs (chiplets), 32 per
 // XCD at full occupancy. Each round of `grid` logical tiles is dealt to the
-// XCDs in blocks of grid / 8 consecutive tiles (queue_tile below); logical
+// XCDs in blocks of grid / 8 consecutive tiles (TileQueue below); logical
 // tiles run in groups of GM m-tiles by all n-tiles (m fastest inside a
 // group), so the 32 concurrent tiles of an XCD form a GM x (32 / GM) block
 // sharing A and B panels in that XCD's L2.
@@ -297,43 +297,63 @@ __device__ __forceinline__ void tile_coords(int t, int mt, int nt, int& tm, int&
 // assignment the slowest one sets the kernel time; stealing only pays when a
 // tile is a small part of a workgroup's work, so the host enables it for
 // launches with many tiles per workgroup.
-struct TileQueue {
-  int* ctr;    // [kXcds] counters, zero before the launch
-  int ntiles;  // logical tiles of this launch
-  int steal;
-};
-
 __device__ __forceinline__ int xcd_id() {
   // s_getreg_b32 hwreg(HW_REG_XCC_ID, 0, 4): the XCD this wave runs on
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kXcds - 1);
 }
 
-// The next logical tile for the calling workgroup, or -1 when none is left.
-// One thread takes it with a vector atomic and broadcasts it through the
-// first word of `bcast` (LDS that no load in flight writes; see the kernels);
-// contains a workgroup barrier.
-__device__ __forceinline__ int queue_tile(const TileQueue& q, char* bcast) {
-  volatile int* slot = reinterpret_cast<volatile int*>(bcast);
-  if (threadIdx.x == 0) {
+struct TileQueue {
+  int* ctr;    // [kXcds] counters, zero before the launch
+  int ntiles;  // logical tiles of this launch
+  int steal;
+  int ahead;   // thread 0: counter value taken by claim_ahead, or kNone
+  static constexpr int kNone = -1;
+
+  __device__ TileQueue(int* c, int n, int st) : ctr(c), ntiles(n), steal(st), ahead(kNone) {}
+
+  // Thread 0: takes the next position of XCD y's counter. An increment, not
+  // an add: the compiler rewrites a lone lane's add into a wave-wide form
+  // that waits for the result on the spot.
+  __device__ __forceinline__ int take(int y) const {
+    return (int)atomicInc(reinterpret_cast<unsigned*>(&ctr[y]), 0xffffffffu);
+  }
+  // The tile at position k of XCD y's queue, or -1 past its end.
+  __device__ __forceinline__ int tile_at(int y, int k) const {
     const int grid = gridDim.x;
     const int per = grid / kXcds;
-    const int full = q.ntiles / grid, rem = q.ntiles - full * grid;
-    const int x = xcd_id();
-    int t = -1;
-    for (int d = 0; d < (q.steal ? kXcds : 1); ++d) {
-      const int y = (x + d) & (kXcds - 1);
-      const int count = full * per + min(per, max(0, rem - per * y));
-      const int k = atomicAdd(&q.ctr[y], 1);
-      if (k < count) {
-        t = (k / per) * grid + y * per + k % per;
-        break;
-      }
-    }
-    *slot = t;
+    const int full = ntiles / grid, rem = ntiles - full * grid;
+    const int count = full * per + min(per, max(0, rem - per * y));
+    return k < count ? (k / per) * grid + y * per + k % per : -1;
   }
-  __syncthreads();
-  return *slot;
-}
+
+  // Called by every thread once a tile's main loop is done: thread 0 takes
+  // the next position of its own XCD's queue now, so that the atomic's
+  // latency is hidden under the epilogue.
+  __device__ __forceinline__ void claim_ahead() {
+    if (threadIdx.x == 0) ahead = take(xcd_id());
+  }
+
+  // The next logical tile for the calling workgroup, or -1 when none is left.
+  // Thread 0 takes it (the position taken ahead, else the next one of its
+  // own XCD's queue, then the other queues when stealing) and broadcasts it
+  // through the first word of `bcast` (LDS that no load in flight writes;
+  // see the kernels); contains a workgroup barrier.
+  __device__ __forceinline__ int next(char* bcast) {
+    volatile int* slot = reinterpret_cast<volatile int*>(bcast);
+    if (threadIdx.x == 0) {
+      const int x = xcd_id();
+      int t = tile_at(x, ahead != kNone ? ahead : take(x));
+      ahead = kNone;
+      for (int d = 1; t < 0 && steal && d < kXcds; ++d) {
+        const int y = (x + d) & (kXcds - 1);
+        t = tile_at(y, take(y));
+      }
+      *slot = t;
+    }
+    __syncthreads();
+    return *slot;
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Main loop.

@@ -329,11 +329,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
   const int tid = threadIdx.x;
   const int nk = P.H / kBK;
 
-  const TileQueue q = {P.queue, ntiles, P.steal};
+  TileQueue q(P.queue, ntiles, P.steal);
   for (;;) {
-    // B slot 3 is free here (see queue_tile): this wave's loads into it are
-    // done, and the next tile's loads write it only after its first barrier
-    const int t = queue_tile(q, rb3);
+    // B slot 3 is free here: this wave's loads into it are done, and the
+    // next tile's loads write it only after its first barrier
+    const int t = q.next(rb3);
     if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_FWD>(t, mt, nt, tm, tn);
@@ -353,6 +353,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     B.init(P.XcT + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
     mainloop<SHIFT>(A, B, nk, ring, acc);
+    q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
     const int lane = lane_fresh(), wave = wave_fresh();
@@ -581,11 +582,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
   const int tid = threadIdx.x;
   const int nk = P.H / kBK;
 
-  const TileQueue q = {P.queue, ntiles, P.steal};
+  TileQueue q(P.queue, ntiles, P.steal);
   for (;;) {
-    // B slot 3 is free here (see queue_tile): this wave's loads into it are
-    // done, and the next tile's loads write it only after its first barrier
-    const int t = queue_tile(q, rb3);
+    // B slot 3 is free here: this wave's loads into it are done, and the
+    // next tile's loads write it only after its first barrier
+    const int t = q.next(rb3);
     if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_DZ>(t, mt, nt, tm, tn);
@@ -609,6 +610,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     B.init(P.XcT + P.c0 + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
     mainloop<SHIFT>(A, B, nk, ring, acc);
+    q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
     const int lane = lane_fresh(), wave = wave_fresh();
@@ -709,11 +711,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   const int nk = (P.V + kBK - 1) / kBK;  // W reads zero past V
   const int32_t* kidx = P.sv.kept_idx + P.c0;
 
-  const TileQueue q = {P.queue, ntiles, P.steal};
+  TileQueue q(P.queue, ntiles, P.steal);
   for (;;) {
-    // B slot 3 is free here (see queue_tile): this wave's loads into it are
-    // done, and the next tile's loads write it only after its first barrier
-    const int t = queue_tile(q, rb3);
+    // B slot 3 is free here: this wave's loads into it are done, and the
+    // next tile's loads write it only after its first barrier
+    const int t = q.next(rb3);
     if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_DX>(t, mt, nt, tm, tn);
@@ -724,6 +726,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     B.init(P.W + (int64_t)tn * kBN, P.H, P.V, P.H - tn * kBN);
     f32x16_t acc[4][4];
     mainloop(A, B, nk, ring, acc);
+    q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
     const int lane = lane_fresh(), wave = wave_fresh();
@@ -776,11 +779,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
   const int tid = threadIdx.x;
   const int nk = (rows + kBK - 1) / kBK;  // dZ rows past `rows` read as zero
 
-  const TileQueue q = {P.queue, ntiles, P.steal};
+  TileQueue q(P.queue, ntiles, P.steal);
   for (;;) {
-    // B slot 3 is free here (see queue_tile): this wave's loads into it are
-    // done, and the next tile's loads write it only after its first barrier
-    const int t = queue_tile(q, rb3);
+    // B slot 3 is free here: this wave's loads into it are done, and the
+    // next tile's loads write it only after its first barrier
+    const int t = q.next(rb3);
     if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_DW>(t, mt, nt, tm, tn);
@@ -791,6 +794,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     B.init(P.dZ + (int64_t)tn * kBN, P.ldz, rows, kBN);  // ldz covers every v of the tile
     f32x16_t acc[4][4];
     mainloop(A, B, nk, ring, acc);
+    q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
     const int lane = lane_fresh(), wave = wave_fresh();
