@@ -149,6 +149,76 @@ int lmhead_bwd(const void* hidden, const void* weight, const int32_t* targets,
                int64_t token_chunk, void* workspace, size_t workspace_bytes,
                void* stream);
 
+/* Vocabulary-shard forward. The weight rows of a vocabulary of V_total
+ * entries are split over several calls (one per rank under tensor
+ * parallelism); this call reads the shard of rows [vocab_start, vocab_start +
+ * V_shard) and writes, per row, its statistics over the shard. In SkyRL PR
+ * #2374 each rank reduces over its vocabulary shard and the ranks combine the
+ * results with collectives over the tensor-parallel group (gemini-code-assist
+ * review); here the per-row combine is lmhead_merge_partials, so one
+ * all-gather of these 16-byte records is the only exchange the forward needs.
+ *
+ *  hidden, targets, keep_mask, N, H: as for lmhead_fwd; targets are indices
+ *             into the whole vocabulary [0, V_total)
+ *  weight_shard bf16 [V_shard, H] row-major: rows vocab_start .. of the weight
+ *  partial    fp32 [N, 4] out: {m, s, b, z_t} per row, natural-log units,
+ *             m = max z, s = sum e^(z - m), b = sum e^(z - m) (z - m) over the
+ *             shard's logits z; z_t = the target logit if the target lies in
+ *             the shard, else NaN. Skipped rows: {-inf, 0, 0, NaN}.
+ *  saved      >= lmhead_saved_bytes(N) bytes, out: compaction state; every
+ *             shard's call fills an identical copy, and lmhead_merge_partials
+ *             completes it (LSE, entropy) for lmhead_bwd_partial
+ *  workspace  >= lmhead_fwd_workspace_bytes(N, H, V_shard) bytes
+ *  Requires 0 <= vocab_start, vocab_start + V_shard <= V_total <= 2^22. A
+ *  kept target outside [0, V_total) is reported by lmhead_check_status.
+ */
+int lmhead_fwd_partial(const void* hidden, const void* weight_shard, const int32_t* targets,
+                       const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V_shard,
+                       int64_t vocab_start, int64_t V_total, float* partial,
+                       void* saved, size_t saved_bytes,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Combines the records of P vocabulary shards that together cover the
+ * vocabulary (disjoint ranges, any order of ranges, combined in the order
+ * given) into the full op's outputs: LSE = m + ln s and entropy = ln s - b / s
+ * of the merged statistics, log-prob = z_t - LSE with z_t from the one shard
+ * that holds the target (NaN if none does).
+ *
+ *  partials   fp32 [P, N, 4]: the P shards' records, each as lmhead_fwd_partial
+ *             wrote it
+ *  logp       fp32 [N] out (+0.0 at skipped rows)
+ *  entropy    fp32 [N] out; must be NULL iff !return_entropy (N > 0)
+ *  entropy_requires_grad  requires return_entropy; recorded in `saved`
+ *  saved      a buffer lmhead_fwd_partial filled for these rows; its LSE and
+ *             entropy are written here
+ */
+int lmhead_merge_partials(const float* partials, int64_t P, int64_t N,
+                          int return_entropy, int entropy_requires_grad,
+                          float* logp, float* entropy,
+                          void* saved, size_t saved_bytes, void* stream);
+
+/* Vocabulary-shard backward: lmhead_bwd restricted to the shard's logits,
+ * with the LSE and entropy of the whole vocabulary from `saved` (after
+ * lmhead_merge_partials). grad_hidden is this shard's share dZ_shard W_shard of
+ * dX: the caller sums it over the shards (one all-reduce), as SkyRL PR #2374
+ * leaves the hidden-gradient reduction to the caller (cursor and greptile
+ * reviews); grad_weight_shard is exactly the shard's rows of dW.
+ *
+ *  hidden, targets, N, H, entropy_requires_grad, grad_logp, grad_entropy,
+ *             token_chunk: as for lmhead_bwd
+ *  weight_shard, V_shard, vocab_start: as passed to lmhead_fwd_partial
+ *  grad_hidden fp32 [N, H] out, fully overwritten (+0.0 rows where skipped)
+ *  grad_weight_shard fp32 [V_shard, H] out, fully overwritten
+ *  workspace  >= lmhead_bwd_workspace_bytes(N, H, V_shard, token_chunk) bytes
+ */
+int lmhead_bwd_partial(const void* hidden, const void* weight_shard, const int32_t* targets,
+                       int64_t N, int64_t H, int64_t V_shard, int64_t vocab_start,
+                       int entropy_requires_grad, const void* saved, size_t saved_bytes,
+                       const float* grad_logp, const float* grad_entropy,
+                       float* grad_hidden, float* grad_weight_shard,
+                       int64_t token_chunk, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* Syncs `stream`, then reads the number of kept rows from `saved` into
  * *n_kept_host (the token fraction the trainer logs, prime-rl PR #3326,
  * Overview). */
@@ -168,8 +238,8 @@ int lmhead_version(void);
 /* Per-kernel timing for benchmarks (not needed to use the op).
  * Kernel kinds, in order: compact, gather_cols, fwd_tiles, merge,
  * zero_skipped, zero_rows, dz_tiles, dx_tiles, dw_tiles, zero_queues,
- * bwd_rows. */
-#define LMHEAD_NUM_KERNELS 11
+ * bwd_rows, merge_shards. */
+#define LMHEAD_NUM_KERNELS 12
 
 /* Static name of kernel kind `kind` (NULL if out of range). */
 const char* lmhead_kernel_name(int kind);

@@ -27,6 +27,7 @@ __all__ = [
     "lmhead_fwd", "lmhead_bwd", "lmhead_read_n_kept", "lmhead_check_status",
     "lmhead_status_string", "lmhead_version", "fused_logprobs", "LMHeadError",
     "DEFAULT_TOKEN_CHUNK", "lmhead_kernel_name", "lmhead_profile_begin", "lmhead_profile_end",
+    "lmhead_fwd_partial", "lmhead_merge_partials", "lmhead_bwd_partial",
 ]
 
 DEFAULT_TOKEN_CHUNK = 0  # library default: largest chunk whose dZ fits 8 GiB
@@ -158,6 +159,104 @@ def lmhead_bwd(hidden, weight, targets, saved, grad_logp, grad_entropy=None,
                       _ptr(grad_weight), int(token_chunk), _ptr(workspace), workspace.numel(),
                       _stream(stream, dev))
     check("lmhead_bwd", st)
+    return grad_hidden, grad_weight
+
+
+def lmhead_fwd_partial(hidden, weight_shard, targets, vocab_start, V_total, keep_mask=None, *,
+                       partial=None, saved=None, workspace=None, stream=None):
+    """Vocabulary-shard forward: weight_shard bf16 [V_shard, H] holds rows
+    vocab_start .. vocab_start + V_shard of a V_total-row weight. Returns
+    (partial fp32 [N, 4] = {m, s, b, z_t} per row, saved uint8 tensor)."""
+    _need(hidden, "hidden", torch.bfloat16)
+    if hidden.dim() != 2:
+        raise ValueError("hidden must be [N, H]")
+    N, H = hidden.shape
+    dev = hidden.device
+    _need(weight_shard, "weight_shard", torch.bfloat16, device=dev)
+    if weight_shard.dim() != 2 or weight_shard.shape[1] != H:
+        raise ValueError("weight_shard must be [V_shard, H]")
+    Vs = weight_shard.shape[0]
+    _need(targets, "targets", torch.int32, (N,), dev)
+    if keep_mask is not None:
+        if keep_mask.dtype == torch.bool:
+            keep_mask = keep_mask.view(torch.uint8)
+        _need(keep_mask, "keep_mask", torch.uint8, (N,), dev)
+    if partial is None:
+        partial = torch.empty(N, 4, dtype=torch.float32, device=dev)
+    _need(partial, "partial", torch.float32, (N, 4), dev)
+    L = _L()
+    if saved is None:
+        saved = torch.empty(int(L.lmhead_saved_bytes(N)), dtype=torch.uint8, device=dev)
+    wb = int(L.lmhead_fwd_workspace_bytes(N, H, Vs))
+    if workspace is None:
+        workspace = torch.empty(max(wb, 1), dtype=torch.uint8, device=dev)
+    st = L.lmhead_fwd_partial(_ptr(hidden), _ptr(weight_shard), _ptr(targets), _ptr(keep_mask),
+                              N, H, Vs, int(vocab_start), int(V_total), _ptr(partial),
+                              _ptr(saved), saved.numel(), _ptr(workspace), workspace.numel(),
+                              _stream(stream, dev))
+    check("lmhead_fwd_partial", st)
+    return partial, saved
+
+
+def lmhead_merge_partials(partials, saved, return_entropy=False, entropy_requires_grad=False, *,
+                          logp=None, entropy=None, stream=None):
+    """Combine the P shards' records partials fp32 [P, N, 4] into (logp fp32
+    [N], entropy fp32 [N] or None); completes `saved` for lmhead_bwd_partial."""
+    _need(partials, "partials", torch.float32)
+    if partials.dim() != 3 or partials.shape[2] != 4:
+        raise ValueError("partials must be [P, N, 4]")
+    P, N = partials.shape[0], partials.shape[1]
+    dev = partials.device
+    _need(saved, "saved", torch.uint8, device=dev)
+    if logp is None:
+        logp = torch.empty(N, dtype=torch.float32, device=dev)
+    _need(logp, "logp", torch.float32, (N,), dev)
+    if return_entropy:
+        if entropy is None:
+            entropy = torch.empty(N, dtype=torch.float32, device=dev)
+        _need(entropy, "entropy", torch.float32, (N,), dev)
+    else:
+        entropy = None
+    st = _L().lmhead_merge_partials(_ptr(partials), P, N, int(bool(return_entropy)),
+                                    int(bool(entropy_requires_grad)), _ptr(logp), _ptr(entropy),
+                                    _ptr(saved), saved.numel(), _stream(stream, dev))
+    check("lmhead_merge_partials", st)
+    return logp, entropy
+
+
+def lmhead_bwd_partial(hidden, weight_shard, targets, vocab_start, saved, grad_logp,
+                       grad_entropy=None, entropy_requires_grad=False, token_chunk=0, *,
+                       grad_hidden=None, grad_weight=None, workspace=None, stream=None):
+    """Vocabulary-shard backward. Returns (grad_hidden fp32 [N, H], this shard's
+    share of dX, and grad_weight fp32 [V_shard, H], the shard's rows of dW)."""
+    _need(hidden, "hidden", torch.bfloat16)
+    N, H = hidden.shape
+    dev = hidden.device
+    _need(weight_shard, "weight_shard", torch.bfloat16, device=dev)
+    Vs = weight_shard.shape[0]
+    _need(targets, "targets", torch.int32, (N,), dev)
+    _need(saved, "saved", torch.uint8, device=dev)
+    _need(grad_logp, "grad_logp", torch.float32, (N,), dev)
+    if entropy_requires_grad:
+        _need(grad_entropy, "grad_entropy", torch.float32, (N,), dev)
+    else:
+        grad_entropy = None
+    if grad_hidden is None:
+        grad_hidden = torch.empty(N, H, dtype=torch.float32, device=dev)
+    if grad_weight is None:
+        grad_weight = torch.empty(Vs, H, dtype=torch.float32, device=dev)
+    _need(grad_hidden, "grad_hidden", torch.float32, (N, H), dev)
+    _need(grad_weight, "grad_weight", torch.float32, (Vs, H), dev)
+    L = _L()
+    wb = int(L.lmhead_bwd_workspace_bytes(N, H, Vs, token_chunk))
+    if workspace is None:
+        workspace = torch.empty(max(wb, 1), dtype=torch.uint8, device=dev)
+    st = L.lmhead_bwd_partial(_ptr(hidden), _ptr(weight_shard), _ptr(targets), N, H, Vs,
+                              int(vocab_start), int(bool(entropy_requires_grad)), _ptr(saved),
+                              saved.numel(), _ptr(grad_logp), _ptr(grad_entropy),
+                              _ptr(grad_hidden), _ptr(grad_weight), int(token_chunk),
+                              _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    check("lmhead_bwd_partial", st)
     return grad_hidden, grad_weight
 
 

@@ -24,6 +24,12 @@ SIGNATURES = {
                            c_vp, c_vp, c_vp, c_size, c_vp, c_size, c_vp]),
     "lmhead_bwd": (c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_size,
                            c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_size, c_vp]),
+    "lmhead_fwd_partial": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                   c_vp, c_vp, c_size, c_vp, c_size, c_vp]),
+    "lmhead_merge_partials": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp,
+                                      c_size, c_vp]),
+    "lmhead_bwd_partial": (c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_int, c_vp,
+                                   c_size, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_size, c_vp]),
     "lmhead_read_n_kept": (c_int, [c_vp, ctypes.POINTER(c_i64), c_vp]),
     "lmhead_check_status": (c_int, [c_vp, c_vp]),
     "lmhead_status_string": (ctypes.c_char_p, [c_int]),
@@ -33,7 +39,7 @@ SIGNATURES = {
     "lmhead_profile_end": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
 }
 
-NUM_KERNELS = 11
+NUM_KERNELS = 12
 
 _lib = None
 

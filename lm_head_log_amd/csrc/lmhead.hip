@@ -167,7 +167,7 @@ constexpr int kCompactThreads = 1024;
 __global__ __launch_bounds__(kCompactThreads) void k_compact(
     const uint8_t* __restrict__ keep, const int32_t* __restrict__ targets, int N, int H, int V,
     int flags, int32_t* __restrict__ kept_idx, int32_t* __restrict__ pos,
-    SavedHeader* __restrict__ hdr, int32_t* __restrict__ tg, int tg_rows) {
+    SavedHeader* __restrict__ hdr, int32_t* __restrict__ tg, int tg_rows, int vocab_start) {
   __shared__ int scan[kCompactThreads];
   const int tid = threadIdx.x;
   const int seg = (N + kCompactThreads - 1) / kCompactThreads;
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(
       const int t = targets[i];
       kept_idx[o] = i;
       pos[i] = o;
-      tg[o] = t;
+      tg[o] = t - vocab_start;  // row of the weight this call reads
       ++o;
       bad |= (t < 0 || t >= V);
     } else {
@@ -455,18 +455,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
 
 // ---------------------------------------------------------------------------
 // Merge of the vocab-tile partials, in ascending tile order within each of 4
-// interleaved splits, then splits 0..3 in order. Writes the saved LSE and
-// entropy and scatters log-prob / entropy to the kept rows.
+// interleaved splits, then splits 0..3 in order. The full op writes the saved
+// LSE and entropy and scatters log-prob / entropy to the kept rows. The
+// vocabulary-shard form (kRecord) writes each kept row's statistics over the
+// shard instead, in natural-log units: {m, s, b, z_t} with m = max z,
+// s = sum e^(z - m), b = sum e^(z - m) (z - m), and z_t the target logit if
+// the target lies in the shard, else NaN.
 // ---------------------------------------------------------------------------
 constexpr int kMergeRows = 64;
 
+template <bool kRecord>
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm,
                                                const float* __restrict__ ps,
                                                const float* __restrict__ pb,
                                                const float* __restrict__ zt, int64_t ldp, int n_vt,
                                                const int32_t* __restrict__ tg, int V,
                                                SavedView sv, float* __restrict__ logp,
-                                               float* __restrict__ entropy) {
+                                               float* __restrict__ entropy,
+                                               float4* __restrict__ rec) {
   __shared__ float sh[3][4][kMergeRows];
   const int rows = sv.hdr->n_kept;
   const int r = threadIdx.x & (kMergeRows - 1);
@@ -486,17 +492,62 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm,
   __syncthreads();
   if (split == 0 && c < rows) {
     for (int k = 1; k < 4; ++k) stat_merge(m, s, b, sh[0][k][r], sh[1][k][r], sh[2][k][r]);
-    const float l2s = log2f(s);
-    const float lse = (m + l2s) * kLn2;
-    const float ent = (l2s - b / s) * kLn2;
     const int row = sv.kept_idx[c];
     const int t = tg[c];
-    const float lp = (t >= 0 && t < V) ? zt[c] - lse : __builtin_nanf("");
-    sv.lse[c] = lse;
-    sv.ent[c] = ent;
-    logp[row] = lp;
-    if (entropy) entropy[row] = ent;
+    const bool has_t = t >= 0 && t < V;
+    if constexpr (kRecord) {
+      rec[row] = make_float4(m * kLn2, s, b * kLn2, has_t ? zt[c] : __builtin_nanf(""));
+    } else {
+      const float l2s = log2f(s);
+      const float lse = (m + l2s) * kLn2;
+      const float ent = (l2s - b / s) * kLn2;
+      const float lp = has_t ? zt[c] - lse : __builtin_nanf("");
+      sv.lse[c] = lse;
+      sv.ent[c] = ent;
+      logp[row] = lp;
+      if (entropy) entropy[row] = ent;
+    }
   }
+}
+
+// Record of a skipped row in the vocabulary-shard form: the empty partial.
+__global__ void k_skipped_records(const int32_t* __restrict__ pos, int N, float4* __restrict__ rec) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < N && pos[i] < 0) rec[i] = make_float4(-INFINITY, 0.f, 0.f, __builtin_nanf(""));
+}
+
+// Combines the records of P vocabulary shards (disjoint ranges that together
+// cover the vocabulary), in shard order, into the full op's outputs: the
+// statistics merge as in stat_merge, and the target logit comes from the one
+// shard that holds the target (NaN if none does). Writes the saved LSE and
+// entropy of every kept row, log-prob / entropy of every row (+0.0 where
+// skipped), and the flags into the saved header.
+__global__ __launch_bounds__(256) void k_merge_shards(const float4* __restrict__ rec, int P,
+                                                      int64_t N, SavedView sv, int flags,
+                                                      float* __restrict__ logp,
+                                                      float* __restrict__ entropy) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) sv.hdr->flags = flags;
+  if (i >= N) return;
+  const int c = sv.pos[i];
+  if (c < 0) {
+    logp[i] = 0.f;
+    if (entropy) entropy[i] = 0.f;
+    return;
+  }
+  float m = -INFINITY, s = 0.f, b = 0.f, z = __builtin_nanf("");
+  for (int p = 0; p < P; ++p) {
+    const float4 q = rec[(int64_t)p * N + i];
+    stat_merge(m, s, b, q.x * kLog2e, q.y, q.z * kLog2e);  // to base-2 units
+    if (!(q.w != q.w) && z != z) z = q.w;
+  }
+  const float l2s = log2f(s);
+  const float lse = (m + l2s) * kLn2;
+  const float ent = (l2s - b / s) * kLn2;
+  sv.lse[c] = lse;
+  sv.ent[c] = ent;
+  logp[i] = z - lse;
+  if (entropy) entropy[i] = ent;
 }
 
 __global__ void k_zero_skipped(const int32_t* __restrict__ pos, int N, float* __restrict__ logp,
@@ -531,7 +582,7 @@ __global__ void k_zero_rows(const int32_t* __restrict__ pos, int N, int H, float
 __global__ __launch_bounds__(256) void k_bwd_rows(SavedView sv, const int32_t* __restrict__ targets,
                                                   const float* __restrict__ g_lp,
                                                   const float* __restrict__ g_h, int n_rows,
-                                                  float4* __restrict__ rc,
+                                                  int vocab_start, float4* __restrict__ rc,
                                                   int32_t* __restrict__ tg) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= n_rows) return;
@@ -545,7 +596,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(SavedView sv, const int32_t* _
     const float ent = g_h ? sv.ent[c] : 0.f;
     const float ca = -(glp + gh * ent), cb = -gh;
     r = make_float4(lse * kLog2e, ca - cb * lse, cb, glp);
-    t = targets[row];
+    t = targets[row] - vocab_start;  // row of the weight this call reads
   }
   rc[c] = r;
   tg[c] = t;
@@ -895,11 +946,12 @@ static int check_sizes(int64_t N, int64_t H, int64_t V) {
 // the launch stream around every launch while profiling is on.
 enum KernelKind {
   KK_COMPACT = 0, KK_GATHER_COLS, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS,
-  KK_DZ, KK_DX, KK_DW, KK_ZERO_QUEUES, KK_BWD_ROWS, KK_COUNT
+  KK_DZ, KK_DX, KK_DW, KK_ZERO_QUEUES, KK_BWD_ROWS, KK_MERGE_SHARDS, KK_COUNT
 };
 static const char* const kKernelNames[KK_COUNT] = {
     "compact",   "gather_cols", "fwd_tiles", "merge",    "zero_skipped",
-    "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles", "zero_queues", "bwd_rows"};
+    "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles", "zero_queues", "bwd_rows",
+    "merge_shards"};
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -980,34 +1032,23 @@ LMH_API size_t lmhead_bwd_workspace_bytes(int64_t N, int64_t H, int64_t V, int64
   return bwd_ws(N, H, V, token_chunk).total;
 }
 
-LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
-                       const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V,
-                       int return_entropy, int entropy_requires_grad, float* logp, float* entropy,
-                       void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
-                       void* stream) {
-  int st = check_sizes(N, H, V);
-  if (st != LMHEAD_OK) return st;
-  if (!saved) return LMHEAD_ERR_INVALID_ARG;
-  if (N > 0 && (!hidden || !weight || !targets || !logp)) return LMHEAD_ERR_INVALID_ARG;
-  if (!weight) return LMHEAD_ERR_INVALID_ARG;
-  // an empty output may have a NULL address, so presence is only checked for N > 0
-  if (N > 0 && (return_entropy != 0) != (entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
-  if (entropy_requires_grad && !return_entropy) return LMHEAD_ERR_INVALID_ARG;
-  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace))
-    return LMHEAD_ERR_INVALID_ARG;
-  if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
+// The forward for the whole vocabulary (rec == nullptr) or for the shard of
+// rows [vocab_start, vocab_start + V) of a vocabulary of V_total entries
+// (rec != nullptr: per-row shard statistics instead of log-prob / entropy).
+static int fwd_impl(const void* hidden, const void* weight, const int32_t* targets,
+                    const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V, int64_t vocab_start,
+                    int64_t V_total, int flags, float* logp, float* entropy, float4* rec,
+                    void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                    hipStream_t s) {
   const FwdWs L = fwd_ws(N, H, V);
   if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return LMHEAD_ERR_WORKSPACE;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
   SavedView sv = saved_view(saved, N);
-  const int flags = (return_entropy ? 1 : 0) | (entropy_requires_grad ? 2 : 0);
-
   char* w = static_cast<char*>(workspace);
   int32_t* tg = reinterpret_cast<int32_t*>(w + L.tg);
   LMH_TRY(launch(KK_COMPACT, k_compact, dim3(1), dim3(kCompactThreads), s, keep_mask, targets,
-                 (int)N, (int)H, (int)V, flags, sv.kept_idx, sv.pos, sv.hdr, tg,
-                 (int)tile_rows(N)));
+                 (int)N, (int)H, (int)V_total, flags, sv.kept_idx, sv.pos, sv.hdr, tg,
+                 (int)tile_rows(N), (int)vocab_start));
   if (N == 0) return LMHEAD_OK;
 
   const int nv = n_vtiles(V);
@@ -1040,36 +1081,98 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
                          k_fwd_tiles<0>, k_fwd_tiles<2>, k_fwd_tiles<4>, k_fwd_tiles<6>,
                          k_fwd_tiles<8>, k_fwd_tiles<10>));
 
-  LMH_TRY(launch(KK_MERGE, k_merge, dim3((unsigned)((N + kMergeRows - 1) / kMergeRows)), dim3(256),
-                 s, (const float*)P.pm, (const float*)P.ps, (const float*)P.pb,
-                 (const float*)P.zt, (int64_t)N, nv, (const int32_t*)tg, (int)V, sv, logp,
-                 entropy));
-  LMH_TRY(launch(KK_ZERO_SKIPPED, k_zero_skipped, dim3((unsigned)((N + 255) / 256)), dim3(256), s,
-                 (const int32_t*)sv.pos, (int)N, logp, entropy));
+  const dim3 mgrid((unsigned)((N + kMergeRows - 1) / kMergeRows));
+  const dim3 rgrid((unsigned)((N + 255) / 256));
+  if (rec) {
+    LMH_TRY(launch(KK_MERGE, k_merge<true>, mgrid, dim3(256), s, (const float*)P.pm,
+                   (const float*)P.ps, (const float*)P.pb, (const float*)P.zt, (int64_t)N, nv,
+                   (const int32_t*)tg, (int)V, sv, (float*)nullptr, (float*)nullptr, rec));
+    LMH_TRY(launch(KK_ZERO_SKIPPED, k_skipped_records, rgrid, dim3(256), s,
+                   (const int32_t*)sv.pos, (int)N, rec));
+  } else {
+    LMH_TRY(launch(KK_MERGE, k_merge<false>, mgrid, dim3(256), s, (const float*)P.pm,
+                   (const float*)P.ps, (const float*)P.pb, (const float*)P.zt, (int64_t)N, nv,
+                   (const int32_t*)tg, (int)V, sv, logp, entropy, (float4*)nullptr));
+    LMH_TRY(launch(KK_ZERO_SKIPPED, k_zero_skipped, rgrid, dim3(256), s, (const int32_t*)sv.pos,
+                   (int)N, logp, entropy));
+  }
   return LMHEAD_OK;
 }
 
-LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* targets, int64_t N,
-                       int64_t H, int64_t V, int entropy_requires_grad, const void* saved,
-                       size_t saved_bytes, const float* grad_logp, const float* grad_entropy,
-                       float* grad_hidden, float* grad_weight, int64_t token_chunk,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
+                       const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V,
+                       int return_entropy, int entropy_requires_grad, float* logp, float* entropy,
+                       void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   int st = check_sizes(N, H, V);
   if (st != LMHEAD_OK) return st;
-  if (!saved || !weight || !grad_weight) return LMHEAD_ERR_INVALID_ARG;
-  if (N > 0 && (!hidden || !targets || !grad_logp || !grad_hidden)) return LMHEAD_ERR_INVALID_ARG;
-  if (N > 0 && (entropy_requires_grad != 0) != (grad_entropy != nullptr))
+  if (!saved) return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (!hidden || !weight || !targets || !logp)) return LMHEAD_ERR_INVALID_ARG;
+  if (!weight) return LMHEAD_ERR_INVALID_ARG;
+  // an empty output may have a NULL address, so presence is only checked for N > 0
+  if (N > 0 && (return_entropy != 0) != (entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
+  if (entropy_requires_grad && !return_entropy) return LMHEAD_ERR_INVALID_ARG;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace))
     return LMHEAD_ERR_INVALID_ARG;
-  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace) ||
-      !aligned16(grad_hidden) || !aligned16(grad_weight))
+  const int flags = (return_entropy ? 1 : 0) | (entropy_requires_grad ? 2 : 0);
+  return fwd_impl(hidden, weight, targets, keep_mask, N, H, V, 0, V, flags, logp, entropy,
+                  nullptr, saved, saved_bytes, workspace, workspace_bytes,
+                  static_cast<hipStream_t>(stream));
+}
+
+LMH_API int lmhead_fwd_partial(const void* hidden, const void* weight_shard,
+                               const int32_t* targets, const uint8_t* keep_mask, int64_t N,
+                               int64_t H, int64_t V_shard, int64_t vocab_start, int64_t V_total,
+                               float* partial, void* saved, size_t saved_bytes,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_sizes(N, H, V_shard);
+  if (st != LMHEAD_OK) return st;
+  if (vocab_start < 0 || V_total > (1 << 22) || vocab_start + V_shard > V_total)
     return LMHEAD_ERR_INVALID_ARG;
+  if (!saved || !weight_shard) return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (!hidden || !targets || !partial)) return LMHEAD_ERR_INVALID_ARG;
+  if (!aligned16(hidden) || !aligned16(weight_shard) || !aligned16(saved) ||
+      !aligned16(workspace) || !aligned16(partial))
+    return LMHEAD_ERR_INVALID_ARG;
+  return fwd_impl(hidden, weight_shard, targets, keep_mask, N, H, V_shard, vocab_start, V_total,
+                  0, nullptr, nullptr, reinterpret_cast<float4*>(partial), saved, saved_bytes,
+                  workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+LMH_API int lmhead_merge_partials(const float* partials, int64_t P, int64_t N,
+                                  int return_entropy, int entropy_requires_grad, float* logp,
+                                  float* entropy, void* saved, size_t saved_bytes,
+                                  void* stream) {
+  if (P < 1 || P > 65536 || N < 0 || N > (1 << 28)) return LMHEAD_ERR_INVALID_ARG;
+  if (!saved) return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (!partials || !logp)) return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (return_entropy != 0) != (entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
+  if (entropy_requires_grad && !return_entropy) return LMHEAD_ERR_INVALID_ARG;
+  if (!aligned16(partials) || !aligned16(saved)) return LMHEAD_ERR_INVALID_ARG;
+  if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
+  const int flags = (return_entropy ? 1 : 0) | (entropy_requires_grad ? 2 : 0);
+  SavedView sv = saved_view(saved, N);
+  const unsigned blocks = (unsigned)(N > 0 ? (N + 255) / 256 : 1);
+  return launch(KK_MERGE_SHARDS, k_merge_shards, dim3(blocks), dim3(256),
+                static_cast<hipStream_t>(stream), reinterpret_cast<const float4*>(partials),
+                (int)P, N, sv, flags, logp, entropy);
+}
+
+// The backward for the whole vocabulary (vocab_start = 0) or for the shard of
+// rows [vocab_start, vocab_start + V) (grad_weight is then the shard's rows
+// and grad_hidden this shard's share of dX).
+static int bwd_impl(const void* hidden, const void* weight, const int32_t* targets, int64_t N,
+                    int64_t H, int64_t V, int64_t vocab_start, int entropy_requires_grad,
+                    const void* saved, size_t saved_bytes, const float* grad_logp,
+                    const float* grad_entropy, float* grad_hidden, float* grad_weight,
+                    int64_t token_chunk, void* workspace, size_t workspace_bytes,
+                    hipStream_t s) {
   if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
   const BwdWs L = bwd_ws(N, H, V, token_chunk);
   if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return LMHEAD_ERR_WORKSPACE;
   const BwdGeom G = bwd_geom(N, V, token_chunk);
   if (G.C > (1 << 22)) return LMHEAD_ERR_UNSUPPORTED;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
   SavedView sv = saved_view(const_cast<void*>(saved), N);
   char* w = static_cast<char*>(workspace);
   uint16_t* XcT = reinterpret_cast<uint16_t*>(w + L.xct);
@@ -1086,15 +1189,14 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
   if (N > 0) {
     const int nrows = (int)tile_rows(N);
     LMH_TRY(launch(KK_BWD_ROWS, k_bwd_rows, dim3((unsigned)(nrows / 256)), dim3(256), s, sv,
-                   targets, grad_logp, entropy_requires_grad ? grad_entropy : nullptr, nrows, rc,
-                   tg));
+                   targets, grad_logp, entropy_requires_grad ? grad_entropy : nullptr, nrows,
+                   (int)vocab_start, rc, tg));
     LMH_TRY(launch(KK_ZERO_ROWS, k_zero_rows, dim3((unsigned)N), dim3(256), s,
                    (const int32_t*)sv.pos, (int)N, (int)H, grad_hidden));
     LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(ldc / kTp), (unsigned)(H / kTp)),
                    dim3(256), s, X, (const SavedHeader*)sv.hdr, (const int32_t*)sv.kept_idx,
                    (int)H, XcT, ldc));
   }
-
   const int nv = n_vtiles(V);
   const int64_t nchunks = N > 0 ? (N + G.C - 1) / G.C : 1;
   for (int64_t ch = 0; ch < nchunks; ++ch) {
@@ -1157,6 +1259,55 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
     LMH_TRY(launch(KK_DW, k_dw_tiles, dim3(dw_grid), dim3(kThreads), s, Wp));
   }
   return LMHEAD_OK;
+}
+
+// Argument checks shared by lmhead_bwd and lmhead_bwd_partial.
+static int bwd_check(const void* hidden, const void* weight, const int32_t* targets, int64_t N,
+                     int entropy_requires_grad, const void* saved, const float* grad_logp,
+                     const float* grad_entropy, const float* grad_hidden,
+                     const float* grad_weight, const void* workspace) {
+  if (!saved || !weight || !grad_weight) return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (!hidden || !targets || !grad_logp || !grad_hidden)) return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (entropy_requires_grad != 0) != (grad_entropy != nullptr))
+    return LMHEAD_ERR_INVALID_ARG;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace) ||
+      !aligned16(grad_hidden) || !aligned16(grad_weight))
+    return LMHEAD_ERR_INVALID_ARG;
+  return LMHEAD_OK;
+}
+
+LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* targets, int64_t N,
+                       int64_t H, int64_t V, int entropy_requires_grad, const void* saved,
+                       size_t saved_bytes, const float* grad_logp, const float* grad_entropy,
+                       float* grad_hidden, float* grad_weight, int64_t token_chunk,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_sizes(N, H, V);
+  if (st != LMHEAD_OK) return st;
+  st = bwd_check(hidden, weight, targets, N, entropy_requires_grad, saved, grad_logp,
+                 grad_entropy, grad_hidden, grad_weight, workspace);
+  if (st != LMHEAD_OK) return st;
+  return bwd_impl(hidden, weight, targets, N, H, V, 0, entropy_requires_grad, saved, saved_bytes,
+                  grad_logp, grad_entropy, grad_hidden, grad_weight, token_chunk, workspace,
+                  workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+LMH_API int lmhead_bwd_partial(const void* hidden, const void* weight_shard,
+                               const int32_t* targets, int64_t N, int64_t H, int64_t V_shard,
+                               int64_t vocab_start, int entropy_requires_grad, const void* saved,
+                               size_t saved_bytes, const float* grad_logp,
+                               const float* grad_entropy, float* grad_hidden,
+                               float* grad_weight_shard, int64_t token_chunk, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  int st = check_sizes(N, H, V_shard);
+  if (st != LMHEAD_OK) return st;
+  if (vocab_start < 0 || vocab_start + V_shard > (1 << 22)) return LMHEAD_ERR_INVALID_ARG;
+  st = bwd_check(hidden, weight_shard, targets, N, entropy_requires_grad, saved, grad_logp,
+                 grad_entropy, grad_hidden, grad_weight_shard, workspace);
+  if (st != LMHEAD_OK) return st;
+  return bwd_impl(hidden, weight_shard, targets, N, H, V_shard, vocab_start,
+                  entropy_requires_grad, saved, saved_bytes, grad_logp, grad_entropy,
+                  grad_hidden, grad_weight_shard, token_chunk, workspace, workspace_bytes,
+                  static_cast<hipStream_t>(stream));
 }
 
 LMH_API int lmhead_read_n_kept(const void* saved, int64_t* n_kept_host, void* stream) {

@@ -37,6 +37,8 @@ and a uint8 keep mask (nonzero = keep; None = keep every row).
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 
@@ -183,3 +185,117 @@ def logits_input_fwd_bwd(logits, targets, g_logp, g_entropy, entropy_requires_gr
                     None if g_entropy is None else np.asarray(g_entropy, np.float64),
                     entropy_requires_grad)
     return dict(logp=lp, entropy=h, lse=lse, dlogits=dZ)
+
+
+# --------------------------------------------------------------------------
+# Vocabulary shards (tensor parallelism over the weight rows)
+# --------------------------------------------------------------------------
+# SkyRL PR #2374 ("feat(megatron): fuse LM-head entropy for RL") splits the
+# weight rows over tensor-parallel ranks: each rank reduces over its own
+# vocabulary range and the ranks combine their results with collectives
+# (gemini-code-assist review); the hidden gradient a rank computes from its
+# shard is its local share, reduced by the caller, while the weight gradient
+# is exactly the shard's rows (cursor and greptile reviews). The functions
+# below state those per-shard quantities and their combination in float64.
+
+def shard_partials_f64(X, W_shard, targets, keep_mask, vocab_start: int) -> np.ndarray:
+    """Per-row statistics of the logits over the vocabulary range
+    [vocab_start, vocab_start + V_shard) that W_shard holds.
+
+    Returns float64 [N, 4]: m = max_v z_v, s = sum_v exp(z_v - m),
+    b = sum_v exp(z_v - m) (z_v - m), and z_t, the target's logit when the
+    target lies in the range (NaN otherwise). Skipped rows get
+    (-inf, 0, 0, NaN), the statistics of an empty set.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W_shard, dtype=np.float64)
+    t = np.asarray(targets, dtype=np.int64)
+    N = X.shape[0]
+    out = np.empty((N, 4))
+    out[:] = (-np.inf, 0.0, 0.0, np.nan)
+    idx = compact(keep_mask, N)
+    if idx.size:
+        Z = X[idx] @ W.T
+        m = Z.max(axis=1)
+        D = Z - m[:, None]
+        E = np.exp(D)
+        local = t[idx] - vocab_start
+        inside = (local >= 0) & (local < W.shape[0])
+        z = np.full(idx.size, np.nan)
+        rows = np.flatnonzero(inside)
+        z[rows] = Z[rows, local[rows]]
+        out[idx, 0] = m
+        out[idx, 1] = E.sum(axis=1)
+        out[idx, 2] = (E * D).sum(axis=1)
+        out[idx, 3] = z
+    return out
+
+
+def merge_shard_partials(parts, keep_mask, N: int):
+    """Combines the statistics of disjoint vocabulary ranges, in the order
+    given, into the whole vocabulary's: with M = max_p m_p and
+    a_p = exp(m_p - M),
+        s = sum_p a_p s_p,   b = sum_p a_p (b_p + (m_p - M) s_p),
+    so that LSE = M + ln s and entropy = ln s - b / s (both follow from
+    sum_v exp(z_v - M) = s and sum_v exp(z_v - M)(z_v - M) = b). The
+    log-probability takes z_t from the range that holds the target.
+    Returns dict(logp, entropy, lse) with zeros at skipped rows.
+    """
+    parts = np.asarray(parts, dtype=np.float64)
+    idx = compact(keep_mask, N)
+    logp = np.zeros(N)
+    ent = np.zeros(N)
+    lse = np.zeros(N)
+    for i in idx:
+        M = -np.inf
+        for p in range(parts.shape[0]):
+            M = max(M, parts[p, i, 0])
+        s = 0.0
+        b = 0.0
+        z = np.nan
+        for p in range(parts.shape[0]):
+            mp, sp, bp, zp = parts[p, i]
+            if mp == -np.inf:
+                continue
+            a = math.exp(mp - M)
+            s += a * sp
+            b += a * (bp + (mp - M) * sp)
+            if not np.isnan(zp):
+                z = zp
+        lse[i] = M + math.log(s)
+        ent[i] = math.log(s) - b / s
+        logp[i] = z - lse[i]
+    return dict(logp=logp, entropy=ent, lse=lse)
+
+
+def backward_shard_f64(X, W_shard, targets, keep_mask, vocab_start: int, lse, ent,
+                       g_logp, g_entropy, entropy_requires_grad: bool):
+    """One vocabulary shard's backward with the whole vocabulary's LSE and
+    entropy (full-length [N] arrays, as merge_shard_partials returns them):
+    dZ over the shard's columns by the same formula as logit_grad, then
+    (dX_share [N, H] = dZ W_shard on the kept rows, zero elsewhere;
+    dW_shard [V_shard, H] = dZ^T X_kept)."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W_shard, dtype=np.float64)
+    t = np.asarray(targets, dtype=np.int64)
+    N = X.shape[0]
+    idx = compact(keep_mask, N)
+    dX = np.zeros_like(X)
+    dW = np.zeros_like(W)
+    if idx.size:
+        Z = X[idx] @ W.T
+        logP = Z - np.asarray(lse, np.float64)[idx][:, None]
+        P = np.exp(logP)
+        local = t[idx] - vocab_start
+        onehot = np.zeros_like(P)
+        rows = np.flatnonzero((local >= 0) & (local < W.shape[0]))
+        onehot[rows, local[rows]] = 1.0
+        g = np.asarray(g_logp, np.float64)[idx]
+        dZ = g[:, None] * (onehot - P)
+        if entropy_requires_grad:
+            gh = np.asarray(g_entropy, np.float64)[idx]
+            h = np.asarray(ent, np.float64)[idx]
+            dZ = dZ - gh[:, None] * P * (logP + h[:, None])
+        dX[idx] = dZ @ W
+        dW = dZ.T @ X[idx]
+    return dX, dW

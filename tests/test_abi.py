@@ -205,3 +205,81 @@ def test_binding_rejects_cpu_tensors():
         m.lmhead_fwd(h, w, t)
     with pytest.raises(TypeError):
         m.lmhead_fwd(h.float(), w, t)
+
+
+def _fwdp(lib, **kw):
+    a = dict(hidden=FAKE, weight=FAKE, targets=FAKE, keep=None, N=8, H=64, Vs=100, v0=0, Vt=300,
+             partial=FAKE, saved=FAKE, saved_bytes=1 << 20, ws=FAKE, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.lmhead_fwd_partial(a["hidden"], a["weight"], a["targets"], a["keep"], a["N"],
+                                  a["H"], a["Vs"], a["v0"], a["Vt"], a["partial"], a["saved"],
+                                  a["saved_bytes"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), 1),
+    (dict(Vs=0), 1),
+    (dict(H=96), 2),
+    (dict(v0=-1), 1),
+    (dict(v0=250), 1),                # shard runs past the vocabulary
+    (dict(Vt=(1 << 22) + 1), 1),
+    (dict(partial=None), 1),
+    (dict(partial=ODD), 1),
+    (dict(weight=None), 1),
+    (dict(saved=None), 1),
+    (dict(saved_bytes=100), 3),
+    (dict(ws_bytes=10), 3),
+])
+def test_fwd_partial_host_validation(lib, kw, code):
+    assert _fwdp(lib, **kw) == code
+
+
+def _merge(lib, **kw):
+    a = dict(parts=FAKE, P=2, N=8, ret=1, erg=1, logp=FAKE, ent=FAKE, saved=FAKE,
+             saved_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.lmhead_merge_partials(a["parts"], a["P"], a["N"], a["ret"], a["erg"], a["logp"],
+                                     a["ent"], a["saved"], a["saved_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(P=0), 1),
+    (dict(N=-1), 1),
+    (dict(parts=None), 1),
+    (dict(logp=None), 1),
+    (dict(ent=None), 1),
+    (dict(ret=0), 1),
+    (dict(ret=0, ent=None), 1),
+    (dict(parts=ODD), 1),
+    (dict(saved=None), 1),
+    (dict(saved_bytes=10), 3),
+])
+def test_merge_partials_host_validation(lib, kw, code):
+    assert _merge(lib, **kw) == code
+
+
+def _bwdp(lib, **kw):
+    a = dict(hidden=FAKE, weight=FAKE, targets=FAKE, N=8, H=64, Vs=100, v0=200, erg=1, saved=FAKE,
+             saved_bytes=1 << 20, glp=FAKE, gh=FAKE, gX=FAKE, gW=FAKE, chunk=0, ws=FAKE,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.lmhead_bwd_partial(a["hidden"], a["weight"], a["targets"], a["N"], a["H"], a["Vs"],
+                                  a["v0"], a["erg"], a["saved"], a["saved_bytes"], a["glp"],
+                                  a["gh"], a["gX"], a["gW"], a["chunk"], a["ws"], a["ws_bytes"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-5), 1),
+    (dict(H=96), 2),
+    (dict(v0=-1), 1),
+    (dict(gW=None), 1),
+    (dict(gh=None), 1),
+    (dict(erg=0), 1),
+    (dict(gX=ODD), 1),
+    (dict(saved_bytes=8), 3),
+    (dict(ws_bytes=0), 3),
+])
+def test_bwd_partial_host_validation(lib, kw, code):
+    assert _bwdp(lib, **kw) == code

@@ -430,3 +430,101 @@ def test_planted_mask_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "backward_f64", bad_backward)
     with pytest.raises(AssertionError):
         test_mask_semantics_equal_dense_on_kept_rows()
+
+
+# --------------------------------------------------------------------------
+# vocabulary shards: the per-range statistics and their combination must give
+# exactly the whole-vocabulary result of the direct definition above
+# --------------------------------------------------------------------------
+
+def _shard_problem(seed=21, N=40, H=24, V=53):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((N, H))
+    W = rng.standard_normal((V, H)) * 0.7
+    t = rng.integers(0, V, N)
+    keep = (rng.random(N) < 0.7).astype(np.uint8)
+    g_lp = rng.standard_normal(N)
+    g_h = rng.standard_normal(N)
+    return X, W, t, keep, g_lp, g_h
+
+
+# uneven ranges, listed out of vocabulary order, one of a single row
+_CUTS = [(30, 53), (0, 17), (17, 18), (18, 30)]
+
+
+def test_single_shard_statistics_are_the_definition():
+    X, W, t, keep, _, _ = _shard_problem()
+    part = oracle.shard_partials_f64(X, W, t, keep, 0)
+    full = oracle.forward_f64(X, W, t, keep)
+    idx = full["kept_idx"]
+    Z = X[idx] @ W.T
+    np.testing.assert_allclose(part[idx, 0], Z.max(axis=1), rtol=0, atol=0)
+    np.testing.assert_allclose(part[idx, 0] + np.log(part[idx, 1]), full["lse"][idx], rtol=1e-13)
+    np.testing.assert_allclose(part[idx, 3], Z[np.arange(idx.size), t[idx]], rtol=0, atol=0)
+    skipped = np.flatnonzero(keep == 0)
+    assert np.all(part[skipped, 0] == -np.inf) and np.all(part[skipped, 1:3] == 0)
+    assert np.all(np.isnan(part[skipped, 3]))
+
+
+def test_shard_merge_equals_whole_vocabulary():
+    X, W, t, keep, _, _ = _shard_problem()
+    N = X.shape[0]
+    parts = np.stack([oracle.shard_partials_f64(X, W[a:b], t, keep, a) for a, b in _CUTS])
+    got = oracle.merge_shard_partials(parts, keep, N)
+    full = oracle.forward_f64(X, W, t, keep)
+    for k in ("logp", "entropy", "lse"):
+        np.testing.assert_allclose(got[k], full[k], rtol=1e-12, atol=1e-12, err_msg=k)
+    # exactly one range holds each kept target
+    idx = full["kept_idx"]
+    assert np.all((~np.isnan(parts[:, idx, 3])).sum(axis=0) == 1)
+
+
+def test_shard_merge_target_outside_every_range_is_nan():
+    X, W, t, keep, _, _ = _shard_problem()
+    N = X.shape[0]
+    parts = np.stack([oracle.shard_partials_f64(X, W[a:b], t, keep, a) for a, b in _CUTS[:2]])
+    got = oracle.merge_shard_partials(parts, keep, N)
+    idx = oracle.compact(keep, N)
+    covered = ((t[idx] >= 30) & (t[idx] < 53)) | (t[idx] < 17)
+    assert np.all(np.isnan(got["logp"][idx[~covered]]))
+    assert np.all(np.isfinite(got["logp"][idx[covered]]))
+
+
+@pytest.mark.parametrize("erg", [False, True])
+def test_shard_backward_sums_to_whole_vocabulary(erg):
+    X, W, t, keep, g_lp, g_h = _shard_problem(seed=22)
+    N = X.shape[0]
+    full = oracle.forward_f64(X, W, t, keep)
+    dX_ref, dW_ref = oracle.backward_f64(X, W, t, keep, g_lp, g_h, erg)
+    dX = np.zeros_like(dX_ref)
+    for a, b in _CUTS:
+        dXs, dWs = oracle.backward_shard_f64(X, W[a:b], t, keep, a, full["lse"], full["entropy"],
+                                             g_lp, g_h, erg)
+        dX += dXs
+        np.testing.assert_allclose(dWs, dW_ref[a:b], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dX, dX_ref, rtol=1e-11, atol=1e-12)
+
+
+def _merge_without_shift_correction(parts, keep_mask, N):
+    """A plausible mistake: b combined without the (m_p - M) s_p term."""
+    parts = np.asarray(parts, dtype=np.float64)
+    idx = oracle.compact(keep_mask, N)
+    out = dict(logp=np.zeros(N), entropy=np.zeros(N), lse=np.zeros(N))
+    for i in idx:
+        M = parts[:, i, 0].max()
+        a = np.exp(parts[:, i, 0] - M)
+        s = (a * parts[:, i, 1]).sum()
+        b = (a * parts[:, i, 2]).sum()
+        out["lse"][i] = M + math.log(s)
+        out["entropy"][i] = math.log(s) - b / s
+    return out
+
+
+def test_planted_shard_merge_mistake_is_caught():
+    X, W, t, keep, _, _ = _shard_problem()
+    N = X.shape[0]
+    parts = np.stack([oracle.shard_partials_f64(X, W[a:b], t, keep, a) for a, b in _CUTS])
+    bad = _merge_without_shift_correction(parts, keep, N)
+    full = oracle.forward_f64(X, W, t, keep)
+    idx = full["kept_idx"]
+    assert np.abs(bad["entropy"][idx] - full["entropy"][idx]).max() > 1e-3
