@@ -99,6 +99,70 @@ def cpu_baseline(w, rows_n: int):
     }
 
 
+# One tensor-parallel rank's share of the dense RL batch: P2's TP4 x CP2 layout
+# at H=4096, V=131072, 16K tokens gives each rank 8192 tokens and 32768
+# vocabulary rows.
+SHARD_ROWS, SHARD_VOCAB, SHARD_RANKS = 8192, 32768, 4
+
+
+def shard_leg(lmh, X, W, t, glp, gh, erg, stream, dev, steps):
+    """Times lmhead_fwd_partial + lmhead_merge_partials (over SHARD_RANKS
+    records, as after the all-gather) + lmhead_bwd_partial on one rank's
+    share. The collectives themselves are not run (one GPU)."""
+    import torch
+    N, H = X.shape
+    V = W.shape[0]
+    Ns, Vs = min(SHARD_ROWS, N), min(SHARD_VOCAB, V)
+    Xs, ts, Ws = X[:Ns].contiguous(), t[:Ns].contiguous(), W[:Vs].contiguous()
+    gls = glp[:Ns].contiguous()
+    ghs = gh[:Ns].contiguous() if (erg and gh is not None) else None
+    parts = torch.empty(SHARD_RANKS, Ns, 4, dtype=torch.float32, device=dev)
+    saved = torch.empty(lmh.lmhead_saved_bytes(Ns), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(max(1, lmh.lmhead_fwd_workspace_bytes(Ns, H, Vs)), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(max(1, lmh.lmhead_bwd_workspace_bytes(Ns, H, Vs, 0)), dtype=torch.uint8,
+                       device=dev)
+    lp = torch.empty(Ns, dtype=torch.float32, device=dev)
+    en = torch.empty(Ns, dtype=torch.float32, device=dev)
+    gXs = torch.empty(Ns, H, dtype=torch.float32, device=dev)
+    gWs = torch.empty(Vs, H, dtype=torch.float32, device=dev)
+
+    def one():
+        # this rank's record goes to slot 0; the other ranks' slots hold records
+        # of the same shape from the warm-up
+        lmh.lmhead_fwd_partial(Xs, Ws, ts, 0, V, None, partial=parts[0], saved=saved,
+                               workspace=ws_f, stream=stream)
+        lmh.lmhead_merge_partials(parts, saved, True, erg, logp=lp, entropy=en, stream=stream)
+        lmh.lmhead_bwd_partial(Xs, Ws, ts, 0, saved, gls, ghs, erg, 0, grad_hidden=gXs,
+                               grad_weight=gWs, workspace=ws_b, stream=stream)
+
+    lmh.lmhead_fwd_partial(Xs, Ws, ts, 0, V, None, partial=parts[0], saved=saved,
+                           workspace=ws_f, stream=stream)
+    parts[1:].copy_(parts[0].expand(SHARD_RANKS - 1, Ns, 4))
+    for _ in range(2):
+        one()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        one()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = 8.0 * Ns * H * Vs
+    return {
+        "workload": f"one tensor-parallel rank (TP4 x CP2 layout) of the dense RL batch: "
+                    f"N {Ns} H {H} V_shard {Vs} of V {V}, fwd_partial + merge of "
+                    f"{SHARD_RANKS} shard records + bwd_partial; collectives not run",
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(Ns / (ms * 1e-3), 1),
+        "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+        "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "steps": steps,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +175,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-keep-sweep", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the vocabulary-shard (one tensor-parallel rank) timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (counter calibration)")
     args = ap.parse_args()
@@ -256,6 +322,11 @@ def main():
             "steps_each": args.sweep_steps,
         }
 
+    shard = None
+    if not args.no_shard and args.config == 2 and do_bwd:
+        shard = shard_leg(lmh, X, W, t, glp, gh, erg, stream, dev, max(args.sweep_steps, 5))
+        log(f"tp shard {shard}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -303,6 +374,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "keep_sweep": sweep,
+        "tp_shard": shard,
     }
     print(json.dumps(out), flush=True)
 
