@@ -219,6 +219,45 @@ int lmhead_bwd_partial(const void* hidden, const void* weight_shard, const int32
                        int64_t token_chunk, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* Logits that already exist: log-prob and entropy from a caller-held
+ * [N, V] logit matrix, the selective_log_softmax contract of twinkle PR #283,
+ * section 1 (fp32 results for bf16 logits; the backward recomputes the
+ * softmax from the logits instead of keeping it). One pass over each row in
+ * each direction and no temporaries, so the pages' row chunking, which bounds
+ * temporaries, is not needed. A -inf logit counts as probability 0.
+ */
+#define LMHEAD_DTYPE_BF16 0
+#define LMHEAD_DTYPE_F32 1
+
+/*  logits     [N, V] row-major, dtype LMHEAD_DTYPE_BF16 (2-byte aligned) or
+ *             LMHEAD_DTYPE_F32 (4-byte aligned); any V >= 1
+ *  targets    int32 [N]; a kept target outside [0, V) gives logp = NaN
+ *  keep_mask  uint8 [N] (nonzero = keep) or NULL; skipped rows get +0.0
+ *  logp       fp32 [N] out; entropy fp32 [N] out, NULL iff !return_entropy
+ *  saved_stats fp32 [N, 2] out: {LSE, entropy} per row (0 for skipped rows),
+ *             the state lmhead_logits_bwd needs
+ */
+int lmhead_logits_fwd(const void* logits, int dtype, int64_t N, int64_t V,
+                      const int32_t* targets, const uint8_t* keep_mask,
+                      int return_entropy, float* logp, float* entropy,
+                      float* saved_stats, void* stream);
+
+/* dL/dlogits = g_lp (onehot(t) - p) - g_H p (ln p + H), p = softmax(row),
+ * the entropy term only if entropy_requires_grad; written in the logits'
+ * dtype (bf16 rounds to nearest even), +0.0 rows where skipped.
+ *
+ *  logits, dtype, N, V, targets, keep_mask: as passed to lmhead_logits_fwd
+ *  saved_stats  as lmhead_logits_fwd wrote it
+ *  grad_logp    fp32 [N]; grad_entropy fp32 [N], NULL iff !entropy_requires_grad
+ *  grad_logits  [N, V] out in `dtype`, fully overwritten; its address must
+ *               have the same offset modulo 16 bytes as `logits`
+ */
+int lmhead_logits_bwd(const void* logits, int dtype, int64_t N, int64_t V,
+                      const int32_t* targets, const uint8_t* keep_mask,
+                      const float* saved_stats, const float* grad_logp,
+                      const float* grad_entropy, int entropy_requires_grad,
+                      void* grad_logits, void* stream);
+
 /* Syncs `stream`, then reads the number of kept rows from `saved` into
  * *n_kept_host (the token fraction the trainer logs, prime-rl PR #3326,
  * Overview). */

@@ -28,7 +28,10 @@ __all__ = [
     "lmhead_status_string", "lmhead_version", "fused_logprobs", "LMHeadError",
     "DEFAULT_TOKEN_CHUNK", "lmhead_kernel_name", "lmhead_profile_begin", "lmhead_profile_end",
     "lmhead_fwd_partial", "lmhead_merge_partials", "lmhead_bwd_partial",
+    "lmhead_logits_fwd", "lmhead_logits_bwd",
 ]
+
+_LOGIT_DTYPES = {torch.bfloat16: 0, torch.float32: 1}  # LMHEAD_DTYPE_BF16 / _F32
 
 DEFAULT_TOKEN_CHUNK = 0  # library default: largest chunk whose dZ fits 8 GiB
 
@@ -258,6 +261,77 @@ def lmhead_bwd_partial(hidden, weight_shard, targets, vocab_start, saved, grad_l
                               _ptr(workspace), workspace.numel(), _stream(stream, dev))
     check("lmhead_bwd_partial", st)
     return grad_hidden, grad_weight
+
+
+def _logit_dtype(logits):
+    if not isinstance(logits, torch.Tensor):
+        raise TypeError("logits must be a torch.Tensor")
+    if logits.dtype not in _LOGIT_DTYPES:
+        raise TypeError(f"logits must be bf16 or fp32, got {logits.dtype}")
+    _need(logits, "logits", logits.dtype)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [N, V]")
+    return _LOGIT_DTYPES[logits.dtype]
+
+
+def lmhead_logits_fwd(logits, targets, keep_mask=None, return_entropy=False, *, logp=None,
+                      entropy=None, saved_stats=None, stream=None):
+    """Log-prob / entropy from materialised logits bf16 or fp32 [N, V].
+    Returns (logp fp32 [N], entropy fp32 [N] or None, saved_stats fp32 [N, 2])."""
+    dt = _logit_dtype(logits)
+    N, V = logits.shape
+    dev = logits.device
+    _need(targets, "targets", torch.int32, (N,), dev)
+    if keep_mask is not None:
+        if keep_mask.dtype == torch.bool:
+            keep_mask = keep_mask.view(torch.uint8)
+        _need(keep_mask, "keep_mask", torch.uint8, (N,), dev)
+    if logp is None:
+        logp = torch.empty(N, dtype=torch.float32, device=dev)
+    _need(logp, "logp", torch.float32, (N,), dev)
+    if return_entropy:
+        if entropy is None:
+            entropy = torch.empty(N, dtype=torch.float32, device=dev)
+        _need(entropy, "entropy", torch.float32, (N,), dev)
+    else:
+        entropy = None
+    if saved_stats is None:
+        saved_stats = torch.empty(N, 2, dtype=torch.float32, device=dev)
+    _need(saved_stats, "saved_stats", torch.float32, (N, 2), dev)
+    st = _L().lmhead_logits_fwd(_ptr(logits), dt, N, V, _ptr(targets), _ptr(keep_mask),
+                                int(bool(return_entropy)), _ptr(logp), _ptr(entropy),
+                                _ptr(saved_stats), _stream(stream, dev))
+    check("lmhead_logits_fwd", st)
+    return logp, entropy, saved_stats
+
+
+def lmhead_logits_bwd(logits, targets, saved_stats, grad_logp, grad_entropy=None,
+                      entropy_requires_grad=False, keep_mask=None, *, grad_logits=None,
+                      stream=None):
+    """dL/dlogits in the logits' dtype [N, V]."""
+    dt = _logit_dtype(logits)
+    N, V = logits.shape
+    dev = logits.device
+    _need(targets, "targets", torch.int32, (N,), dev)
+    if keep_mask is not None:
+        if keep_mask.dtype == torch.bool:
+            keep_mask = keep_mask.view(torch.uint8)
+        _need(keep_mask, "keep_mask", torch.uint8, (N,), dev)
+    _need(saved_stats, "saved_stats", torch.float32, (N, 2), dev)
+    _need(grad_logp, "grad_logp", torch.float32, (N,), dev)
+    if entropy_requires_grad:
+        _need(grad_entropy, "grad_entropy", torch.float32, (N,), dev)
+    else:
+        grad_entropy = None
+    if grad_logits is None:
+        grad_logits = torch.empty_like(logits)
+    _need(grad_logits, "grad_logits", logits.dtype, (N, V), dev)
+    st = _L().lmhead_logits_bwd(_ptr(logits), dt, N, V, _ptr(targets), _ptr(keep_mask),
+                                _ptr(saved_stats), _ptr(grad_logp), _ptr(grad_entropy),
+                                int(bool(entropy_requires_grad)), _ptr(grad_logits),
+                                _stream(stream, dev))
+    check("lmhead_logits_bwd", st)
+    return grad_logits
 
 
 def lmhead_read_n_kept(saved, stream=None) -> int:

@@ -30,6 +30,10 @@ SIGNATURES = {
                                       c_size, c_vp]),
     "lmhead_bwd_partial": (c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_int, c_vp,
                                    c_size, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_size, c_vp]),
+    "lmhead_logits_fwd": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_int, c_vp, c_vp, c_vp,
+                                  c_vp]),
+    "lmhead_logits_bwd": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_int,
+                                  c_vp, c_vp]),
     "lmhead_read_n_kept": (c_int, [c_vp, ctypes.POINTER(c_i64), c_vp]),
     "lmhead_check_status": (c_int, [c_vp, c_vp]),
     "lmhead_status_string": (ctypes.c_char_p, [c_int]),

@@ -13,7 +13,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "lmhead.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("lmhead.hip", "logits_rows.hip")]
 LIB = os.path.join(PKG, "liblmhead.so")
 ARCH = "gfx950"
 
@@ -35,7 +35,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False, asm: bool = False) -> str:
     """Compile liblmhead.so next to this file and return its path."""
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", LIB + ".tmp", SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", LIB + ".tmp", *SRCS]
     if asm:
         cmd.insert(1, "-save-temps=obj")
     if verbose:

@@ -1,0 +1,337 @@
+// logits_rows.hip - log-prob / entropy from logits that already exist in
+// memory, for MI355X (gfx950): the entry points lmhead_logits_fwd and
+// lmhead_logits_bwd declared in include/lmhead.h.
+//
+// This is the contract of twinkle PR #283, section 1 (selective_log_softmax):
+// the caller holds the [N, V] logits (bf16 or fp32); per row the op returns
+// the target's log-probability and the entropy in fp32 and, in backward,
+// recomputes the softmax from the logits instead of keeping it. The pages'
+// version walks the rows in chunks to bound its temporaries; these kernels
+// keep no temporaries at all (each row is streamed once per pass), so the
+// chunking has nothing left to bound.
+//
+// One workgroup per row. The work is a stream over the row with a few VALU
+// operations per element, so the bound is HBM bandwidth: the forward reads
+// the logits once, the backward reads them once more and writes the gradient.
+// Loads are 16 bytes per lane, consecutive lanes on consecutive 16-byte
+// chunks (each wave reads 1 KiB of a row per instruction).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/lmhead.h"
+
+#define LMH_API extern "C" __attribute__((visibility("default")))
+
+namespace lmh_rows {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// A -inf logit (a token the model rules out) counts as probability 0: logits
+// and their scaled differences are clamped to this finite value, whose
+// exponential is 0 next to any real maximum while 0 * value stays finite.
+constexpr float kFloor = -1e30f;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float load_one(const uint16_t* p) {
+  return __uint_as_float((uint32_t)(*p) << 16);
+}
+__device__ __forceinline__ float load_one(const float* p) { return *p; }
+
+// Elements per 16-byte vector.
+template <class T>
+struct Vec;
+template <>
+struct Vec<uint16_t> {
+  static constexpr int n = 8;
+  static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[8]) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const float (&x)[8]) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x2_t h = {(__bf16)x[2 * k], (__bf16)x[2 * k + 1]};  // round to nearest even
+      w[k] = __builtin_bit_cast(uint32_t, h);
+    }
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int n = 4;
+  static __device__ __forceinline__ void load(const float* p, float (&x)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x;
+    x[1] = v.y;
+    x[2] = v.z;
+    x[3] = v.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&x)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+};
+
+__device__ __forceinline__ void store_one(uint16_t* p, float x) {
+  *p = __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ void store_one(float* p, float x) { *p = x; }
+
+// Online statistics in base-2 units over a set S of logits z, y = z log2 e:
+// m = max y, s = sum 2^(y - m), b = sum 2^(y - m) (y - m).
+struct Stats {
+  float m = -INFINITY, s = 0.f, b = 0.f;
+
+  // Adds logits whose maximum is cz.
+  template <int K>
+  __device__ __forceinline__ void add(const float (&z)[K], float cz) {
+    const float cm = fmaxf(cz * kLog2e, kFloor);
+    if (cm > m) {
+      // rescale to the new maximum: b' = a (b + (m - m') s), s' = a s
+      if (m != -INFINITY) {
+        const float d = m - cm;
+        const float a = exp2f(d);
+        b = a * fmaf(d, s, b);
+        s *= a;
+      }
+      m = cm;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float d = fmaxf(fmaf(z[k], kLog2e, -m), kFloor);
+      const float e = exp2f(d);
+      s += e;
+      b = fmaf(e, d, b);
+    }
+  }
+
+  // Merges another partial (two partials combine exactly up to rounding).
+  __device__ __forceinline__ void merge(float m2, float s2, float b2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;
+    float a1 = 0.f, a2 = 0.f, t1 = 0.f, t2 = 0.f;
+    if (m != -INFINITY) {
+      const float d = m - mn;
+      a1 = exp2f(d);
+      t1 = a1 * fmaf(d, s, b);
+      a1 *= s;
+    }
+    if (m2 != -INFINITY) {
+      const float d = m2 - mn;
+      a2 = exp2f(d);
+      t2 = a2 * fmaf(d, s2, b2);
+      a2 *= s2;
+    }
+    m = mn;
+    s = a1 + a2;
+    b = t1 + t2;
+  }
+};
+
+// Elements of the row before the first 16-byte boundary.
+template <class T>
+__device__ __forceinline__ int64_t head_len(const T* row, int64_t V) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(row);
+  const int64_t h = (int64_t)(((16 - (a & 15)) & 15) / sizeof(T));
+  return h < V ? h : V;
+}
+
+template <class T>
+__global__ __launch_bounds__(kThreads) void k_logits_fwd(const T* __restrict__ logits, int64_t N,
+                                                          int64_t V,
+                                                          const int32_t* __restrict__ targets,
+                                                          const uint8_t* __restrict__ keep,
+                                                          float* __restrict__ logp,
+                                                          float* __restrict__ entropy,
+                                                          float* __restrict__ stats) {
+  __shared__ float red[3][kThreads / 64];
+  const int64_t i = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (keep && keep[i] == 0) {
+    if (tid == 0) {
+      logp[i] = 0.f;
+      if (entropy) entropy[i] = 0.f;
+      stats[2 * i] = 0.f;
+      stats[2 * i + 1] = 0.f;
+    }
+    return;
+  }
+  const T* row = logits + i * V;
+  constexpr int K = Vec<T>::n;
+  Stats st;
+  const int64_t h = head_len(row, V);
+  const int64_t nv = (V - h) / K;  // whole vectors after the head
+  // head and tail elements one at a time
+  for (int64_t v = tid; v < h; v += kThreads) {
+    const float z[1] = {load_one(row + v)};
+    st.add(z, z[0]);
+  }
+  for (int64_t v = h + nv * K + tid; v < V; v += kThreads) {
+    const float z[1] = {load_one(row + v)};
+    st.add(z, z[0]);
+  }
+  const T* body = row + h;
+  for (int64_t c = tid; c < nv; c += kThreads) {
+    float z[K];
+    Vec<T>::load(body + c * K, z);
+    float cz = z[0];
+#pragma unroll
+    for (int k = 1; k < K; ++k) cz = fmaxf(cz, z[k]);
+    st.add(z, cz);
+  }
+  // wave then workgroup reduction, in a fixed order
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    st.merge(__shfl_xor(st.m, off), __shfl_xor(st.s, off), __shfl_xor(st.b, off));
+  const int wave = tid >> 6;
+  if ((tid & 63) == 0) {
+    red[0][wave] = st.m;
+    red[1][wave] = st.s;
+    red[2][wave] = st.b;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    Stats t;
+    for (int w = 0; w < kThreads / 64; ++w) t.merge(red[0][w], red[1][w], red[2][w]);
+    const float l2s = log2f(t.s);
+    const float lse = (t.m + l2s) * kLn2;
+    const float ent = (l2s - t.b / t.s) * kLn2;
+    const int tt = targets[i];
+    const float lp = (tt >= 0 && tt < V) ? load_one(row + tt) - lse : __builtin_nanf("");
+    logp[i] = lp;
+    if (entropy) entropy[i] = ent;
+    stats[2 * i] = lse;
+    stats[2 * i + 1] = ent;
+  }
+}
+
+// dz = g_lp (onehot - p) - g_H p (ln p + H), p = e^(z - LSE), written in the
+// logits' precision (bf16 rounds to nearest even); skipped rows get +0.0.
+template <class T>
+__global__ __launch_bounds__(kThreads) void k_logits_bwd(
+    const T* __restrict__ logits, int64_t N, int64_t V, const int32_t* __restrict__ targets,
+    const uint8_t* __restrict__ keep, const float* __restrict__ stats,
+    const float* __restrict__ g_lp, const float* __restrict__ g_h, T* __restrict__ grad) {
+  const int64_t i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const T* row = logits + i * V;
+  T* out = grad + i * V;
+  constexpr int K = Vec<T>::n;
+  const int64_t h = head_len(row, V);
+  const int64_t nv = (V - h) / K;
+  if (keep && keep[i] == 0) {
+    const float zero[K] = {};
+    for (int64_t v = tid; v < h; v += kThreads) store_one(out + v, 0.f);
+    for (int64_t v = h + nv * K + tid; v < V; v += kThreads) store_one(out + v, 0.f);
+    for (int64_t c = tid; c < nv; c += kThreads) Vec<T>::store(out + h + c * K, zero);
+    return;
+  }
+  // dz = p (ca' + cb z) + g_lp [v = t], p = 2^(z log2 e - LSE log2 e),
+  // ca' = ca - cb LSE, ca = -(g_lp + g_H H), cb = -g_H
+  const float lse = stats[2 * i], ent = stats[2 * i + 1];
+  const float gl = g_lp[i];
+  const float gh = g_h ? g_h[i] : 0.f;
+  const float cb = -gh;
+  const float ca = -(gl + gh * ent) - cb * lse;
+  const float l2 = lse * kLog2e;
+  const int64_t tt = targets[i];
+  auto dz = [&](float z) {
+    const float zc = fmaxf(z, kFloor);
+    const float p = exp2f(fmaf(zc, kLog2e, -l2));
+    return p * fmaf(cb, zc, ca);
+  };
+  for (int64_t v = tid; v < h; v += kThreads)
+    store_one(out + v, dz(load_one(row + v)) + (v == tt ? gl : 0.f));
+  for (int64_t v = h + nv * K + tid; v < V; v += kThreads)
+    store_one(out + v, dz(load_one(row + v)) + (v == tt ? gl : 0.f));
+  const T* body = row + h;
+  T* obody = out + h;
+  for (int64_t c = tid; c < nv; c += kThreads) {
+    float z[K];
+    Vec<T>::load(body + c * K, z);
+    float d[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) d[k] = dz(z[k]);
+    const int64_t local = tt - (h + c * K);
+    if (local >= 0 && local < K) {
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (k == local) d[k] += gl;
+    }
+    Vec<T>::store(obody + c * K, d);
+  }
+}
+
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+static int check_rows(const void* logits, int dtype, int64_t N, int64_t V) {
+  if (N < 0 || V <= 0) return LMHEAD_ERR_INVALID_ARG;
+  if (dtype != LMHEAD_DTYPE_BF16 && dtype != LMHEAD_DTYPE_F32) return LMHEAD_ERR_UNSUPPORTED;
+  if (N > (int64_t(1) << 31) - 1 || V > (int64_t(1) << 31) - 1) return LMHEAD_ERR_UNSUPPORTED;
+  if (N > 0 && !logits) return LMHEAD_ERR_INVALID_ARG;
+  if (dtype == LMHEAD_DTYPE_F32 && !aligned4(logits)) return LMHEAD_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(logits) & 1) != 0) return LMHEAD_ERR_INVALID_ARG;
+  return LMHEAD_OK;
+}
+
+}  // namespace lmh_rows
+
+using namespace lmh_rows;
+
+LMH_API int lmhead_logits_fwd(const void* logits, int dtype, int64_t N, int64_t V,
+                              const int32_t* targets, const uint8_t* keep_mask,
+                              int return_entropy, float* logp, float* entropy,
+                              float* saved_stats, void* stream) {
+  int st = check_rows(logits, dtype, N, V);
+  if (st != LMHEAD_OK) return st;
+  if (N > 0 && (!targets || !logp || !saved_stats)) return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (return_entropy != 0) != (entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
+  if (N == 0) return LMHEAD_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == LMHEAD_DTYPE_BF16)
+    hipLaunchKernelGGL(k_logits_fwd<uint16_t>, dim3((unsigned)N), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(logits), N, V, targets, keep_mask, logp,
+                       entropy, saved_stats);
+  else
+    hipLaunchKernelGGL(k_logits_fwd<float>, dim3((unsigned)N), dim3(kThreads), 0, s,
+                       static_cast<const float*>(logits), N, V, targets, keep_mask, logp,
+                       entropy, saved_stats);
+  return hipGetLastError() == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_HIP;
+}
+
+LMH_API int lmhead_logits_bwd(const void* logits, int dtype, int64_t N, int64_t V,
+                              const int32_t* targets, const uint8_t* keep_mask,
+                              const float* saved_stats, const float* grad_logp,
+                              const float* grad_entropy, int entropy_requires_grad,
+                              void* grad_logits, void* stream) {
+  int st = check_rows(logits, dtype, N, V);
+  if (st != LMHEAD_OK) return st;
+  if (N > 0 && (!targets || !saved_stats || !grad_logp || !grad_logits))
+    return LMHEAD_ERR_INVALID_ARG;
+  if (N > 0 && (entropy_requires_grad != 0) != (grad_entropy != nullptr))
+    return LMHEAD_ERR_INVALID_ARG;
+  // the gradient has the logits' layout, so the same element alignment
+  if ((reinterpret_cast<uintptr_t>(grad_logits) & 15) !=
+      (reinterpret_cast<uintptr_t>(logits) & 15))
+    return LMHEAD_ERR_INVALID_ARG;
+  if (N == 0) return LMHEAD_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == LMHEAD_DTYPE_BF16)
+    hipLaunchKernelGGL(k_logits_bwd<uint16_t>, dim3((unsigned)N), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(logits), N, V, targets, keep_mask,
+                       saved_stats, grad_logp, entropy_requires_grad ? grad_entropy : nullptr,
+                       static_cast<uint16_t*>(grad_logits));
+  else
+    hipLaunchKernelGGL(k_logits_bwd<float>, dim3((unsigned)N), dim3(kThreads), 0, s,
+                       static_cast<const float*>(logits), N, V, targets, keep_mask, saved_stats,
+                       grad_logp, entropy_requires_grad ? grad_entropy : nullptr,
+                       static_cast<float*>(grad_logits));
+  return hipGetLastError() == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_HIP;
+}

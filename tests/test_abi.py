@@ -283,3 +283,50 @@ def _bwdp(lib, **kw):
 ])
 def test_bwd_partial_host_validation(lib, kw, code):
     assert _bwdp(lib, **kw) == code
+
+
+def _lfwd(lib, **kw):
+    a = dict(logits=FAKE, dtype=0, N=8, V=100, targets=FAKE, keep=None, ret=1, logp=FAKE,
+             ent=FAKE, stats=FAKE, stream=None)
+    a.update(kw)
+    return lib.lmhead_logits_fwd(a["logits"], a["dtype"], a["N"], a["V"], a["targets"], a["keep"],
+                                 a["ret"], a["logp"], a["ent"], a["stats"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), 1),
+    (dict(V=0), 1),
+    (dict(dtype=2), 2),
+    (dict(logits=None), 1),
+    (dict(logits=ctypes.c_void_p(0x10001)), 1),   # odd address
+    (dict(dtype=1, logits=ODD), 1),               # fp32 needs 4-byte alignment
+    (dict(targets=None), 1),
+    (dict(logp=None), 1),
+    (dict(stats=None), 1),
+    (dict(ent=None), 1),
+    (dict(ret=0), 1),
+])
+def test_logits_fwd_host_validation(lib, kw, code):
+    assert _lfwd(lib, **kw) == code
+
+
+def _lbwd(lib, **kw):
+    a = dict(logits=FAKE, dtype=0, N=8, V=100, targets=FAKE, keep=None, stats=FAKE, glp=FAKE,
+             gh=FAKE, erg=1, grad=FAKE, stream=None)
+    a.update(kw)
+    return lib.lmhead_logits_bwd(a["logits"], a["dtype"], a["N"], a["V"], a["targets"], a["keep"],
+                                 a["stats"], a["glp"], a["gh"], a["erg"], a["grad"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), 1),
+    (dict(dtype=5), 2),
+    (dict(stats=None), 1),
+    (dict(glp=None), 1),
+    (dict(gh=None), 1),
+    (dict(erg=0), 1),
+    (dict(grad=None), 1),
+    (dict(grad=ctypes.c_void_p(0x10008)), 1),     # not the logits' offset modulo 16
+])
+def test_logits_bwd_host_validation(lib, kw, code):
+    assert _lbwd(lib, **kw) == code

@@ -1,0 +1,110 @@
+"""GPU parity of the logits-input entry points (lmhead_logits_fwd /
+lmhead_logits_bwd) against the CPU float64 oracle's logits_input_fwd_bwd:
+bf16 and fp32 logits, row lengths that leave rows misaligned to 16 bytes, a
+vocabulary shorter than one vector, masked rows, with and without the
+entropy gradient, and -inf logits.
+
+Bars: log-prob, entropy and LSE within 2e-3 absolute; dL/dlogits of kept
+rows within 1e-2 relative Frobenius error; skipped rows +0.0 (bitwise).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import lm_head_log_amd as lmh
+import oracle
+from tests.gpu_helpers import TOL_ENT, TOL_GRAD_REL, TOL_LOGP, assert_pos_zero, rel_fro, say
+from workloads import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(N, V, seed, scale=2.0, keep_fraction=0.7):
+    rng = np.random.default_rng(seed)
+    z = (rng.standard_normal((N, V)) * scale).astype(np.float32)
+    t = rng.integers(0, V, N).astype(np.int32)
+    keep = (rng.random(N) < keep_fraction).astype(np.uint8)
+    g_lp = rng.standard_normal(N).astype(np.float32)
+    g_h = rng.standard_normal(N).astype(np.float32)
+    return z, t, keep, g_lp, g_h
+
+
+def _device_logits(z, dtype):
+    if dtype == torch.bfloat16:
+        bits = f32_to_bf16_bits(z)
+        host = oracle.bf16_to_f64(bits)
+        dev = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        host = z.astype(np.float64)
+        dev = torch.from_numpy(z).cuda()
+    return host, dev
+
+
+def _grad_to_f64(g):
+    if g.dtype == torch.bfloat16:
+        return oracle.bf16_to_f64(g.view(torch.int16).cpu().numpy().view(np.uint16))
+    return g.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("N,V,dtype,erg,seed", [
+    (300, 1000, torch.bfloat16, True, 41),
+    (257, 1001, torch.bfloat16, True, 42),    # odd row length: rows alternate alignment
+    (130, 3, torch.float32, True, 43),        # shorter than one vector
+    (64, 50000, torch.float32, False, 44),    # long rows, no entropy gradient
+    (200, 4099, torch.float32, True, 45),     # fp32 rows misaligned to 16 bytes
+    (33, 151936, torch.bfloat16, True, 46),   # a Qwen-size vocabulary row
+])
+def test_logits_entry_parity(N, V, dtype, erg, seed):
+    say(f"case: logits N{N} V{V} {dtype} erg={erg}")
+    z, t, keep, g_lp, g_h = _case(N, V, seed)
+    host, dz = _device_logits(z, dtype)
+    dt = torch.from_numpy(t).cuda()
+    dk = torch.from_numpy(keep).cuda()
+    lp, ent, stats = lmh.lmhead_logits_fwd(dz, dt, dk, True)
+    grad = lmh.lmhead_logits_bwd(dz, dt, stats, torch.from_numpy(g_lp).cuda(),
+                                 torch.from_numpy(g_h).cuda() if erg else None, erg, dk)
+    torch.cuda.synchronize()
+    kept = np.flatnonzero(keep)
+    skipped = np.flatnonzero(keep == 0)
+    ref = oracle.logits_input_fwd_bwd(host[kept], t[kept], g_lp[kept], g_h[kept], erg)
+    lp_g, ent_g, st_g = lp.cpu().numpy(), ent.cpu().numpy(), stats.cpu().numpy()
+    e_lp = np.abs(lp_g[kept] - ref["logp"]).max()
+    e_h = np.abs(ent_g[kept] - ref["entropy"]).max()
+    e_l = np.abs(st_g[kept, 0] - ref["lse"]).max()
+    say(f"logp err {e_lp:.2e} entropy err {e_h:.2e} lse err {e_l:.2e}")
+    assert e_lp <= TOL_LOGP and e_h <= TOL_ENT and e_l <= TOL_LOGP
+    np.testing.assert_allclose(st_g[kept, 1], ent_g[kept], rtol=0, atol=0)
+    assert_pos_zero(lp_g[skipped], "logp skipped")
+    assert_pos_zero(ent_g[skipped], "entropy skipped")
+    g = _grad_to_f64(grad)
+    eg = rel_fro(g[kept], ref["dlogits"])
+    say(f"dlogits rel err {eg:.2e}")
+    assert eg <= TOL_GRAD_REL
+    assert_pos_zero(g[skipped].astype(np.float32), "dlogits skipped rows")
+
+
+def test_minus_infinity_logits_count_as_zero_probability():
+    """-inf entries drop out exactly: the result equals the oracle on the row
+    without those columns (same distribution over the rest)."""
+    N, V = 40, 600
+    z, t, _, g_lp, g_h = _case(N, V, 47, keep_fraction=1.0)
+    rng = np.random.default_rng(48)
+    dead = rng.random((N, V)) < 0.3
+    dead[np.arange(N), t] = False
+    z[dead] = -np.inf
+    dz = torch.from_numpy(z).cuda()
+    dt = torch.from_numpy(t).cuda()
+    lp, ent, stats = lmh.lmhead_logits_fwd(dz, dt, None, True)
+    grad = lmh.lmhead_logits_bwd(dz, dt, stats, torch.from_numpy(g_lp).cuda(),
+                                 torch.from_numpy(g_h).cuda(), True)
+    lp, ent, grad = lp.cpu().numpy(), ent.cpu().numpy(), grad.cpu().numpy()
+    assert np.all(grad[dead] == 0)
+    for i in range(N):
+        live = np.flatnonzero(~dead[i])
+        ti = int(np.flatnonzero(live == t[i])[0])
+        ref = oracle.logits_input_fwd_bwd(z[i:i + 1, live].astype(np.float64), np.array([ti]),
+                                          g_lp[i:i + 1], g_h[i:i + 1], True)
+        assert abs(lp[i] - ref["logp"][0]) <= TOL_LOGP
+        assert abs(ent[i] - ref["entropy"][0]) <= TOL_ENT
+        assert rel_fro(grad[i, live], ref["dlogits"][0]) <= TOL_GRAD_REL
