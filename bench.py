@@ -163,6 +163,74 @@ def shard_leg(lmh, X, W, t, glp, gh, erg, stream, dev, steps):
     }
 
 
+# Materialised-logits entry at the shape of twinkle PR #283's experiment
+# (16384 tokens, vocabulary 151936, bf16 logits).
+LOGITS_N, LOGITS_V = 16384, 151936
+PEAK_HBM_GBPS = 8000.0
+
+
+def logits_leg(lmh, stream, dev, steps):
+    """Times lmhead_logits_fwd + lmhead_logits_bwd on synthetic bf16 logits
+    already in HBM; both are HBM-bound streams (the forward reads the logits,
+    the backward reads them and writes the gradient)."""
+    import torch
+    N, V = LOGITS_N, LOGITS_V
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    z = (torch.randn(N, V, generator=g, device=dev) * 2.0).to(torch.bfloat16)
+    t = torch.randint(0, V, (N,), generator=g, device=dev, dtype=torch.int32)
+    glp = torch.randn(N, generator=g, device=dev)
+    gh = torch.randn(N, generator=g, device=dev)
+    lp = torch.empty(N, dtype=torch.float32, device=dev)
+    en = torch.empty(N, dtype=torch.float32, device=dev)
+    st = torch.empty(N, 2, dtype=torch.float32, device=dev)
+    gz = torch.empty_like(z)
+
+    def fwd():
+        lmh.lmhead_logits_fwd(z, t, None, True, logp=lp, entropy=en, saved_stats=st,
+                              stream=stream)
+
+    def bwd():
+        lmh.lmhead_logits_bwd(z, t, st, glp, gh, True, None, grad_logits=gz, stream=stream)
+
+    for _ in range(2):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fwd()
+        ev[2 * i + 1].record(stream)
+        bwd()
+        ev[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    f = float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]))
+    b = float(np.median([ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(steps)]))
+    nbytes = N * V * 2
+    del z, gz
+    return {
+        "workload": f"materialised bf16 logits N {N} V {V}, fwd (log-prob + entropy) + bwd "
+                    f"(dL/dlogits with the entropy term)",
+        "fwd_ms": round(f, 4),
+        "bwd_ms": round(b, 4),
+        "ms_per_step": round(f + b, 4),
+        "tokens_per_s": round(N / ((f + b) * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "fwd_GBps": round(nbytes / (f * 1e-3) / 1e9, 1),
+            "bwd_GBps": round(2 * nbytes / (b * 1e-3) / 1e9, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "fwd_frac": round(nbytes / (f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "bwd_frac": round(2 * nbytes / (b * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "bytes": "fwd reads N*V*2; bwd reads N*V*2 and writes N*V*2 (per-row vectors "
+                     "are < 0.1 %)",
+        },
+        "steps": steps,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +243,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-keep-sweep", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--no-logits", action="store_true",
+                    help="skip the materialised-logits entry timing")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the vocabulary-shard (one tensor-parallel rank) timing")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -327,6 +397,11 @@ def main():
         shard = shard_leg(lmh, X, W, t, glp, gh, erg, stream, dev, max(args.sweep_steps, 5))
         log(f"tp shard {shard}")
 
+    logits = None
+    if not args.no_logits and args.config == 2:
+        logits = logits_leg(lmh, stream, dev, max(args.sweep_steps, 5))
+        log(f"logits entry {logits}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -375,6 +450,7 @@ def main():
         "cpu_baseline": cpu,
         "keep_sweep": sweep,
         "tp_shard": shard,
+        "logits_input": logits,
     }
     print(json.dumps(out), flush=True)
 
