@@ -32,6 +32,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // exponential is 0 next to any real maximum while 0 * value stays finite.
 constexpr float kFloor = -1e30f;
 constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
 
 __device__ __forceinline__ float load_one(const uint16_t* p) {
   return __uint_as_float((uint32_t)(*p) << 16);
@@ -105,8 +106,10 @@ struct Stats {
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
+      // d <= 0: the hardware exp2 (results below 2^-126 flush to 0, which
+      // next to the maximum's 1 changes nothing)
       const float d = fmaxf(fmaf(z[k], kLog2e, -m), kFloor);
-      const float e = exp2f(d);
+      const float e = __builtin_amdgcn_exp2f(d);
       s += e;
       b = fmaf(e, d, b);
     }
@@ -178,7 +181,22 @@ __global__ __launch_bounds__(kThreads) void k_logits_fwd(const T* __restrict__ l
     st.add(z, z[0]);
   }
   const T* body = row + h;
-  for (int64_t c = tid; c < nv; c += kThreads) {
+  // kUnroll vectors in flight per lane: with one, the loads a CU keeps in
+  // flight cannot cover the memory latency at full bandwidth
+  int64_t c = tid;
+  for (; c + (kUnroll - 1) * kThreads < nv; c += kUnroll * kThreads) {
+    float z[kUnroll][K];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) Vec<T>::load(body + (c + u * kThreads) * K, z[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float cz = z[u][0];
+#pragma unroll
+      for (int k = 1; k < K; ++k) cz = fmaxf(cz, z[u][k]);
+      st.add(z[u], cz);
+    }
+  }
+  for (; c < nv; c += kThreads) {
     float z[K];
     Vec<T>::load(body + c * K, z);
     float cz = z[0];
@@ -244,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void k_logits_bwd(
   const int64_t tt = targets[i];
   auto dz = [&](float z) {
     const float zc = fmaxf(z, kFloor);
-    const float p = exp2f(fmaf(zc, kLog2e, -l2));
+    const float p = __builtin_amdgcn_exp2f(fmaf(zc, kLog2e, -l2));
     return p * fmaf(cb, zc, ca);
   };
   for (int64_t v = tid; v < h; v += kThreads)
@@ -253,9 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_logits_bwd(
     store_one(out + v, dz(load_one(row + v)) + (v == tt ? gl : 0.f));
   const T* body = row + h;
   T* obody = out + h;
-  for (int64_t c = tid; c < nv; c += kThreads) {
-    float z[K];
-    Vec<T>::load(body + c * K, z);
+  auto finish = [&](int64_t c, float (&z)[K]) {
     float d[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) d[k] = dz(z[k]);
@@ -266,6 +282,19 @@ __global__ __launch_bounds__(kThreads) void k_logits_bwd(
         if (k == local) d[k] += gl;
     }
     Vec<T>::store(obody + c * K, d);
+  };
+  int64_t c = tid;
+  for (; c + (kUnroll - 1) * kThreads < nv; c += kUnroll * kThreads) {
+    float z[kUnroll][K];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) Vec<T>::load(body + (c + u * kThreads) * K, z[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) finish(c + u * kThreads, z[u]);
+  }
+  for (; c < nv; c += kThreads) {
+    float z[K];
+    Vec<T>::load(body + c * K, z);
+    finish(c, z);
   }
 }
 
