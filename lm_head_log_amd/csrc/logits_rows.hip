@@ -39,15 +39,19 @@ __device__ __forceinline__ float load_one(const uint16_t* p) {
 }
 __device__ __forceinline__ float load_one(const float* p) { return *p; }
 
-// Elements per 16-byte vector.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Elements per 16-byte vector; rows are streamed once, so the vector
+// accesses are non-temporal.
 template <class T>
 struct Vec;
 template <>
 struct Vec<uint16_t> {
   static constexpr int n = 8;
   static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[8]) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       x[2 * k] = __uint_as_float(w[k] << 16);
@@ -62,21 +66,23 @@ struct Vec<uint16_t> {
       const bf16x2_t h = {(__bf16)x[2 * k], (__bf16)x[2 * k + 1]};  // round to nearest even
       w[k] = __builtin_bit_cast(uint32_t, h);
     }
-    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    const u32x4_t v = {w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
   }
 };
 template <>
 struct Vec<float> {
   static constexpr int n = 4;
   static __device__ __forceinline__ void load(const float* p, float (&x)[4]) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x;
-    x[1] = v.y;
-    x[2] = v.z;
-    x[3] = v.w;
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    x[0] = v[0];
+    x[1] = v[1];
+    x[2] = v[2];
+    x[3] = v[3];
   }
   static __device__ __forceinline__ void store(float* p, const float (&x)[4]) {
-    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    const f32x4_t v = {x[0], x[1], x[2], x[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
   }
 };
 
