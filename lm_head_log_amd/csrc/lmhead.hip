@@ -617,6 +617,9 @@ struct DzParams {
   int steal;
 };
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 // bf16 pairs: (__bf16)x rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
@@ -729,7 +732,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
         const int tr = 4 * u + (lane >> 4);
         const uint4 x = *reinterpret_cast<const uint4*>(stage + tr * 256 + ((q ^ (tr & 15)) << 4));
         const int c = tn * kBN + wn * 128 + j * 32 + tr;  // chunk row
-        *reinterpret_cast<uint4*>(P.dZ + (int64_t)c * P.ldz + vbase + q * 8) = x;
+        // non-temporal: 4 GiB of dZ streams past the caches the operand panels use
+        const u32x4_t v = {x.x, x.y, x.z, x.w};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(P.dZ + (int64_t)c * P.ldz + vbase + q * 8));
       }
     }
   }
@@ -892,7 +897,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
             x.z += o.z;
             x.w += o.w;
           }
-          *reinterpret_cast<float4*>(dst) = x;
+          const f32x4_t v = {x.x, x.y, x.z, x.w};
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(dst));
         }
       }
     }
