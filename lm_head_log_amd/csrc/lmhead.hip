@@ -219,7 +219,9 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(
 // Two partials merge exactly (up to rounding) as
 //   m = max(m1, m2), a_k = 2^(m_k - m), s = sum a_k s_k,
 //   b = sum a_k (b_k + (m_k - m) s_k).
-// Then LSE = (m + log2 s) ln 2 and entropy = (log2 s - b / s) ln 2.
+// Then LSE = (m + log2 s) ln 2 and entropy = (log2 s - b / s) ln 2. The
+// scale factors use the hardware exp2: m_k - m <= 0, and a partial more than
+// 126 (base-2 units) below the maximum contributes below 2^-126 of it.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void stat_merge(float& m, float& s, float& b, float m2, float s2,
                                            float b2) {
@@ -228,13 +230,13 @@ __device__ __forceinline__ void stat_merge(float& m, float& s, float& b, float m
   float a1 = 0.f, a2 = 0.f, t1 = 0.f, t2 = 0.f;
   if (m != -INFINITY) {
     const float d = m - mn;
-    a1 = exp2f(d);
+    a1 = __builtin_amdgcn_exp2f(d);
     t1 = a1 * (b + d * s);
     a1 *= s;
   }
   if (m2 != -INFINITY) {
     const float d = m2 - mn;
-    a2 = exp2f(d);
+    a2 = __builtin_amdgcn_exp2f(d);
     t2 = a2 * (b2 + d * s2);
     a2 *= s2;
   }
@@ -454,15 +456,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the vocab-tile partials, in ascending tile order within each of 4
-// interleaved splits, then splits 0..3 in order. The full op writes the saved
+// Merge of the vocab-tile partials, in ascending tile order within each of 8
+// interleaved splits, then splits 0..7 in order (32 rows per workgroup, so a
+// split reads 128 contiguous bytes of each partial array per tile). The full op writes the saved
 // LSE and entropy and scatters log-prob / entropy to the kept rows. The
 // vocabulary-shard form (kRecord) writes each kept row's statistics over the
 // shard instead, in natural-log units: {m, s, b, z_t} with m = max z,
 // s = sum e^(z - m), b = sum e^(z - m) (z - m), and z_t the target logit if
 // the target lies in the shard, else NaN.
 // ---------------------------------------------------------------------------
-constexpr int kMergeRows = 64;
+constexpr int kMergeRows = 32;
+constexpr int kMergeSplits = 256 / kMergeRows;
 
 template <bool kRecord>
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm,
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm,
                                                SavedView sv, float* __restrict__ logp,
                                                float* __restrict__ entropy,
                                                float4* __restrict__ rec) {
-  __shared__ float sh[3][4][kMergeRows];
+  __shared__ float sh[3][kMergeSplits][kMergeRows];
   const int rows = sv.hdr->n_kept;
   const int r = threadIdx.x & (kMergeRows - 1);
   const int split = threadIdx.x / kMergeRows;
@@ -481,7 +485,8 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm,
   if (blockIdx.x * kMergeRows >= rows) return;
   float m = -INFINITY, s = 0.f, b = 0.f;
   if (c < rows) {
-    for (int vt = split; vt < n_vt; vt += 4) {
+#pragma unroll 4
+    for (int vt = split; vt < n_vt; vt += kMergeSplits) {
       const int64_t o = (int64_t)vt * ldp + c;
       stat_merge(m, s, b, pm[o], ps[o], pb[o]);
     }
@@ -491,7 +496,7 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm,
   sh[2][split][r] = b;
   __syncthreads();
   if (split == 0 && c < rows) {
-    for (int k = 1; k < 4; ++k) stat_merge(m, s, b, sh[0][k][r], sh[1][k][r], sh[2][k][r]);
+    for (int k = 1; k < kMergeSplits; ++k) stat_merge(m, s, b, sh[0][k][r], sh[1][k][r], sh[2][k][r]);
     const int row = sv.kept_idx[c];
     const int t = tg[c];
     const bool has_t = t >= 0 && t < V;
