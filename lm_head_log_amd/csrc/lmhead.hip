@@ -28,6 +28,12 @@
 //      k_dw_tiles    dW^T (+)= X_c^T dZ        (K = chunk rows), stored as dW
 // Every GEMM reads a K-major A (W, dZ, X_c^T) and an MN-major B (X_c^T, W, dZ)
 // as they are stored.
+// Vocabulary-shard form (tensor parallelism over the weight rows; SkyRL PR
+// #2374 gemini-code-assist and cursor reviews): the same kernels on a slice
+// of the weight rows. Compaction and k_bwd_rows subtract the slice's first
+// row from the targets, the tile merge writes per-row statistics records
+// instead of log-probs (k_merge<true>), and k_merge_shards combines the
+// records of all slices into the whole op's outputs.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -53,7 +59,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // 16K-token batch at V = 131072 (4 GiB of dZ), which saves the
 // read-modify-write of dW between chunks.
 constexpr int64_t kDefaultDzBudget = int64_t(8) << 30;
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: vocabulary-shard and logits-input entry points
 
 // ---------------------------------------------------------------------------
 // Saved-state layout (device memory, filled by the forward).
