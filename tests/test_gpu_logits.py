@@ -108,3 +108,20 @@ def test_minus_infinity_logits_count_as_zero_probability():
         assert abs(lp[i] - ref["logp"][0]) <= TOL_LOGP
         assert abs(ent[i] - ref["entropy"][0]) <= TOL_ENT
         assert rel_fro(grad[i, live], ref["dlogits"][0]) <= TOL_GRAD_REL
+
+
+def test_logits_entry_empty_batch_and_single_entry_vocabulary():
+    z = torch.zeros(0, 5, dtype=torch.bfloat16, device="cuda")
+    t = torch.zeros(0, dtype=torch.int32, device="cuda")
+    lp, ent, st = lmh.lmhead_logits_fwd(z, t, None, True)
+    assert lp.numel() == 0
+    # V = 1: log-prob 0 and entropy 0 for every row, gradient 0
+    z = torch.randn(7, 1, device="cuda")
+    t = torch.zeros(7, dtype=torch.int32, device="cuda")
+    lp, ent, st = lmh.lmhead_logits_fwd(z, t, None, True)
+    g = lmh.lmhead_logits_bwd(z, t, st, torch.ones(7, device="cuda"), torch.ones(7, device="cuda"),
+                              True)
+    torch.cuda.synchronize()
+    assert np.abs(lp.cpu().numpy()).max() <= 1e-6
+    assert np.abs(ent.cpu().numpy()).max() <= 1e-6
+    assert np.abs(g.cpu().numpy()).max() <= 1e-6

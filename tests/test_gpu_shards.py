@@ -92,3 +92,44 @@ def test_shard_forward_merge_backward(N, H, V, cuts, seed):
     say(f"summed dX rel err {ex:.2e}")
     assert ex <= TOL_GRAD_REL
     torch.cuda.synchronize()
+
+
+def test_shards_without_mask_and_with_token_chunks():
+    """Every row kept (no mask) and a backward in 256-row chunks."""
+    N, H, V = 600, 256, 1300
+    cuts = [(0, 700), (700, 1300)]
+    say(f"case: shards no mask, chunked backward N{N} H{H} V{V}")
+    w = wl.small(N, H, V, seed=34, keep_fraction=1.0)
+    X, W, t, _, glp, gh = dev_tensors(w)
+    parts, saveds = [], []
+    for a, b in cuts:
+        part, saved = lmh.lmhead_fwd_partial(X, W[a:b].contiguous(), t, a, V, None)
+        parts.append(part)
+        saveds.append(saved)
+    saved = saveds[0]
+    logp, ent = lmh.lmhead_merge_partials(torch.stack(parts), saved, True, True)
+    ref = oracle.forward(w.hidden, w.weight, w.targets, None)
+    assert np.abs(logp.cpu().numpy() - ref["logp"]).max() <= TOL_LOGP
+    assert np.abs(ent.cpu().numpy() - ref["entropy"]).max() <= TOL_ENT
+    dX_ref, dW_ref = oracle.backward(w.hidden, w.weight, w.targets, None, w.g_logp,
+                                     w.g_entropy, True)
+    dX = np.zeros((N, H))
+    for a, b in cuts:
+        gX, gW = lmh.lmhead_bwd_partial(X, W[a:b].contiguous(), t, a, saved, glp, gh, True, 256)
+        dX += gX.cpu().numpy()
+        assert rel_fro(gW.cpu().numpy(), dW_ref[a:b]) <= TOL_GRAD_REL
+    assert rel_fro(dX, dX_ref) <= TOL_GRAD_REL
+    torch.cuda.synchronize()
+
+
+def test_single_shard_merge_matches_whole_vocabulary_call():
+    N, H, V = 257, 128, 999
+    say(f"case: one shard N{N} H{H} V{V}")
+    w = wl.small(N, H, V, seed=35, keep_fraction=0.5)
+    X, W, t, km, _, _ = dev_tensors(w)
+    part, saved = lmh.lmhead_fwd_partial(X, W, t, 0, V, km)
+    lp, h = lmh.lmhead_merge_partials(part[None], saved, True, False)
+    lp_full, h_full, _ = lmh.lmhead_fwd(X, W, t, km, True, False)
+    assert np.abs(lp.cpu().numpy() - lp_full.cpu().numpy()).max() <= 1e-5
+    assert np.abs(h.cpu().numpy() - h_full.cpu().numpy()).max() <= 1e-5
+    torch.cuda.synchronize()
