@@ -125,3 +125,32 @@ def test_logits_entry_empty_batch_and_single_entry_vocabulary():
     assert np.abs(lp.cpu().numpy()).max() <= 1e-6
     assert np.abs(ent.cpu().numpy()).max() <= 1e-6
     assert np.abs(g.cpu().numpy()).max() <= 1e-6
+
+
+def _pages_figures():
+    import os
+    g = {}
+    path = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.txt")
+    for line in open(path):
+        line = line.split("#", 1)[0]
+        if "=" in line:
+            k, v = line.split("=", 1)
+            g[k.strip()] = float(v.split()[0])
+    return g
+
+
+def test_bf16_logits_error_within_the_pages_figure():
+    """twinkle PR #283, Experiment results: with float32 compute, bf16 logits
+    give a max |log-prob error| of 3.0e-2 against float64 at N=512,
+    V=151936. Here the float64 reference takes the float32 logits before
+    their rounding to bf16, as a float64 reference of the model would; the
+    GPU path reads the rounded bf16 logits."""
+    g = _pages_figures()
+    N, V = int(g["twinkle_acc_N"]), int(g["twinkle_acc_V"])
+    z, t, _, g_lp, g_h = _case(N, V, 49, scale=2.0, keep_fraction=1.0)
+    _, dz = _device_logits(z, torch.bfloat16)
+    lp, ent, _ = lmh.lmhead_logits_fwd(dz, torch.from_numpy(t).cuda(), None, True)
+    ref = oracle.logits_input_fwd_bwd(z.astype(np.float64), t, g_lp, g_h, True)
+    err = np.abs(lp.cpu().numpy() - ref["logp"]).max()
+    say(f"bf16 logits max |logp err| vs float64 of the unrounded logits: {err:.2e}")
+    assert err <= g["twinkle_logp_err_bf16_after"]
