@@ -799,20 +799,43 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     const int lane = lane_fresh(), wave = wave_fresh();
     const int wm = wave >> 1, wn = wave & 1;
 
-    const int mrow = tm * kBM + wm * 128 + acc_row_lane(lane);
-    const int mlim = rows - mrow;
+    // dX rows leave through LDS: a lane holds, per register, one column of
+    // a row, so direct stores wrote 4-byte pieces (and looked up the row's
+    // original position once per register). Each wave stages one 32-row block
+    // of its 128 x 128 (16 KiB, a private half of ring slot 0 or 1) and
+    // stores whole 512-byte row segments, two rows per instruction, looking
+    // up each row's position once.
+    const int fence = acc_read_fence();
+    __syncthreads();  // every wave is done reading the ring
+    float* stage = reinterpret_cast<float*>((wave < 2 ? ra0 : ra1) + (wave & 1) * 16384);
+    const int m0 = tm * kBM + wm * 128;  // first chunk row of the wave's block
+    const int n0 = tn * kBN + wn * 128;  // first h of the wave's block
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      // row 8 (r / 4) + 4 (lane / 32) + r % 4 of the block, column j * 32 + lane % 32;
+      // rows of 128 floats, 16-byte chunk q of row t at chunk q ^ (t & 31)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (acc_row_fixed(i, r) >= mlim) continue;
-        float* drow = P.dX + (int64_t)kidx[mrow + acc_row_fixed(i, r)] * P.H;
+        const int t = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int n = tn * kBN + wn * 128 + j * 32 + (lane & 31);
-          if (n < P.H) drow[n] = acc[i][j][r];
+          const int col = j * 32 + (lane & 31);
+          stage[t * 128 + ((((col >> 2) ^ (t & 31))) << 2) + (col & 3)] =
+              acc_read(acc[i][j][r], fence);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      const int q = lane & 31;  // 16-byte chunk of the row
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int t = 2 * u + (lane >> 5);
+        const int m = m0 + i * 32 + t;
+        const int h = n0 + q * 4;
+        const float4 x = *reinterpret_cast<const float4*>(stage + t * 128 + ((q ^ (t & 31)) << 2));
+        if (m < rows && h < P.H)  // H is a multiple of 4: a chunk is whole
+          *reinterpret_cast<float4*>(P.dX + (int64_t)kidx[m] * P.H + h) = x;
+      }
+    }
   }
 }
 
