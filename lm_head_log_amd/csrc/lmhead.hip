@@ -765,6 +765,7 @@ struct DxParams {
   int steal;
 };
 
+template <int SHIFT>
 __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   LMH_DECLARE_RING;
 
@@ -792,7 +793,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     A.init(P.dZ + (int64_t)tm * kBM * P.ldz, P.ldz, rows - tm * kBM);
     B.init(P.W + (int64_t)tn * kBN, P.H, P.V, P.H - tn * kBN);
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, ring, acc);
+    mainloop<SHIFT>(A, B, nk, ring, acc);
     q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
@@ -854,6 +855,7 @@ struct DwParams {
   int steal;
 };
 
+template <int SHIFT>
 __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
   LMH_DECLARE_RING;
 
@@ -883,7 +885,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     A.init(P.XcT + (int64_t)tm * kBM * P.ldc + P.c0, P.ldc, P.H - tm * kBM);
     B.init(P.dZ + (int64_t)tn * kBN, P.ldz, rows, kBN);  // ldz covers every v of the tile
     f32x16_t acc[4][4];
-    mainloop(A, B, nk, ring, acc);
+    mainloop<SHIFT>(A, B, nk, ring, acc);
     q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
@@ -1045,6 +1047,10 @@ static int launch_shifted(int kind, int shift, dim3 grid, hipStream_t s, const P
   static_assert(sizeof...(Kernels) == 6, "one instance per even shift");
   return launch(kind, table[shift / 2], grid, dim3(kThreads), s, p);
 }
+
+// The stage shift for nk stages: the rotation runs pairs of stages, so an
+// odd count gets one padding stage.
+static int shift_for(int nk) { return stage_shift(nk + (nk & 1)); }
 
 
 #define LMH_TRY(expr)                  \
@@ -1278,7 +1284,9 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
       const int dx_grid = persistent_grid(dx_tiles);
       X2.queue = queues + (ch * 3 + 1) * kQueueInts;
       X2.steal = steal_for(dx_tiles, dx_grid);
-      LMH_TRY(launch(KK_DX, k_dx_tiles, dim3(dx_grid), dim3(kThreads), s, X2));
+      LMH_TRY(launch_shifted(KK_DX, shift_for((int)((V + kBK - 1) / kBK)), dim3(dx_grid), s, X2,
+                             k_dx_tiles<0>, k_dx_tiles<2>, k_dx_tiles<4>, k_dx_tiles<6>,
+                             k_dx_tiles<8>, k_dx_tiles<10>));
     }
     DwParams Wp;
     Wp.XcT = XcT;
@@ -1296,7 +1304,11 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
     const int dw_grid = persistent_grid(dw_tiles);
     Wp.queue = queues + (ch * 3 + 2) * kQueueInts;
     Wp.steal = steal_for(dw_tiles, dw_grid);
-    LMH_TRY(launch(KK_DW, k_dw_tiles, dim3(dw_grid), dim3(kThreads), s, Wp));
+    // the shift of a full chunk; a shorter last chunk runs a few padding
+    // stages, which read zeros
+    LMH_TRY(launch_shifted(KK_DW, shift_for((int)(G.C / kBK)), dim3(dw_grid), s, Wp,
+                           k_dw_tiles<0>, k_dw_tiles<2>, k_dw_tiles<4>, k_dw_tiles<6>,
+                           k_dw_tiles<8>, k_dw_tiles<10>));
   }
   return LMHEAD_OK;
 }
