@@ -6,12 +6,14 @@ V=131072 (SkyRL PR #2374, Performance), differentiable entropy, every row kept.
 One step = lmhead_fwd + lmhead_bwd over one synthetic batch whose inputs are
 already resident in HBM; every buffer is preallocated. After the timed steps,
 the keep-fraction sweep of the same page (same batch, nested masks) is timed
-and fitted as t = t0 + f * t1. Prints ONE JSON line on stdout; progress goes
-to stderr.
+and fitted as t = t0 + f * t1. An MFMA probe (the GEMMs' MFMA step with
+operands in registers) gives the rate and clock the chip holds under pure MFMA
+load, with this batch's own operand bits and with zeros. Prints ONE JSON line
+on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--keep 1.0]
                     [--config 2] [--token-chunk 0] [--no-cpu-baseline]
-                    [--no-keep-sweep]
+                    [--no-keep-sweep] [--no-probe]
 """
 
 from __future__ import annotations
@@ -231,6 +233,34 @@ def logits_leg(lmh, stream, dev, steps):
     }
 
 
+def probe_leg(lmh, W, X, stream, step_tflops, kernel_tflops, iters=200000):
+    """The GEMM engine's MFMA step with operands in registers (no loads, LDS
+    or epilogue), once with fragments of this batch's own W and X bits and
+    once with zero operands: the rate and clock the chip holds under pure MFMA
+    load, against which the step and its dominant kernel are also given."""
+    import torch
+    ws = torch.empty(lmh.lmhead_mfma_probe_workspace_bytes(), dtype=torch.uint8, device=X.device)
+    # warm-up: from idle the clock takes tens of milliseconds to settle
+    lmh.lmhead_mfma_probe(W, X, iters // 4, workspace=ws, stream=stream)
+    data = lmh.lmhead_mfma_probe(W, X, iters, workspace=ws, stream=stream)
+    zero = lmh.lmhead_mfma_probe(None, None, iters, workspace=ws, stream=stream,
+                                 device=X.device)
+
+    def rec(r):
+        return {"tflops": round(r["tflops"], 1), "clock_ghz": round(r["clock_ghz"], 3),
+                "ms": round(r["ms"], 3), "frac_of_bf16_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4)}
+
+    return {
+        "what": "v_mfma_f32_32x32x16_bf16, 4x4 blocks per wave, 4 waves per CU, one workgroup "
+                "per CU, operands in registers (no loads, LDS, barriers or epilogue)",
+        "operands_from_batch": rec(data),
+        "zero_operands": rec(zero),
+        "step_frac_of_batch_ceiling": round(step_tflops / data["tflops"], 4),
+        "dominant_kernel_frac_of_batch_ceiling": round(kernel_tflops / data["tflops"], 4),
+        "iters": iters,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +277,8 @@ def main():
                     help="skip the materialised-logits entry timing")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the vocabulary-shard (one tensor-parallel rank) timing")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the MFMA ceiling probe (operands in registers, no memory traffic)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (counter calibration)")
     args = ap.parse_args()
@@ -363,6 +395,11 @@ def main():
         if k in kern:
             kern[k]["tflops"] = round(fl_gemm / (kern[k]["ms_per_step"] * 1e-3) / 1e12, 1)
 
+    probe = None
+    if not args.no_probe:
+        probe = probe_leg(lmh, W, X, stream, tflops, achieved)
+        log(f"mfma probe {probe}")
+
     sweep = None
     if not args.no_keep_sweep and args.config == 2:
         import workloads as wl
@@ -448,6 +485,7 @@ def main():
             "traffic": measured_traffic(dom, w.name),
         },
         "cpu_baseline": cpu,
+        "mfma_ceiling": probe,
         "keep_sweep": sweep,
         "tp_shard": shard,
         "logits_input": logits,

@@ -294,6 +294,29 @@ int lmhead_profile_begin(void);
  * (arrays of LMHEAD_NUM_KERNELS; either may be NULL). Syncs the events. */
 int lmhead_profile_end(double* ms, int64_t* launches);
 
+/* MFMA ceiling probe for benchmarks (not needed to use the op).
+ * Runs the GEMM kernels' inner step -- v_mfma_f32_32x32x16_bf16 in 4 x 4
+ * blocks per wave, four waves per workgroup, one workgroup per CU -- with all
+ * operands in registers: no loads, no LDS traffic, no barriers. `iters` passes
+ * of four k steps each; the flop count is exact. Its rate bounds what the GEMM
+ * kernels can reach at the clock the chip holds under MFMA load, which
+ * depends on how often operand bits switch: operand fragments are read once
+ * from `a` and `b` (device bf16 arrays of a_elems / b_elems >= 8 entries,
+ * 16-byte aligned; pass the GEMMs' own operands to get their bit statistics),
+ * or are all zero when both are NULL.
+ *   workspace: device, 16-byte aligned, >= lmhead_mfma_probe_workspace_bytes()
+ *     (per-workgroup cycle counts and a per-thread sum that keeps the products
+ *     live; overwritten).
+ *   ms: elapsed kernel time (hipEvents on `stream`); flops: work done;
+ *   clock_ghz: mean s_memtime cycles of a workgroup's loop / elapsed time.
+ * Any output pointer may be NULL. Syncs `stream`. Errors: INVALID_ARG for
+ * iters outside [1, 2^24], one of a / b NULL, a short or misaligned array;
+ * WORKSPACE for a small workspace; HIP for a failed launch or event. */
+size_t lmhead_mfma_probe_workspace_bytes(void);
+int lmhead_mfma_probe(const void* a, int64_t a_elems, const void* b, int64_t b_elems,
+                      int64_t iters, void* workspace, size_t workspace_bytes,
+                      double* ms, double* flops, double* clock_ghz, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,8 @@ __all__ = [
     "lmhead_status_string", "lmhead_version", "fused_logprobs", "LMHeadError",
     "DEFAULT_TOKEN_CHUNK", "lmhead_kernel_name", "lmhead_profile_begin", "lmhead_profile_end",
     "lmhead_fwd_partial", "lmhead_merge_partials", "lmhead_bwd_partial",
-    "lmhead_logits_fwd", "lmhead_logits_bwd",
+    "lmhead_logits_fwd", "lmhead_logits_bwd", "lmhead_mfma_probe_workspace_bytes",
+    "lmhead_mfma_probe",
 ]
 
 _LOGIT_DTYPES = {torch.bfloat16: 0, torch.float32: 1}  # LMHEAD_DTYPE_BF16 / _F32
@@ -361,6 +362,34 @@ def lmhead_profile_end() -> dict:
     cnt = (ctypes.c_int64 * k)()
     check("lmhead_profile_end", _L().lmhead_profile_end(ms, cnt))
     return {lmhead_kernel_name(i): (float(ms[i]), int(cnt[i])) for i in range(k)}
+
+
+def lmhead_mfma_probe_workspace_bytes() -> int:
+    return int(_L().lmhead_mfma_probe_workspace_bytes())
+
+
+def lmhead_mfma_probe(a=None, b=None, iters=40000, *, workspace=None, stream=None,
+                      device=None) -> dict:
+    """Benchmark-only MFMA ceiling: the GEMM kernels' MFMA step with operands
+    in registers. `a`, `b`: bf16 GPU tensors whose bits feed the operand
+    fragments, or both None for zero operands. Returns
+    {"ms", "tflops", "clock_ghz"}."""
+    if (a is None) != (b is None):
+        raise ValueError("pass both operand tensors or neither")
+    for t, n in ((a, "a"), (b, "b")):
+        if t is not None:
+            _need(t, n, torch.bfloat16)
+    dev = a.device if a is not None else torch.device(device or "cuda:0")
+    if workspace is None:
+        workspace = torch.empty(lmhead_mfma_probe_workspace_bytes(), dtype=torch.uint8,
+                                device=dev)
+    ms, fl, clk = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0)
+    check("lmhead_mfma_probe", _L().lmhead_mfma_probe(
+        _ptr(a), 0 if a is None else a.numel(), _ptr(b), 0 if b is None else b.numel(), iters,
+        _ptr(workspace), workspace.numel(), ctypes.byref(ms), ctypes.byref(fl),
+        ctypes.byref(clk), _stream(stream, dev)))
+    return {"ms": ms.value, "tflops": fl.value / (ms.value * 1e-3) / 1e12 if ms.value > 0 else 0.0,
+            "clock_ghz": clk.value}
 
 
 class _FusedLMHead(torch.autograd.Function):

@@ -41,6 +41,10 @@ SIGNATURES = {
     "lmhead_kernel_name": (ctypes.c_char_p, [c_int]),
     "lmhead_profile_begin": (c_int, []),
     "lmhead_profile_end": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
+    "lmhead_mfma_probe_workspace_bytes": (c_size, []),
+    "lmhead_mfma_probe": (c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_size,
+                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(ctypes.c_double), c_vp]),
 }
 
 NUM_KERNELS = 12

@@ -13,7 +13,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("lmhead.hip", "logits_rows.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("lmhead.hip", "logits_rows.hip", "mfma_probe.hip")]
 LIB = os.path.join(PKG, "liblmhead.so")
 ARCH = "gfx950"
 

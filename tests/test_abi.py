@@ -330,3 +330,31 @@ def _lbwd(lib, **kw):
 ])
 def test_logits_bwd_host_validation(lib, kw, code):
     assert _lbwd(lib, **kw) == code
+
+
+def _probe(lib, a=FAKE, a_elems=64, b=FAKE, b_elems=64, iters=10, ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.lmhead_mfma_probe_workspace_bytes()
+    return lib.lmhead_mfma_probe(a, a_elems, b, b_elems, iters, ws, ws_bytes, None, None, None,
+                                 None)
+
+
+def test_probe_workspace_covers_one_record_per_cu(lib):
+    # a cycle count per workgroup (8 bytes) and a float per thread (256 threads),
+    # one workgroup per CU; without a GPU the library assumes 256 CUs
+    n = lib.lmhead_mfma_probe_workspace_bytes()
+    assert n > 0 and n % (8 + 256 * 4) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(iters=0), 1),
+    (dict(iters=(1 << 24) + 1), 1),
+    (dict(a=None), 1),                # one operand array without the other
+    (dict(b=None), 1),
+    (dict(a_elems=4), 1),             # fewer than one fragment of 8 values
+    (dict(b=ODD), 1),                 # misaligned
+    (dict(ws=None), 1),
+    (dict(ws_bytes=16), 3),
+])
+def test_probe_host_validation(lib, kw, code):
+    assert _probe(lib, **kw) == code
