@@ -125,6 +125,28 @@ int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
                void* workspace, size_t workspace_bytes,
                void* stream);
 
+/* Block-sparse forward: the same arguments, outputs and saved state as
+ * lmhead_fwd, but rows are not compacted. The rows are taken in place in
+ * tiles of 256 consecutive rows (the GEMMs' token tile), and only tiles with
+ * no kept row are skipped (SkyRL PR #2374, "How it works": block-sparse
+ * forward and backward that skip inactive tiles). Every row of a tile that
+ * holds a kept row runs through the projection. Rows that are not kept still
+ * get +0.0 log-prob and entropy, and lmhead_bwd gives them an all-zero logit
+ * gradient: a +0.0 dX row and no dW contribution. Per row, log-prob, entropy
+ * and dX equal those of lmhead_fwd + lmhead_bwd bit for bit, because a row's
+ * results do not depend on which other rows share its tile. dW sums the same
+ * rows with zero rows between them, in a different order, so it agrees to
+ * rounding. The saved header counts the listed rows as n_kept (what
+ * lmhead_read_n_kept reports) and sets bit 2 of its flags. Take the
+ * backward with lmhead_bwd. Same errors as lmhead_fwd. */
+int lmhead_fwd_blocksparse(const void* hidden, const void* weight, const int32_t* targets,
+                           const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V,
+                           int return_entropy, int entropy_requires_grad,
+                           float* logp, float* entropy,
+                           void* saved, size_t saved_bytes,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Backward: per chunk of `token_chunk` kept rows, recompute the logit tile,
  * form dZ (above) in bf16, then dX rows = dZ W (scattered back to the rows'
  * original positions) and dW (+)= dZ^T X. The first chunk writes dW, later
@@ -260,7 +282,8 @@ int lmhead_logits_bwd(const void* logits, int dtype, int64_t N, int64_t V,
 
 /* Syncs `stream`, then reads the number of kept rows from `saved` into
  * *n_kept_host (the token fraction the trainer logs, prime-rl PR #3326,
- * Overview). */
+ * Overview); after lmhead_fwd_blocksparse, the number of rows in the tiles it
+ * ran. */
 int lmhead_read_n_kept(const void* saved, int64_t* n_kept_host, void* stream);
 
 /* Syncs `stream`, then returns LMHEAD_ERR_TARGET_RANGE if the forward that

@@ -24,7 +24,8 @@ from ._lib import LMHeadError, check
 
 __all__ = [
     "lmhead_saved_bytes", "lmhead_fwd_workspace_bytes", "lmhead_bwd_workspace_bytes",
-    "lmhead_fwd", "lmhead_bwd", "lmhead_read_n_kept", "lmhead_check_status",
+    "lmhead_fwd", "lmhead_fwd_blocksparse", "lmhead_bwd", "lmhead_read_n_kept",
+    "lmhead_check_status",
     "lmhead_status_string", "lmhead_version", "fused_logprobs", "LMHeadError",
     "DEFAULT_TOKEN_CHUNK", "lmhead_kernel_name", "lmhead_profile_begin", "lmhead_profile_end",
     "lmhead_fwd_partial", "lmhead_merge_partials", "lmhead_bwd_partial",
@@ -88,7 +89,7 @@ def lmhead_version() -> int:
 
 def lmhead_fwd(hidden, weight, targets, keep_mask=None, return_entropy=False,
                entropy_requires_grad=False, *, logp=None, entropy=None, saved=None,
-               workspace=None, stream=None):
+               workspace=None, stream=None, _entry="lmhead_fwd"):
     """Forward. hidden bf16 [N, H], weight bf16 [V, H], targets int32 [N],
     keep_mask uint8/bool [N] or None. Returns (logp fp32 [N], entropy fp32 [N]
     or None, saved uint8 tensor). Output and scratch buffers may be passed in
@@ -123,12 +124,23 @@ def lmhead_fwd(hidden, weight, targets, keep_mask=None, return_entropy=False,
     wb = int(L.lmhead_fwd_workspace_bytes(N, H, V))
     if workspace is None:
         workspace = torch.empty(max(wb, 1), dtype=torch.uint8, device=dev)
-    st = L.lmhead_fwd(_ptr(hidden), _ptr(weight), _ptr(targets), _ptr(keep_mask), N, H, V,
-                      int(bool(return_entropy)), int(bool(entropy_requires_grad)),
-                      _ptr(logp), _ptr(entropy), _ptr(saved), saved.numel(),
-                      _ptr(workspace), workspace.numel(), _stream(stream, dev))
-    check("lmhead_fwd", st)
+    st = getattr(L, _entry)(_ptr(hidden), _ptr(weight), _ptr(targets), _ptr(keep_mask), N, H,
+                            V, int(bool(return_entropy)), int(bool(entropy_requires_grad)),
+                            _ptr(logp), _ptr(entropy), _ptr(saved), saved.numel(),
+                            _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    check(_entry, st)
     return logp, entropy, saved
+
+
+def lmhead_fwd_blocksparse(hidden, weight, targets, keep_mask=None, return_entropy=False,
+                           entropy_requires_grad=False, *, logp=None, entropy=None, saved=None,
+                           workspace=None, stream=None):
+    """Block-sparse forward: as lmhead_fwd, but the rows stay in place and only
+    256-row tiles with no kept row are skipped. Same outputs; the backward is
+    lmhead_bwd."""
+    return lmhead_fwd(hidden, weight, targets, keep_mask, return_entropy, entropy_requires_grad,
+                      logp=logp, entropy=entropy, saved=saved, workspace=workspace,
+                      stream=stream, _entry="lmhead_fwd_blocksparse")
 
 
 def lmhead_bwd(hidden, weight, targets, saved, grad_logp, grad_entropy=None,

@@ -22,6 +22,8 @@ SIGNATURES = {
     "lmhead_bwd_workspace_bytes": (c_size, [c_i64, c_i64, c_i64, c_i64]),
     "lmhead_fwd": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_int,
                            c_vp, c_vp, c_vp, c_size, c_vp, c_size, c_vp]),
+    "lmhead_fwd_blocksparse": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int,
+                                       c_int, c_vp, c_vp, c_vp, c_size, c_vp, c_size, c_vp]),
     "lmhead_bwd": (c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_size,
                            c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_size, c_vp]),
     "lmhead_fwd_partial": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,

@@ -59,7 +59,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // 16K-token batch at V = 131072 (4 GiB of dZ), which saves the
 // read-modify-write of dW between chunks.
 constexpr int64_t kDefaultDzBudget = int64_t(8) << 30;
-constexpr int kVersion = 200;  // 0.2.0: vocabulary-shard and logits-input entry points
+constexpr int kVersion = 300;  // 0.3.0: block-sparse forward, MFMA ceiling probe
 
 // ---------------------------------------------------------------------------
 // Saved-state layout (device memory, filled by the forward).
@@ -167,20 +167,38 @@ static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk)
 
 // ---------------------------------------------------------------------------
 // Compaction (one workgroup; each thread owns a contiguous segment).
+// Rows are taken in blocks of `block` consecutive rows: a block is listed,
+// whole, when any of its rows is kept. block = 1 lists exactly the kept rows
+// (the compacting forward); block = 256 lists every row of each 256-row tile
+// that holds a kept row, in place, so that the GEMMs skip only the tiles whose
+// rows are all masked (the block-sparse forward). A listed row that is not
+// kept gets pos = -2 - c (c its listed position) and target -1; the merge
+// and the backward give it +0.0 outputs and an all-zero dz row.
 // ---------------------------------------------------------------------------
 constexpr int kCompactThreads = 1024;
 
+__device__ __forceinline__ bool block_listed(const uint8_t* __restrict__ keep, int b0, int b1) {
+  if (keep == nullptr) return true;
+  for (int i = b0; i < b1; ++i)
+    if (keep[i] != 0) return true;
+  return false;
+}
+
 __global__ __launch_bounds__(kCompactThreads) void k_compact(
     const uint8_t* __restrict__ keep, const int32_t* __restrict__ targets, int N, int H, int V,
-    int flags, int32_t* __restrict__ kept_idx, int32_t* __restrict__ pos,
+    int flags, int block, int32_t* __restrict__ kept_idx, int32_t* __restrict__ pos,
     SavedHeader* __restrict__ hdr, int32_t* __restrict__ tg, int tg_rows, int vocab_start) {
   __shared__ int scan[kCompactThreads];
   const int tid = threadIdx.x;
-  const int seg = (N + kCompactThreads - 1) / kCompactThreads;
+  int seg = (N + kCompactThreads - 1) / kCompactThreads;
+  seg = (seg + block - 1) / block * block;  // segments hold whole blocks
   const int beg = min(N, tid * seg);
   const int end = min(N, beg + seg);
   int cnt = 0;
-  for (int i = beg; i < end; ++i) cnt += keep ? (keep[i] != 0) : 1;
+  for (int b0 = beg; b0 < end; b0 += block) {
+    const int b1 = min(end, b0 + block);
+    if (block_listed(keep, b0, b1)) cnt += b1 - b0;
+  }
   scan[tid] = cnt;
   __syncthreads();
   // Hillis-Steele inclusive scan over the per-thread counts.
@@ -192,20 +210,29 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(
   }
   int o = scan[tid] - cnt;
   int bad = 0;
-  for (int i = beg; i < end; ++i) {
-    const bool k = keep ? (keep[i] != 0) : true;
-    if (k) {
-      const int t = targets[i];
+  for (int b0 = beg; b0 < end; b0 += block) {
+    const int b1 = min(end, b0 + block);
+    const bool listed = block_listed(keep, b0, b1);
+    for (int i = b0; i < b1; ++i) {
+      if (!listed) {
+        pos[i] = -1;
+        continue;
+      }
+      const bool k = keep ? (keep[i] != 0) : true;
       kept_idx[o] = i;
-      pos[i] = o;
-      tg[o] = t - vocab_start;  // row of the weight this call reads
+      if (k) {
+        const int t = targets[i];
+        pos[i] = o;
+        tg[o] = t - vocab_start;  // row of the weight this call reads
+        bad |= (t < 0 || t >= V);
+      } else {
+        pos[i] = -2 - o;
+        tg[o] = -1;
+      }
       ++o;
-      bad |= (t < 0 || t >= V);
-    } else {
-      pos[i] = -1;
     }
   }
-  // compact targets past the kept rows: -1 matches no vocabulary row
+  // compact targets past the listed rows: -1 matches no vocabulary row
   for (int c = scan[kCompactThreads - 1] + tid; c < tg_rows; c += kCompactThreads) tg[c] = -1;
   bad = __syncthreads_or(bad);
   if (tid == 0) {
@@ -509,14 +536,15 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm,
     if constexpr (kRecord) {
       rec[row] = make_float4(m * kLn2, s, b * kLn2, has_t ? zt[c] : __builtin_nanf(""));
     } else {
+      const bool live = sv.pos[row] == c;  // a listed row of a masked block is not kept
       const float l2s = log2f(s);
       const float lse = (m + l2s) * kLn2;
       const float ent = (l2s - b / s) * kLn2;
       const float lp = has_t ? zt[c] - lse : __builtin_nanf("");
       sv.lse[c] = lse;
       sv.ent[c] = ent;
-      logp[row] = lp;
-      if (entropy) entropy[row] = ent;
+      logp[row] = live ? lp : 0.f;
+      if (entropy) entropy[row] = live ? ent : 0.f;
     }
   }
 }
@@ -589,7 +617,8 @@ __global__ void k_zero_rows(const int32_t* __restrict__ pos, int N, int H, float
 //   dz = p (ca + cb (z - LSE)) + g_lp [v = t],  p = 2^(z log2 e - LSE log2 e),
 //   ca = -(g_lp + g_H H),  cb = -g_H,
 // stored as {LSE log2 e, ca - cb LSE, cb, g_lp} with the target t beside it.
-// Rows past the kept ones get zeros and target -1, so their dz is exactly 0.
+// Rows past the listed ones, and listed rows that are not kept (block-sparse
+// forward), get zeros and target -1, so their dz is exactly 0.
 __global__ __launch_bounds__(256) void k_bwd_rows(SavedView sv, const int32_t* __restrict__ targets,
                                                   const float* __restrict__ g_lp,
                                                   const float* __restrict__ g_h, int n_rows,
@@ -599,8 +628,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(SavedView sv, const int32_t* _
   if (c >= n_rows) return;
   float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
   int t = -1;
-  if (c < sv.hdr->n_kept) {
-    const int row = sv.kept_idx[c];
+  const int row = c < sv.hdr->n_kept ? sv.kept_idx[c] : -1;
+  if (row >= 0 && sv.pos[row] == c) {
     const float lse = sv.lse[c];
     const float glp = g_lp[row];
     const float gh = g_h ? g_h[row] : 0.f;
@@ -1083,9 +1112,9 @@ LMH_API size_t lmhead_bwd_workspace_bytes(int64_t N, int64_t H, int64_t V, int64
 // (rec != nullptr: per-row shard statistics instead of log-prob / entropy).
 static int fwd_impl(const void* hidden, const void* weight, const int32_t* targets,
                     const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V, int64_t vocab_start,
-                    int64_t V_total, int flags, float* logp, float* entropy, float4* rec,
-                    void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
-                    hipStream_t s) {
+                    int64_t V_total, int flags, int block, float* logp, float* entropy,
+                    float4* rec, void* saved, size_t saved_bytes, void* workspace,
+                    size_t workspace_bytes, hipStream_t s) {
   const FwdWs L = fwd_ws(N, H, V);
   if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return LMHEAD_ERR_WORKSPACE;
   if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
@@ -1093,7 +1122,7 @@ static int fwd_impl(const void* hidden, const void* weight, const int32_t* targe
   char* w = static_cast<char*>(workspace);
   int32_t* tg = reinterpret_cast<int32_t*>(w + L.tg);
   LMH_TRY(launch(KK_COMPACT, k_compact, dim3(1), dim3(kCompactThreads), s, keep_mask, targets,
-                 (int)N, (int)H, (int)V_total, flags, sv.kept_idx, sv.pos, sv.hdr, tg,
+                 (int)N, (int)H, (int)V_total, flags, block, sv.kept_idx, sv.pos, sv.hdr, tg,
                  (int)tile_rows(N), (int)vocab_start));
   if (N == 0) return LMHEAD_OK;
 
@@ -1145,11 +1174,14 @@ static int fwd_impl(const void* hidden, const void* weight, const int32_t* targe
   return LMHEAD_OK;
 }
 
-LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
-                       const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V,
-                       int return_entropy, int entropy_requires_grad, float* logp, float* entropy,
-                       void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+// Shared by the two whole-vocabulary forwards: block = 1 compacts to the kept
+// rows, block = kBlockSparseRows lists whole row tiles (flag bit 2 records it).
+constexpr int kBlockSparseRows = kBN;  // one GEMM token tile
+static int fwd_entry(const void* hidden, const void* weight, const int32_t* targets,
+                     const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V,
+                     int return_entropy, int entropy_requires_grad, float* logp, float* entropy,
+                     void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                     void* stream, int block) {
   int st = check_sizes(N, H, V);
   if (st != LMHEAD_OK) return st;
   if (!saved) return LMHEAD_ERR_INVALID_ARG;
@@ -1160,10 +1192,32 @@ LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* ta
   if (entropy_requires_grad && !return_entropy) return LMHEAD_ERR_INVALID_ARG;
   if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace))
     return LMHEAD_ERR_INVALID_ARG;
-  const int flags = (return_entropy ? 1 : 0) | (entropy_requires_grad ? 2 : 0);
-  return fwd_impl(hidden, weight, targets, keep_mask, N, H, V, 0, V, flags, logp, entropy,
+  const int flags = (return_entropy ? 1 : 0) | (entropy_requires_grad ? 2 : 0) |
+                    (block > 1 ? 4 : 0);
+  return fwd_impl(hidden, weight, targets, keep_mask, N, H, V, 0, V, flags, block, logp, entropy,
                   nullptr, saved, saved_bytes, workspace, workspace_bytes,
                   static_cast<hipStream_t>(stream));
+}
+
+LMH_API int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
+                       const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V,
+                       int return_entropy, int entropy_requires_grad, float* logp, float* entropy,
+                       void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return fwd_entry(hidden, weight, targets, keep_mask, N, H, V, return_entropy,
+                   entropy_requires_grad, logp, entropy, saved, saved_bytes, workspace,
+                   workspace_bytes, stream, 1);
+}
+
+LMH_API int lmhead_fwd_blocksparse(const void* hidden, const void* weight,
+                                   const int32_t* targets, const uint8_t* keep_mask, int64_t N,
+                                   int64_t H, int64_t V, int return_entropy,
+                                   int entropy_requires_grad, float* logp, float* entropy,
+                                   void* saved, size_t saved_bytes, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return fwd_entry(hidden, weight, targets, keep_mask, N, H, V, return_entropy,
+                   entropy_requires_grad, logp, entropy, saved, saved_bytes, workspace,
+                   workspace_bytes, stream, kBlockSparseRows);
 }
 
 LMH_API int lmhead_fwd_partial(const void* hidden, const void* weight_shard,
@@ -1181,7 +1235,7 @@ LMH_API int lmhead_fwd_partial(const void* hidden, const void* weight_shard,
       !aligned16(workspace) || !aligned16(partial))
     return LMHEAD_ERR_INVALID_ARG;
   return fwd_impl(hidden, weight_shard, targets, keep_mask, N, H, V_shard, vocab_start, V_total,
-                  0, nullptr, nullptr, reinterpret_cast<float4*>(partial), saved, saved_bytes,
+                  0, 1, nullptr, nullptr, reinterpret_cast<float4*>(partial), saved, saved_bytes,
                   workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 

@@ -37,12 +37,13 @@ def dev_tensors(w, device="cuda:0", keep=None, use_mask=True):
 
 
 def run(w, keep=None, use_mask=True, token_chunk=0, backward=True, erg=None, ret=None,
-        device="cuda:0"):
-    """Run forward (and backward) on the GPU; return numpy results."""
+        device="cuda:0", fwd=None):
+    """Run forward (and backward) on the GPU; return numpy results. `fwd` is
+    the forward call (lmhead_fwd by default)."""
     X, W, t, km, glp, gh = dev_tensors(w, device, keep, use_mask)
     erg = w.entropy_requires_grad if erg is None else erg
     ret = w.return_entropy if ret is None else ret
-    logp, ent, saved = lmh.lmhead_fwd(X, W, t, km, ret, erg)
+    logp, ent, saved = (fwd or lmh.lmhead_fwd)(X, W, t, km, ret, erg)
     out = dict(logp=logp.cpu().numpy(), entropy=None if ent is None else ent.cpu().numpy())
     n = lmh.lmhead_read_n_kept(saved)
     out["n_kept"] = n
