@@ -13,7 +13,7 @@ on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--keep 1.0]
                     [--config 2] [--token-chunk 0] [--no-cpu-baseline]
-                    [--no-keep-sweep] [--no-probe]
+                    [--no-keep-sweep] [--no-probe] [--no-blocksparse]
 """
 
 from __future__ import annotations
@@ -233,6 +233,49 @@ def logits_leg(lmh, stream, dev, steps):
     }
 
 
+def blocksparse_leg(lmh, stream, dev, steps):
+    """The scoring batch (N 262144, H 5120, V 152064, keep in contiguous spans
+    of 64-2048 tokens), forward only: the compacting forward against the
+    block-sparse one, which runs every row of each 256-row tile that holds a
+    kept row in place (SkyRL PR #2374, "How it works")."""
+    import torch
+
+    import workloads as wl
+    w = wl.config5()
+    N, H, V = w.N, w.H, w.V
+    X = torch.from_numpy(w.hidden.view(np.int16)).view(torch.bfloat16).to(dev)
+    W = torch.from_numpy(w.weight.view(np.int16)).view(torch.bfloat16).to(dev)
+    t = torch.from_numpy(w.targets).to(dev)
+    km = torch.from_numpy(w.keep).to(dev)
+    n_kept = int(w.keep.sum())
+    del w
+    lp = torch.empty(N, dtype=torch.float32, device=dev)
+    ent = torch.empty(N, dtype=torch.float32, device=dev)
+    saved = torch.empty(lmh.lmhead_saved_bytes(N), dtype=torch.uint8, device=dev)
+    ws = torch.empty(lmh.lmhead_fwd_workspace_bytes(N, H, V), dtype=torch.uint8, device=dev)
+    out = {"workload": f"scoring N{N} H{H} V{V}, keep in spans of 64-2048 tokens, forward only",
+           "n_kept": n_kept, "steps": steps}
+    for name, fn in (("compact", lmh.lmhead_fwd), ("block_sparse", lmh.lmhead_fwd_blocksparse)):
+        def call():
+            fn(X, W, t, km, True, False, logp=lp, entropy=ent, saved=saved, workspace=ws,
+               stream=stream)
+        call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        rows = lmh.lmhead_read_n_kept(saved)
+        out[name] = {"ms": round(ms, 3), "rows_run": rows,
+                     "tflops_over_kept_rows": round(2.0 * n_kept * H * V / (ms * 1e-3) / 1e12, 1),
+                     "tflops_over_rows_run": round(2.0 * rows * H * V / (ms * 1e-3) / 1e12, 1)}
+    out["block_sparse_over_compact_time"] = round(out["block_sparse"]["ms"] / out["compact"]["ms"], 4)
+    return out
+
+
 def probe_leg(lmh, W, X, stream, step_tflops, kernel_tflops, iters=200000):
     """The GEMM engine's MFMA step with operands in registers (no loads, LDS
     or epilogue), once with fragments of this batch's own W and X bits and
@@ -277,6 +320,8 @@ def main():
                     help="skip the materialised-logits entry timing")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the vocabulary-shard (one tensor-parallel rank) timing")
+    ap.add_argument("--no-blocksparse", action="store_true",
+                    help="skip the block-sparse vs compacting forward on the scoring batch")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the MFMA ceiling probe (operands in registers, no memory traffic)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -439,6 +484,11 @@ def main():
         logits = logits_leg(lmh, stream, dev, max(args.sweep_steps, 5))
         log(f"logits entry {logits}")
 
+    bsp = None
+    if not args.no_blocksparse and args.config == 2:
+        bsp = blocksparse_leg(lmh, stream, dev, 3)
+        log(f"block-sparse vs compacting forward {bsp}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -489,6 +539,7 @@ def main():
         "keep_sweep": sweep,
         "tp_shard": shard,
         "logits_input": logits,
+        "block_sparse_scoring": bsp,
     }
     print(json.dumps(out), flush=True)
 
