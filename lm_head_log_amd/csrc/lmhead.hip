@@ -4,8 +4,8 @@
 // Forward (prime-rl PR #3326 Overview: compact -> chunked log-prob/entropy ->
 // expand back; SkyRL PR #2374 "How it works": one projection gives both the
 // selected-token log-prob and the entropy):
-//   1. k_compact     keep mask -> ascending kept rows, row -> compact position,
-//                    target of each compact row
+//   1. k_compact_*   keep mask -> ascending kept rows, row -> compact position,
+//                    target of each compact row (count, scan, write)
 //   2. k_gather_cols X_c^T = X[kept]^T [h][c], the token operand of the logit
 //                    GEMM (k = h rows, tokens contiguous)
 //   3. k_fwd_tiles   Z^T tile = W[vtile] X[kept]^T on MFMA, never stored; per
@@ -108,7 +108,8 @@ static inline int64_t ldc_of(int64_t N) { return round_up(N, 64); }
 static inline int64_t tile_rows(int64_t N) { return round_up(N, 256); }
 
 // Forward workspace: tile-queue counters | compact targets [tile_rows] |
-// target logits [N] | partial m, s, b [n_vt][N] each | X_c^T [H][ldc] (bf16).
+// target logits [N] (first the compaction's per-chunk counts and flags) |
+// partial m, s, b [n_vt][N] each | X_c^T [H][ldc] (bf16).
 struct FwdWs {
   size_t q, tg, zt, pm, ps, pb, xct, total;
 };
@@ -166,7 +167,13 @@ static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk)
 }
 
 // ---------------------------------------------------------------------------
-// Compaction (one workgroup; each thread owns a contiguous segment).
+// Compaction, in three launches so that it scales with N: every workgroup owns
+// kCompactRows consecutive rows (16 per thread), (1) counts the rows it lists
+// and flags kept rows whose target is out of range, (2) one workgroup scans
+// the per-chunk counts into offsets and writes the saved header, (3) every
+// workgroup writes its rows at its offset. The per-chunk counts and flags live
+// in the forward's target-logit array, which the projection fills only later.
+//
 // Rows are taken in blocks of `block` consecutive rows: a block is listed,
 // whole, when any of its rows is kept. block = 1 lists exactly the kept rows
 // (the compacting forward); block = 256 lists every row of each 256-row tile
@@ -175,74 +182,148 @@ static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk)
 // kept gets pos = -2 - c (c its listed position) and target -1; the merge
 // and the backward give it +0.0 outputs and an all-zero dz row.
 // ---------------------------------------------------------------------------
-constexpr int kCompactThreads = 1024;
+constexpr int kCompactThreads = 256;
+constexpr int kCompactPerThread = 16;
+constexpr int kCompactRows = kCompactThreads * kCompactPerThread;  // 4096, a whole number of 256-row blocks
+constexpr int kScanThreads = 1024;
 
-__device__ __forceinline__ bool block_listed(const uint8_t* __restrict__ keep, int b0, int b1) {
-  if (keep == nullptr) return true;
-  for (int i = b0; i < b1; ++i)
-    if (keep[i] != 0) return true;
-  return false;
-}
+static inline int compact_chunks(int64_t N) { return (int)((N + kCompactRows - 1) / kCompactRows); }
 
-__global__ __launch_bounds__(kCompactThreads) void k_compact(
-    const uint8_t* __restrict__ keep, const int32_t* __restrict__ targets, int N, int H, int V,
-    int flags, int block, int32_t* __restrict__ kept_idx, int32_t* __restrict__ pos,
-    SavedHeader* __restrict__ hdr, int32_t* __restrict__ tg, int tg_rows, int vocab_start) {
-  __shared__ int scan[kCompactThreads];
-  const int tid = threadIdx.x;
-  int seg = (N + kCompactThreads - 1) / kCompactThreads;
-  seg = (seg + block - 1) / block * block;  // segments hold whole blocks
-  const int beg = min(N, tid * seg);
-  const int end = min(N, beg + seg);
-  int cnt = 0;
-  for (int b0 = beg; b0 < end; b0 += block) {
-    const int b1 = min(end, b0 + block);
-    if (block_listed(keep, b0, b1)) cnt += b1 - b0;
-  }
-  scan[tid] = cnt;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the per-thread counts.
-  for (int off = 1; off < kCompactThreads; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  int o = scan[tid] - cnt;
-  int bad = 0;
-  for (int b0 = beg; b0 < end; b0 += block) {
-    const int b1 = min(end, b0 + block);
-    const bool listed = block_listed(keep, b0, b1);
-    for (int i = b0; i < b1; ++i) {
-      if (!listed) {
-        pos[i] = -1;
-        continue;
-      }
-      const bool k = keep ? (keep[i] != 0) : true;
-      kept_idx[o] = i;
-      if (k) {
-        const int t = targets[i];
-        pos[i] = o;
-        tg[o] = t - vocab_start;  // row of the weight this call reads
-        bad |= (t < 0 || t >= V);
-      } else {
-        pos[i] = -2 - o;
-        tg[o] = -1;
-      }
-      ++o;
+// Kept-row bits of this thread's 16 rows starting at r0 (bit j: row r0 + j),
+// and whether each row is listed: with block = 256 the 16 threads of a block
+// (16 adjacent lanes) combine their bits.
+__device__ __forceinline__ void compact_bits(const uint8_t* __restrict__ keep, int N, int r0,
+                                             int block, uint32_t& kept, uint32_t& listed) {
+  kept = 0;
+  uint32_t valid = 0;
+#pragma unroll
+  for (int j = 0; j < kCompactPerThread; ++j) {
+    const int i = r0 + j;
+    if (i < N) {
+      valid |= 1u << j;
+      if (keep == nullptr || keep[i] != 0) kept |= 1u << j;
     }
   }
-  // compact targets past the listed rows: -1 matches no vocabulary row
-  for (int c = scan[kCompactThreads - 1] + tid; c < tg_rows; c += kCompactThreads) tg[c] = -1;
+  listed = kept;
+  if (block > 1) {
+    int any = kept != 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) any |= __shfl_xor(any, d, 16);
+    listed = any ? valid : 0u;
+  }
+}
+
+// Exclusive prefix sum over a workgroup of kCompactThreads threads.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kCompactThreads; off <<= 1) {
+    const int u = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += u;
+    __syncthreads();
+  }
+  const int incl = sh[tid];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kCompactThreads) void k_compact_count(
+    const uint8_t* __restrict__ keep, const int32_t* __restrict__ targets, int N, int V,
+    int block, int* __restrict__ scratch, int nchunks) {
+  __shared__ int sh[kCompactThreads];
+  const int r0 = blockIdx.x * kCompactRows + threadIdx.x * kCompactPerThread;
+  uint32_t kept, listed;
+  compact_bits(keep, N, r0, block, kept, listed);
+  int bad = 0;
+  for (uint32_t k = kept; k; k &= k - 1) {
+    const int t = targets[r0 + __builtin_ctz(k)];
+    bad |= (t < 0 || t >= V);
+  }
+  const int cnt = __builtin_popcount(listed);
+  const int before = wg_exclusive_scan(cnt, sh);
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == kCompactThreads - 1) {
+    scratch[blockIdx.x] = before + cnt;
+    scratch[nchunks + blockIdx.x] = bad;
+  }
+}
+
+// One workgroup: per-chunk counts -> exclusive offsets (in place), and the
+// saved header.
+__global__ __launch_bounds__(kScanThreads) void k_compact_scan(int* __restrict__ scratch,
+                                                               int nchunks, int N, int H, int V,
+                                                               int flags,
+                                                               SavedHeader* __restrict__ hdr) {
+  __shared__ int sh[kScanThreads];
+  const int tid = threadIdx.x;
+  const int seg = (nchunks + kScanThreads - 1) / kScanThreads;
+  const int beg = min(nchunks, tid * seg), end = min(nchunks, beg + seg);
+  int sum = 0, bad = 0;
+  for (int b = beg; b < end; ++b) {
+    sum += scratch[b];
+    bad |= scratch[nchunks + b];
+  }
+  sh[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int u = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += u;
+    __syncthreads();
+  }
+  int o = sh[tid] - sum;
+  for (int b = beg; b < end; ++b) {
+    const int c = scratch[b];
+    scratch[b] = o;
+    o += c;
+  }
   bad = __syncthreads_or(bad);
   if (tid == 0) {
-    hdr->n_kept = scan[kCompactThreads - 1];
+    hdr->n_kept = sh[kScanThreads - 1];
     hdr->status = bad ? LMHEAD_ERR_TARGET_RANGE : LMHEAD_OK;
     hdr->N = N;
     hdr->H = H;
     hdr->V = V;
     hdr->flags = flags;
   }
+}
+
+__global__ __launch_bounds__(kCompactThreads) void k_compact_write(
+    const uint8_t* __restrict__ keep, const int32_t* __restrict__ targets, int N, int block,
+    const int* __restrict__ scratch, const SavedHeader* __restrict__ hdr,
+    int32_t* __restrict__ kept_idx, int32_t* __restrict__ pos, int32_t* __restrict__ tg,
+    int tg_rows, int vocab_start) {
+  __shared__ int sh[kCompactThreads];
+  const int r0 = blockIdx.x * kCompactRows + threadIdx.x * kCompactPerThread;
+  uint32_t kept, listed;
+  compact_bits(keep, N, r0, block, kept, listed);
+  int o = scratch[blockIdx.x] + wg_exclusive_scan(__builtin_popcount(listed), sh);
+#pragma unroll
+  for (int j = 0; j < kCompactPerThread; ++j) {
+    const int i = r0 + j;
+    if (i >= N) break;
+    if (!((listed >> j) & 1u)) {
+      pos[i] = -1;
+      continue;
+    }
+    kept_idx[o] = i;
+    if ((kept >> j) & 1u) {
+      pos[i] = o;
+      tg[o] = targets[i] - vocab_start;  // row of the weight this call reads
+    } else {
+      pos[i] = -2 - o;
+      tg[o] = -1;
+    }
+    ++o;
+  }
+  // compact targets past the listed rows: -1 matches no vocabulary row; this
+  // workgroup fills its share of [n_kept, tg_rows)
+  const int total = hdr->n_kept;
+  const int c0 = total + blockIdx.x * kCompactRows;
+  for (int c = c0 + threadIdx.x; c < min(tg_rows, c0 + kCompactRows); c += kCompactThreads)
+    tg[c] = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -1121,10 +1202,18 @@ static int fwd_impl(const void* hidden, const void* weight, const int32_t* targe
   SavedView sv = saved_view(saved, N);
   char* w = static_cast<char*>(workspace);
   int32_t* tg = reinterpret_cast<int32_t*>(w + L.tg);
-  LMH_TRY(launch(KK_COMPACT, k_compact, dim3(1), dim3(kCompactThreads), s, keep_mask, targets,
-                 (int)N, (int)H, (int)V_total, flags, block, sv.kept_idx, sv.pos, sv.hdr, tg,
-                 (int)tile_rows(N), (int)vocab_start));
+  // the target-logit array is the compaction's scratch until the projection writes it
+  int* cscratch = reinterpret_cast<int*>(w + L.zt);
+  const int nch = compact_chunks(N);
+  if (nch > 0)
+    LMH_TRY(launch(KK_COMPACT, k_compact_count, dim3(nch), dim3(kCompactThreads), s, keep_mask,
+                   targets, (int)N, (int)V_total, block, cscratch, nch));
+  LMH_TRY(launch(KK_COMPACT, k_compact_scan, dim3(1), dim3(kScanThreads), s, cscratch, nch,
+                 (int)N, (int)H, (int)V_total, flags, sv.hdr));
   if (N == 0) return LMHEAD_OK;
+  LMH_TRY(launch(KK_COMPACT, k_compact_write, dim3(nch), dim3(kCompactThreads), s, keep_mask,
+                 targets, (int)N, block, (const int*)cscratch, (const SavedHeader*)sv.hdr,
+                 sv.kept_idx, sv.pos, tg, (int)tile_rows(N), (int)vocab_start));
 
   const int nv = n_vtiles(V);
   const int64_t ldc = ldc_of(N);
