@@ -85,13 +85,18 @@ size_t lmhead_saved_bytes(int64_t N);
  * ([H][N rounded up to 64]). Returns 0 on invalid sizes. */
 size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V);
 
-/* Workspace bytes lmhead_bwd needs: 24 tile-queue counters per token chunk,
+/* Workspace bytes lmhead_bwd needs: 32 tile-queue counters per token chunk,
  * 20 bytes per kept row (N rounded up to 256 entries) of logit-gradient
  * coefficients and targets, a bf16 transposed copy of the kept rows of X
- * ([H][N rounded up to 64]) and
- * the bf16 logit gradient dZ of one chunk
+ * ([H][N rounded up to 64]), the bf16 logit gradient dZ of one chunk
  * of C rows ([C][V rounded up to 256], token-major), where C = token_chunk
- * rounded up to a multiple of 256 (at most N rounded up to 256).
+ * rounded up to a multiple of 256 (at most N rounded up to 256), and, for
+ * V >= 16384, fp32 partial dX tiles: when the dX tiles of a chunk past its
+ * last whole round of workgroups number at most 256 (S - 1) / S, each is
+ * computed as S pieces of the vocabulary range that the whole device runs,
+ * then summed in a fixed order; S = 8 when 8 pieces of a multiple of 64
+ * vocabulary rows fit in V rounded up to 256, else 4
+ * (min(256 (S - 1) / S, C / 256 * ceil(H / 256)) * S tiles of 256 x 256).
  * token_chunk <= 0 selects the largest chunk whose dZ fits 8 GiB (prime-rl PR
  * #3326, Overview, uses the chunk to bound memory; its default of 8192 rows
  * was set for a smaller memory). Returns 0 on invalid sizes. */
@@ -132,11 +137,12 @@ int lmhead_fwd(const void* hidden, const void* weight, const int32_t* targets,
  * forward and backward that skip inactive tiles). Every row of a tile that
  * holds a kept row runs through the projection. Rows that are not kept still
  * get +0.0 log-prob and entropy, and lmhead_bwd gives them an all-zero logit
- * gradient: a +0.0 dX row and no dW contribution. Per row, log-prob, entropy
- * and dX equal those of lmhead_fwd + lmhead_bwd bit for bit, because a row's
- * results do not depend on which other rows share its tile. dW sums the same
- * rows with zero rows between them, in a different order, so it agrees to
- * rounding. The saved header counts the listed rows as n_kept (what
+ * gradient: a +0.0 dX row and no dW contribution. Per row, log-prob and
+ * entropy equal those of lmhead_fwd bit for bit, because a row's results do
+ * not depend on which other rows share its tile; so does dX unless the two
+ * row counts split the dX tail differently (see lmhead_bwd_workspace_bytes),
+ * when it agrees to rounding. dW sums the same rows with zero rows between
+ * them, in a different order, so it agrees to rounding. The saved header counts the listed rows as n_kept (what
  * lmhead_read_n_kept reports) and sets bit 2 of its flags. Take the
  * backward with lmhead_bwd. Same errors as lmhead_fwd. */
 int lmhead_fwd_blocksparse(const void* hidden, const void* weight, const int32_t* targets,
@@ -300,8 +306,8 @@ int lmhead_version(void);
 /* Per-kernel timing for benchmarks (not needed to use the op).
  * Kernel kinds, in order: compact, gather_cols, fwd_tiles, merge,
  * zero_skipped, zero_rows, dz_tiles, dx_tiles, dw_tiles, zero_queues,
- * bwd_rows, merge_shards. */
-#define LMHEAD_NUM_KERNELS 12
+ * bwd_rows, merge_shards, dx_reduce. */
+#define LMHEAD_NUM_KERNELS 13
 
 /* Static name of kernel kind `kind` (NULL if out of range). */
 const char* lmhead_kernel_name(int kind);

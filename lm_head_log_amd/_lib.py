@@ -49,7 +49,7 @@ SIGNATURES = {
                                   ctypes.POINTER(ctypes.c_double), c_vp]),
 }
 
-NUM_KERNELS = 12
+NUM_KERNELS = 13
 
 _lib = None
 

@@ -145,24 +145,54 @@ static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
   return g;
 }
 
-// Backward workspace: tile-queue counters (three GEMMs per chunk) | per-row
+// dX tail split. The dX GEMM of a chunk has ceil(rows / 256) x ceil(H / 256)
+// tiles of K = V, each a long run (2.8 ms at V = 131072). When the tiles past
+// the last whole round of the grid -- the tail -- number at most
+// 256 (S - 1) / S, each tail tile is cut into S pieces of the K range, which
+// the whole chip runs, and a fixed-order sum of the pieces writes the tile:
+// 672 tiles on 256 CUs take 2.625 tile times instead of 3. Only for
+// V >= kDxSplitMinV, where a piece is long enough to pay for its prologue and
+// epilogue. Pieces are kp = a multiple of 64 vocabulary rows, with S kp within
+// the dZ row pitch (V rounded up to 256) so that no piece reads past its
+// row: S = 8 where that holds, else 4 (the pitch is a multiple of 4 x 64).
+constexpr int64_t kDxSplitMinV = 16384;
+static inline int64_t dz_pitch(int64_t V) { return round_up(V, 256); }
+static inline int dx_piece_k_for(int64_t V, int S) { return (int)round_up((V + S - 1) / S, 64); }
+static inline int dx_pieces(int64_t V) {
+  if (V < kDxSplitMinV) return 1;
+  return 8 * (int64_t)dx_piece_k_for(V, 8) <= dz_pitch(V) ? 8 : 4;
+}
+static inline int dx_piece_k(int64_t V) { return dx_piece_k_for(V, dx_pieces(V)); }
+static inline int64_t dx_tiles_per_chunk(int64_t C, int64_t H) {
+  return (C / kBM) * ((H + kBN - 1) / kBN);
+}
+static inline int dx_tail_max(int64_t C, int64_t H, int64_t V) {
+  const int S = dx_pieces(V);
+  if (S == 1) return 0;
+  return (int)std::min<int64_t>(256 * (S - 1) / S, dx_tiles_per_chunk(C, H));
+}
+
+// Backward workspace: tile-queue counters (four launches per chunk) | per-row
 // dZ coefficients (float4) and compact targets [tile_rows] | X_c^T [H][ldc] |
-// dZ [C][ldz], both bf16.
+// dZ [C][ldz], both bf16 | fp32 partial dX tiles of a split tail
+// [tail max x pieces][256][256].
+constexpr int kBwdQueueSets = 4;  // dz, dx, dx pieces, dw
 struct BwdWs {
-  size_t q, rc, tg, xct, dz, total;
+  size_t q, rc, tg, xct, dz, part, total;
   int64_t nq;  // counters
 };
 static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
   const BwdGeom g = bwd_geom(N, V, token_chunk);
   BwdWs w;
   const int64_t nchunks = N > 0 ? (N + g.C - 1) / g.C : 1;
-  w.nq = nchunks * 3 * kQueueInts;
+  w.nq = nchunks * kBwdQueueSets * kQueueInts;
   w.q = 0;
   w.rc = w.q + align256((size_t)w.nq * 4);
   w.tg = w.rc + align256((size_t)tile_rows(N) * 16);
   w.xct = w.tg + align256((size_t)tile_rows(N) * 4);
   w.dz = w.xct + align256((size_t)H * (size_t)ldc_of(N) * 2);
-  w.total = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
+  w.part = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
+  w.total = w.part + (size_t)dx_tail_max(g.C, H, V) * dx_pieces(V) * kBM * kBN * 4;
   return w;
 }
 
@@ -873,7 +903,29 @@ struct DxParams {
   float* dX;
   int* queue;  // tile-queue counters of this launch (zero before it)
   int steal;
+  // tail split (see kDxPieces)
+  int G;       // grid of the whole-tile launch: its tiles past the last whole round are the tail
+  int S;       // pieces per split tail tile (1: never split)
+  int rmax;    // largest tail that is split; `part` holds rmax * S tiles
+  int kp;      // vocabulary rows per piece, a multiple of 64
+  int pieces;  // 0: the whole tiles (and an unsplit tail), 1: the pieces of a split tail
+  float* part;  // [rmax * S][256][256] partial tiles, piece p of tail tile r at p * R + r
 };
+
+// The tail of a dX launch, from the kept-row count on the device.
+struct DxTail {
+  int T, R, full;
+  bool split;
+};
+__device__ __forceinline__ DxTail dx_tail(const DxParams& P, int rows) {
+  DxTail d;
+  const int mt = (rows + kBM - 1) / kBM;
+  d.T = mt * ((P.H + kBN - 1) / kBN);
+  d.R = d.T % P.G;
+  d.split = P.S > 1 && d.R > 0 && d.R <= P.rmax;
+  d.full = d.split ? d.T - d.R : d.T;
+  return d;
+}
 
 template <int SHIFT>
 __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
@@ -884,24 +936,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   if (rows <= 0) return;
   const int mt = (rows + kBM - 1) / kBM;
   const int nt = (P.H + kBN - 1) / kBN;
-  const int ntiles = mt * nt;
+  const DxTail tail = dx_tail(P, rows);
+  // whole tiles, or the S pieces of each split tail tile (unit u: piece u / R
+  // of tail tile u % R, so concurrent pieces share their K range)
+  const int nunits = P.pieces ? (tail.split ? tail.R * P.S : 0) : tail.full;
+  if (nunits == 0) return;
   const int tid = threadIdx.x;
-  const int nk = (P.V + kBK - 1) / kBK;  // W reads zero past V
+  const int nk = P.pieces ? P.kp / kBK : (P.V + kBK - 1) / kBK;  // W reads zero past V
   const int32_t* kidx = P.sv.kept_idx + P.c0;
 
-  TileQueue q(P.queue, ntiles, P.steal);
+  TileQueue q(P.queue, nunits, P.steal);
   for (;;) {
     // B slot 3 is free here: this wave's loads into it are done, and the
     // next tile's loads write it only after its first barrier
-    const int t = q.next(rb3);
-    if (t < 0) break;
+    const int u = q.next(rb3);
+    if (u < 0) break;
+    int t = u, k0 = 0;
+    if (P.pieces) {
+      t = tail.full + u % tail.R;
+      k0 = (u / tail.R) * P.kp;
+    }
     int tm, tn;
     tile_coords<LMH_GM_DX>(t, mt, nt, tm, tn);
 
     ASrc A;
     BSrc B;
-    A.init(P.dZ + (int64_t)tm * kBM * P.ldz, P.ldz, rows - tm * kBM);
-    B.init(P.W + (int64_t)tn * kBN, P.H, P.V, P.H - tn * kBN);
+    // a piece reads dZ columns and W rows [k0, k0 + kp): W rows at or past V
+    // read as zero, so dZ entries past V (finite) add nothing
+    A.init(P.dZ + (int64_t)tm * kBM * P.ldz + k0, P.ldz, rows - tm * kBM);
+    B.init(P.W + (int64_t)k0 * P.H + (int64_t)tn * kBN, P.H,
+           P.pieces ? min(P.kp, P.V - k0) : P.V, P.H - tn * kBN);
     f32x16_t acc[4][4];
     mainloop<SHIFT>(A, B, nk, ring, acc);
     q.claim_ahead();
@@ -938,16 +1002,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
       __builtin_amdgcn_sched_barrier(0);
       const int q = lane & 31;  // 16-byte chunk of the row
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int t = 2 * u + (lane >> 5);
+      for (int uu = 0; uu < 16; ++uu) {
+        const int t = 2 * uu + (lane >> 5);
         const int m = m0 + i * 32 + t;
         const int h = n0 + q * 4;
         const float4 x = *reinterpret_cast<const float4*>(stage + t * 128 + ((q ^ (t & 31)) << 2));
-        if (m < rows && h < P.H)  // H is a multiple of 4: a chunk is whole
+        if (P.pieces)  // the whole partial tile, row-major
+          *reinterpret_cast<float4*>(P.part + (int64_t)u * (kBM * kBN) +
+                                     (m - tm * kBM) * kBN + (h - tn * kBN)) = x;
+        else if (m < rows && h < P.H)  // H is a multiple of 4: a chunk is whole
           *reinterpret_cast<float4*>(P.dX + (int64_t)kidx[m] * P.H + h) = x;
       }
     }
   }
+}
+
+// The split tail's dX tiles: the S partial tiles of each are summed in piece
+// order (a fixed order, so results are reproducible) and scattered to the
+// rows' original positions. One thread per 16-byte chunk of a tile row.
+__global__ __launch_bounds__(256) void k_dx_reduce(DxParams P) {
+  const int n_kept = P.sv.hdr->n_kept;
+  const int rows = min(P.C, n_kept - P.c0);
+  if (rows <= 0) return;
+  const DxTail tail = dx_tail(P, rows);
+  if (!tail.split) return;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int kChunks = kBN / 4;
+  if (idx >= (int64_t)tail.R * kBM * kChunks) return;
+  const int r = (int)(idx / (kBM * kChunks));
+  const int e = (int)(idx % (kBM * kChunks));
+  const int row = e / kChunks, q = e % kChunks;
+  int tm, tn;
+  tile_coords<LMH_GM_DX>(tail.full + r, (rows + kBM - 1) / kBM, (P.H + kBN - 1) / kBN, tm, tn);
+  const int m = tm * kBM + row, h = tn * kBN + q * 4;
+  if (m >= rows || h >= P.H) return;
+  const float* src = P.part + (int64_t)r * (kBM * kBN) + row * kBN + q * 4;
+  float4 acc = *reinterpret_cast<const float4*>(src);
+  for (int p = 1; p < P.S; ++p) {
+    const float4 x = *reinterpret_cast<const float4*>(src + (int64_t)p * tail.R * (kBM * kBN));
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  *reinterpret_cast<float4*>(P.dX + (int64_t)P.sv.kept_idx[P.c0 + m] * P.H + h) = acc;
 }
 
 // dW^T (+)= X_c^T dZ: M = H (A = X_c^T rows), N = vocab (B = dZ: k = chunk
@@ -1098,12 +1196,12 @@ static int check_sizes(int64_t N, int64_t H, int64_t V) {
 // the launch stream around every launch while profiling is on.
 enum KernelKind {
   KK_COMPACT = 0, KK_GATHER_COLS, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS,
-  KK_DZ, KK_DX, KK_DW, KK_ZERO_QUEUES, KK_BWD_ROWS, KK_MERGE_SHARDS, KK_COUNT
+  KK_DZ, KK_DX, KK_DW, KK_ZERO_QUEUES, KK_BWD_ROWS, KK_MERGE_SHARDS, KK_DX_REDUCE, KK_COUNT
 };
 static const char* const kKernelNames[KK_COUNT] = {
     "compact",   "gather_cols", "fwd_tiles", "merge",    "zero_skipped",
     "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles", "zero_queues", "bwd_rows",
-    "merge_shards"};
+    "merge_shards", "dx_reduce"};
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -1407,7 +1505,7 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
       D.dZ = dZ;
       const int64_t dz_tiles = (int64_t)nv * (G.C / kBN);
       const int dz_grid = persistent_grid(dz_tiles);
-      D.queue = queues + (ch * 3 + 0) * kQueueInts;
+      D.queue = queues + (ch * kBwdQueueSets + 0) * kQueueInts;
       D.steal = steal_for(dz_tiles, dz_grid);
       LMH_TRY(launch_shifted(KK_DZ, stage_shift((int)(H / kBK)), dim3(dz_grid), s, D,
                              k_dz_tiles<0>, k_dz_tiles<2>, k_dz_tiles<4>, k_dz_tiles<6>,
@@ -1423,13 +1521,33 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
       X2.c0 = c0;
       X2.C = (int)G.C;
       X2.dX = grad_hidden;
-      const int64_t dx_tiles = (G.C / kBM) * ((H + kBN - 1) / kBN);
+      const int64_t dx_tiles = dx_tiles_per_chunk(G.C, H);
       const int dx_grid = persistent_grid(dx_tiles);
-      X2.queue = queues + (ch * 3 + 1) * kQueueInts;
+      X2.queue = queues + (ch * kBwdQueueSets + 1) * kQueueInts;
       X2.steal = steal_for(dx_tiles, dx_grid);
+      X2.G = dx_grid;
+      X2.S = dx_pieces(V);
+      X2.rmax = dx_tail_max(G.C, H, V);
+      X2.kp = dx_piece_k(V);
+      X2.part = reinterpret_cast<float*>(w + L.part);
+      X2.pieces = 0;
       LMH_TRY(launch_shifted(KK_DX, shift_for((int)((V + kBK - 1) / kBK)), dim3(dx_grid), s, X2,
                              k_dx_tiles<0>, k_dx_tiles<2>, k_dx_tiles<4>, k_dx_tiles<6>,
                              k_dx_tiles<8>, k_dx_tiles<10>));
+      if (X2.S > 1) {
+        // the pieces of a split tail, then their sum; both exit at once when
+        // the kept rows leave no tail to split (decided on the device)
+        X2.pieces = 1;
+        const int64_t units = (int64_t)X2.rmax * X2.S;
+        const int pgrid = persistent_grid(units);
+        X2.queue = queues + (ch * kBwdQueueSets + 2) * kQueueInts;
+        X2.steal = steal_for(units, pgrid);
+        LMH_TRY(launch_shifted(KK_DX, shift_for(X2.kp / kBK), dim3(pgrid), s, X2, k_dx_tiles<0>,
+                               k_dx_tiles<2>, k_dx_tiles<4>, k_dx_tiles<6>, k_dx_tiles<8>,
+                               k_dx_tiles<10>));
+        LMH_TRY(launch(KK_DX_REDUCE, k_dx_reduce, dim3((unsigned)(X2.rmax * (kBM * kBN / 4) / 256)),
+                       dim3(256), s, X2));
+      }
     }
     DwParams Wp;
     Wp.XcT = XcT;
@@ -1445,7 +1563,7 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
     Wp.dW = grad_weight;
     const int64_t dw_tiles = (int64_t)nv * ((H + kBN - 1) / kBN);
     const int dw_grid = persistent_grid(dw_tiles);
-    Wp.queue = queues + (ch * 3 + 2) * kQueueInts;
+    Wp.queue = queues + (ch * kBwdQueueSets + 3) * kQueueInts;
     Wp.steal = steal_for(dw_tiles, dw_grid);
     // the shift of a full chunk; a shorter last chunk runs a few padding
     // stages, which read zeros

@@ -92,13 +92,20 @@ def _bwd_ws(N, H, V, chunk):
     C = min(up(want, 256), up(N, 256)) if N > 0 else 0
     nchunks = (N + C - 1) // C if N > 0 else 1
     rows = up(N, 256)
-    return (_align(nchunks * 3 * 32) + _align(16 * rows) + _align(4 * rows)
-            + _align(H * up(N, 64) * 2) + _align(C * up(V, 256) * 2))
+    # partial dX tiles of a split tail: S pieces of each of at most 256 (S - 1) / S
+    # tiles; S = 8 when 8 pieces of a multiple of 64 rows fit in V rounded to 256
+    pieces = 1
+    if V >= 16384:
+        pieces = 8 if 8 * up(-(-V // 8), 64) <= up(V, 256) else 4
+    tail = min(256 * (pieces - 1) // pieces, C // 256 * up(H, 256) // 256) if pieces > 1 else 0
+    return (_align(nchunks * 4 * 32) + _align(16 * rows) + _align(4 * rows)
+            + _align(H * up(N, 64) * 2) + _align(C * up(V, 256) * 2)
+            + tail * pieces * 256 * 256 * 4)
 
 
 def test_workspace_sizes(lib):
     for (N, H, V) in ((16384, 4096, 131072), (128, 512, 8192), (10, 64, 1000), (0, 64, 5),
-                      (262144, 5120, 152064)):
+                      (262144, 5120, 152064), (700, 256, 20000), (16384, 2560, 151936)):
         assert lib.lmhead_fwd_workspace_bytes(N, H, V) == _fwd_ws(N, H, V)
         for chunk in (0, 100, 256, 8192, 1 << 20):
             assert lib.lmhead_bwd_workspace_bytes(N, H, V, chunk) == _bwd_ws(N, H, V, chunk)
@@ -107,7 +114,7 @@ def test_workspace_sizes(lib):
     N, H, V = 16384, 4096, 131072
     assert _bwd_ws(N, H, V, 0) == _bwd_ws(N, H, V, 16384)
     # the 4096-row chunking has four chunks' tile-queue counters instead of one
-    queues = _align(4 * 3 * 32) - _align(1 * 3 * 32)
+    queues = _align(4 * 4 * 32) - _align(1 * 4 * 32)
     assert _bwd_ws(N, H, V, 0) - _bwd_ws(N, H, V, 4096) == (16384 - 4096) * V * 2 - queues
     assert _bwd_ws(262144, 4096, 152064, 0) == _bwd_ws(262144, 4096, 152064, 28160)
     # invalid sizes

@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import lm_head_log_amd as lmh
 import oracle
 import workloads as wl
 from tests.gpu_helpers import (TOL_ENT, TOL_GRAD_REL, TOL_LOGP, assert_pos_zero, rel_fro,
@@ -25,8 +26,10 @@ pytestmark = pytest.mark.gpu
 SAMPLE = 512
 
 
-def _full_check(w, sample_seed, backward=True):
+def _full_check(w, sample_seed, backward=True, blocksparse=False):
     g = run(w, backward=backward)
+    if blocksparse:
+        _blocksparse_check(w, g)
     kept = w.kept_rows()
     np.testing.assert_array_equal(g["kept_idx"], kept)
     assert g["status"] == 0
@@ -81,6 +84,23 @@ def test_config4_fp32_stress():
     _full_check(wl.config4(), 4)
 
 
+def _blocksparse_check(w, g):
+    """The block-sparse forward on the same batch: it runs every row of each
+    256-row tile with a kept row (checked bit-exact), and its log-prob and
+    entropy equal the compacting forward's bit for bit."""
+    gb = run(w, backward=False, fwd=lmh.lmhead_fwd_blocksparse)
+    tiles = np.flatnonzero(np.add.reduceat(w.keep.astype(np.int64), np.arange(0, w.N, 256)) > 0)
+    listed = (tiles[:, None] * 256 + np.arange(256)[None, :]).ravel()
+    listed = listed[listed < w.N].astype(np.int32)
+    say(f"{w.name}: block-sparse runs {listed.size} rows for {int(w.keep.sum())} kept")
+    np.testing.assert_array_equal(gb["kept_idx"], listed)
+    assert gb["status"] == 0
+    np.testing.assert_array_equal(gb["logp"].view(np.uint32), g["logp"].view(np.uint32))
+    np.testing.assert_array_equal(gb["entropy"].view(np.uint32), g["entropy"].view(np.uint32))
+    del gb
+    gc.collect()
+
+
 def test_config5_scoring_forward():
-    say("case: config5 scoring N262144 H5120 V152064 forward only")
-    _full_check(wl.config5(), 5, backward=False)
+    say("case: config5 scoring N262144 H5120 V152064 forward only, compacting and block-sparse")
+    _full_check(wl.config5(), 5, backward=False, blocksparse=True)

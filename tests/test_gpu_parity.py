@@ -244,3 +244,22 @@ def test_autograd_wrapper_matches_the_c_calls():
     # metric-only entropy carries no gradient
     lp2, ent2 = lmh.fused_logprobs(Xr, Wr, t.reshape(2, 96), return_entropy=True)
     assert not ent2.requires_grad and lp2.requires_grad
+
+
+@pytest.mark.parametrize("N,H,V,chunk,seed", [
+    (600, 512, 16384, 0, 51),    # 6 dX tiles on a grid of 8: all split, 8 pieces each
+    (700, 256, 20000, 256, 52),  # 4 pieces (8 would overrun the dZ row); 3 chunks, each split
+    (300, 192, 131072, 0, 53),   # the bench vocabulary: pieces of 16384 rows, ragged H
+])
+def test_dx_tail_split(N, H, V, chunk, seed):
+    """dX tiles past the last whole round of the grid are computed as pieces of
+    the vocabulary range and summed in a fixed order: same bar against the
+    oracle, and bitwise reproducible."""
+    say(f"case: dX tail split N{N} H{H} V{V} chunk {chunk}")
+    w = wl.small(N, H, V, seed=seed, keep_fraction=0.9)
+    g = run(w, token_chunk=chunk)
+    errs = check_against_oracle(w, g, what=f"dX split N{N} H{H} V{V}")
+    say(f"dX split errors {errs}")
+    g2 = run(w, token_chunk=chunk)
+    np.testing.assert_array_equal(g2["dX"].view(np.uint32), g["dX"].view(np.uint32))
+    np.testing.assert_array_equal(g2["dW"].view(np.uint32), g["dW"].view(np.uint32))
