@@ -47,10 +47,13 @@ def _masks(N):
     }
 
 
-@pytest.mark.parametrize("kind", ["spans", "sparse", "last_row_only", "none_kept", "bernoulli",
-                                  "null"])
-def test_blocksparse_matches_compaction_and_oracle(kind):
-    N, H, V = 5000, 256, 3000
+@pytest.mark.parametrize("kind,N,H,V", [
+    ("spans", 5000, 256, 3000), ("sparse", 5000, 256, 3000), ("last_row_only", 5000, 256, 3000),
+    ("none_kept", 5000, 256, 3000), ("bernoulli", 5000, 256, 3000), ("null", 5000, 256, 3000),
+    # V >= 16384: both row lists leave every dX tile in the split tail (all pieces)
+    ("spans", 1100, 256, 16384),
+])
+def test_blocksparse_matches_compaction_and_oracle(kind, N, H, V):
     say(f"case: block-sparse N{N} H{H} V{V} mask {kind}")
     w = wl.small(N, H, V, seed=43)
     keep = None if kind == "null" else _masks(N)[kind]
