@@ -254,7 +254,12 @@ def blocksparse_leg(lmh, stream, dev, steps):
     saved = torch.empty(lmh.lmhead_saved_bytes(N), dtype=torch.uint8, device=dev)
     ws = torch.empty(lmh.lmhead_fwd_workspace_bytes(N, H, V), dtype=torch.uint8, device=dev)
     out = {"workload": f"scoring N{N} H{H} V{V}, keep in spans of 64-2048 tokens, forward only",
-           "n_kept": n_kept, "steps": steps}
+           "n_kept": n_kept, "steps": steps,
+           # every device buffer of this leg (the op allocates nothing itself)
+           # against the fp32 logits a materialising forward would hold
+           "device_bytes": sum(x.numel() * x.element_size()
+                               for x in (X, W, t, km, lp, ent, saved, ws)),
+           "fp32_logits_bytes": N * V * 4}
     for name, fn in (("compact", lmh.lmhead_fwd), ("block_sparse", lmh.lmhead_fwd_blocksparse)):
         def call():
             fn(X, W, t, km, True, False, logp=lp, entropy=ent, saved=saved, workspace=ws,

@@ -104,3 +104,26 @@ def _blocksparse_check(w, g):
 def test_config5_scoring_forward():
     say("case: config5 scoring N262144 H5120 V152064 forward only, compacting and block-sparse")
     _full_check(wl.config5(), 5, backward=False, blocksparse=True)
+
+
+def test_compaction_many_chunks():
+    """More than 1024 chunks of 4096 rows, so every thread of the scan owns
+    several chunks: kept positions and the block-sparse listing bit-exact, a
+    sample of rows against the oracle, +0.0 at skipped rows."""
+    N, H, V = (1024 + 7) * 4096 + 123, 64, 300
+    say(f"case: compaction over {N} rows ({(N + 4095) // 4096} chunks)")
+    w = wl.small(N, H, V, seed=61, keep_fraction=0.4)
+    w.keep[:300000] = 0            # whole 256-row tiles with no kept row
+    w.keep[-5000:] = 0
+    g = run(w, backward=False)
+    kept = w.kept_rows()
+    np.testing.assert_array_equal(g["kept_idx"], kept)
+    assert g["n_kept"] == kept.size and g["status"] == 0
+    skipped = np.setdiff1d(np.arange(N), kept)
+    assert_pos_zero(g["logp"][skipped], "logp skipped")
+    rows = wl.sample_rows(kept, 256, 62)
+    ref = oracle.rows_fwd_bwd(w.hidden, w.weight, w.targets, rows, w.g_logp, w.g_entropy,
+                              False, want_dw=False)
+    assert np.abs(g["logp"][rows] - ref["logp"]).max() <= TOL_LOGP
+    assert np.abs(g["entropy"][rows] - ref["entropy"]).max() <= TOL_ENT
+    _blocksparse_check(w, g)
