@@ -263,3 +263,15 @@ def test_dx_tail_split(N, H, V, chunk, seed):
     g2 = run(w, token_chunk=chunk)
     np.testing.assert_array_equal(g2["dX"].view(np.uint32), g["dX"].view(np.uint32))
     np.testing.assert_array_equal(g2["dW"].view(np.uint32), g["dW"].view(np.uint32))
+
+
+@pytest.mark.parametrize("N,H,V,seed", [
+    (64, 64, 1 << 22, 71),    # the largest vocabulary the library takes (16384 vocab tiles; dX split)
+    (40, 1 << 20, 300, 72),   # the largest hidden size (32768 k stages per tile)
+])
+def test_maximum_sizes(N, H, V, seed):
+    say(f"case: maximum size N{N} H{H} V{V}")
+    w = wl.small(N, H, V, seed=seed, keep_fraction=0.7)
+    g = run(w)
+    errs = check_against_oracle(w, g, what=f"max N{N} H{H} V{V}")
+    say(f"maximum size errors {errs}")
