@@ -262,8 +262,10 @@ struct BSrc {
 constexpr int kXcds = 8;
 // Group widths (m-tiles per group) of each GEMM; a group is swept with m
 // fastest, so an XCD's 32 concurrent tiles cover gm m-tiles by 32 / gm n-tiles
-// and read gm + 32 / gm operand panels (12 for gm = 8, the fewest). Timed at
-// N=16384 H=4096 V=131072 on random operands, 4 and 8 tie and 16 is slower.
+// and read gm + 32 / gm operand panels (12 for gm = 4 or 8, the fewest). Timed
+// per GEMM with widths 4, 8 and 16 on three batches (N 16384 with H 4096 /
+// V 131072, H 4096 / V 151936 and H 2560 / V 151936): 16 is slower for every
+// GEMM; 8 is best or tied for fwd, dz and dW; dX is 0.4-1.1 % faster with 4.
 #ifndef LMH_GM_FWD
 #define LMH_GM_FWD 8
 #endif
@@ -271,7 +273,7 @@ constexpr int kXcds = 8;
 #define LMH_GM_DZ 8
 #endif
 #ifndef LMH_GM_DX
-#define LMH_GM_DX 8
+#define LMH_GM_DX 4
 #endif
 #ifndef LMH_GM_DW
 #define LMH_GM_DW 8
