@@ -128,12 +128,12 @@ FAKE = ctypes.c_void_p(0x10000)   # 16-byte aligned, never dereferenced
 ODD = ctypes.c_void_p(0x10002)
 
 
-def _fwd(lib, **kw):
+def _fwd(lib, entry="lmhead_fwd", **kw):
     a = dict(hidden=FAKE, weight=FAKE, targets=FAKE, keep=None, N=8, H=64, V=100,
              ret=1, erg=1, logp=FAKE, ent=FAKE, saved=FAKE, saved_bytes=1 << 20,
              ws=FAKE, ws_bytes=1 << 30, stream=None)
     a.update(kw)
-    return lib.lmhead_fwd(a["hidden"], a["weight"], a["targets"], a["keep"], a["N"], a["H"],
+    return getattr(lib, entry)(a["hidden"], a["weight"], a["targets"], a["keep"], a["N"], a["H"],
                           a["V"], a["ret"], a["erg"], a["logp"], a["ent"], a["saved"],
                           a["saved_bytes"], a["ws"], a["ws_bytes"], a["stream"])
 
@@ -169,6 +169,8 @@ def _bwd(lib, **kw):
 ])
 def test_fwd_host_validation(lib, kw, code):
     assert _fwd(lib, **kw) == code
+    # the block-sparse forward takes the same arguments and checks them the same way
+    assert _fwd(lib, entry="lmhead_fwd_blocksparse", **kw) == code
 
 
 @pytest.mark.parametrize("kw,code", [
