@@ -407,9 +407,10 @@ def lmhead_mfma_probe(a=None, b=None, iters=40000, *, workspace=None, stream=Non
 class _FusedLMHead(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, targets, keep_mask, return_entropy, entropy_requires_grad,
-                token_chunk):
-        logp, ent, saved = lmhead_fwd(hidden, weight, targets, keep_mask, return_entropy,
-                                      entropy_requires_grad)
+                token_chunk, block_sparse):
+        fwd = lmhead_fwd_blocksparse if block_sparse else lmhead_fwd
+        logp, ent, saved = fwd(hidden, weight, targets, keep_mask, return_entropy,
+                               entropy_requires_grad)
         ctx.save_for_backward(hidden, weight, targets, saved)
         ctx.erg = bool(entropy_requires_grad)
         ctx.ret_ent = bool(return_entropy)
@@ -430,15 +431,18 @@ class _FusedLMHead(torch.autograd.Function):
                             g_ent if ctx.erg else None, ctx.erg, ctx.token_chunk)
         gX = gX.to(hidden.dtype) if ctx.needs_input_grad[0] else None
         gW = gW.to(weight.dtype) if ctx.needs_input_grad[1] else None
-        return gX, gW, None, None, None, None, None
+        return gX, gW, None, None, None, None, None, None
 
 
 def fused_logprobs(hidden, weight, targets, keep_mask=None, return_entropy=False,
-                   entropy_requires_grad=False, token_chunk_size=DEFAULT_TOKEN_CHUNK):
+                   entropy_requires_grad=False, token_chunk_size=DEFAULT_TOKEN_CHUNK,
+                   block_sparse=False):
     """Selected-target log-probs (and entropy) of ``hidden @ weight.T`` without
     materialising the logits. ``hidden`` may be [..., H]; outputs have the
     leading shape of ``hidden`` and dtype float32. Rows where ``keep_mask`` is
-    false get 0 and no gradient."""
+    false get 0 and no gradient. ``block_sparse`` runs the rows in place and
+    skips only 256-row tiles with no kept row (lmhead_fwd_blocksparse) instead
+    of compacting them; the results are the same."""
     if entropy_requires_grad and not return_entropy:
         raise ValueError("entropy_requires_grad requires return_entropy")
     lead = hidden.shape[:-1]
@@ -448,7 +452,8 @@ def fused_logprobs(hidden, weight, targets, keep_mask=None, return_entropy=False
     if keep_mask is not None:
         km = keep_mask.reshape(-1).to(torch.uint8).contiguous()
     out = _FusedLMHead.apply(h2, weight.contiguous(), t, km, bool(return_entropy),
-                             bool(entropy_requires_grad), int(token_chunk_size))
+                             bool(entropy_requires_grad), int(token_chunk_size),
+                             bool(block_sparse))
     if return_entropy:
         lp, ent = out
         return lp.reshape(lead), ent.reshape(lead)

@@ -244,6 +244,15 @@ def test_autograd_wrapper_matches_the_c_calls():
     # metric-only entropy carries no gradient
     lp2, ent2 = lmh.fused_logprobs(Xr, Wr, t.reshape(2, 96), return_entropy=True)
     assert not ent2.requires_grad and lp2.requires_grad
+    # the block-sparse forward through the same wrapper: same values and gradients
+    Xb = X.reshape(2, 96, 128).clone().requires_grad_(True)
+    lp3, ent3 = lmh.fused_logprobs(Xb, Wr, t.reshape(2, 96), km.reshape(2, 96).bool(),
+                                   return_entropy=True, entropy_requires_grad=True,
+                                   block_sparse=True)
+    ((lp3 * glp.reshape(2, 96)).sum() + (ent3 * gh.reshape(2, 96)).sum()).backward()
+    np.testing.assert_array_equal(lp3.detach().cpu().numpy(), lp.detach().cpu().numpy())
+    np.testing.assert_array_equal(ent3.detach().cpu().numpy(), ent.detach().cpu().numpy())
+    np.testing.assert_array_equal(Xb.grad.float().cpu().numpy(), Xr.grad.float().cpu().numpy())
 
 
 @pytest.mark.parametrize("N,H,V,chunk,seed", [
