@@ -367,3 +367,24 @@ def test_probe_workspace_covers_one_record_per_cu(lib):
 ])
 def test_probe_host_validation(lib, kw, code):
     assert _probe(lib, **kw) == code
+
+
+def test_plain_c_caller(lib, tmp_path):
+    """The header compiles as C and the library links and answers from a C
+    program (size queries, status strings, host-side argument checks)."""
+    import shutil
+    import subprocess
+    from lm_head_log_amd import _lib
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    exe = tmp_path / "abi_client"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    src = os.path.join(ROOT, "tests", "c_client", "abi_client.c")
+    r = subprocess.run([cc, "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        src, "-o", str(exe), "-L", libdir, "-llmhead", f"-Wl,-rpath,{libdir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout
