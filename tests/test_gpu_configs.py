@@ -26,8 +26,8 @@ pytestmark = pytest.mark.gpu
 SAMPLE = 512
 
 
-def _full_check(w, sample_seed, backward=True, blocksparse=False):
-    g = run(w, backward=backward)
+def _full_check(w, sample_seed, backward=True, blocksparse=False, token_chunk=0):
+    g = run(w, backward=backward, token_chunk=token_chunk)
     if blocksparse:
         _blocksparse_check(w, g)
     kept = w.kept_rows()
@@ -68,10 +68,11 @@ def _full_check(w, sample_seed, backward=True, blocksparse=False):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("frac", [1.0, 0.23])
-def test_config2_dense_rl(frac):
-    say(f"case: config2 N16384 H4096 V131072 keep {frac}")
-    _full_check(wl.config2(frac), 2)
+@pytest.mark.parametrize("frac,chunk", [(1.0, 0), (0.23, 0), (1.0, 8192)])
+def test_config2_dense_rl(frac, chunk):
+    # chunk 8192: the pages' default token chunk, two chunks with dW added in order
+    say(f"case: config2 N16384 H4096 V131072 keep {frac} token chunk {chunk or 'default'}")
+    _full_check(wl.config2(frac), 2, token_chunk=chunk)
 
 
 def test_config3_packed_grpo():
