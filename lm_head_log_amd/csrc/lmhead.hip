@@ -774,7 +774,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // bf16 pairs: (__bf16)x rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
-template <int SHIFT>
+// kEntGrad: whether the entropy term of dz is formed. Without it (metric-only
+// entropy, or no entropy) cb = 0 and dz = p ca' (+ g_lp at the target), one
+// FMA per logit fewer, with the same bits.
+template <int SHIFT, bool kEntGrad>
 __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
   LMH_DECLARE_RING;
 
@@ -856,7 +859,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
         for (int r = 0; r < 16; ++r) {
           const float z = acc_read(acc[i][j][r], fence);
           const float p = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -k.x));
-          d[r] = p * fmaf(k.z, z, k.y);
+          d[r] = kEntGrad ? p * fmaf(k.z, z, k.y) : p * k.y;
         }
         // the one-hot term of the target, in the one lane that holds it
         if (hit && (want >> 4) == i) {
@@ -1507,9 +1510,15 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
       const int dz_grid = persistent_grid(dz_tiles);
       D.queue = queues + (ch * kBwdQueueSets + 0) * kQueueInts;
       D.steal = steal_for(dz_tiles, dz_grid);
-      LMH_TRY(launch_shifted(KK_DZ, stage_shift((int)(H / kBK)), dim3(dz_grid), s, D,
-                             k_dz_tiles<0>, k_dz_tiles<2>, k_dz_tiles<4>, k_dz_tiles<6>,
-                             k_dz_tiles<8>, k_dz_tiles<10>));
+      const int dz_shift = stage_shift((int)(H / kBK));
+      if (entropy_requires_grad)
+        LMH_TRY(launch_shifted(KK_DZ, dz_shift, dim3(dz_grid), s, D, k_dz_tiles<0, true>,
+                               k_dz_tiles<2, true>, k_dz_tiles<4, true>, k_dz_tiles<6, true>,
+                               k_dz_tiles<8, true>, k_dz_tiles<10, true>));
+      else
+        LMH_TRY(launch_shifted(KK_DZ, dz_shift, dim3(dz_grid), s, D, k_dz_tiles<0, false>,
+                               k_dz_tiles<2, false>, k_dz_tiles<4, false>, k_dz_tiles<6, false>,
+                               k_dz_tiles<8, false>, k_dz_tiles<10, false>));
 
       DxParams X2;
       X2.dZ = dZ;
