@@ -12,7 +12,7 @@ load, with this batch's own operand bits and with zeros. Prints ONE JSON line
 on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--keep 1.0]
-                    [--config 2] [--token-chunk 0] [--no-cpu-baseline]
+                    [--workload dense_rl] [--token-chunk 0] [--no-cpu-baseline]
                     [--no-keep-sweep] [--no-probe] [--no-blocksparse]
 """
 
@@ -40,13 +40,11 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def make_workload(cfg: int, keep: float):
+def make_workload(name: str, keep: float):
     import workloads as wl
-    if cfg == 1:
-        return wl.config1()
-    if cfg == 2:
-        return wl.config2(keep)
-    return wl.CONFIGS[cfg]()
+    if name == "dense_rl":
+        return wl.dense_rl(keep)
+    return wl.WORKLOADS[name]()
 
 
 def kernel_source_hash() -> str:
@@ -241,7 +239,7 @@ def blocksparse_leg(lmh, stream, dev, steps):
     import torch
 
     import workloads as wl
-    w = wl.config5()
+    w = wl.scoring()
     N, H, V = w.N, w.H, w.V
     X = torch.from_numpy(w.hidden.view(np.int16)).view(torch.bfloat16).to(dev)
     W = torch.from_numpy(w.weight.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -314,7 +312,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", default="dense_rl",
+                    choices=["dense_rl", "packed_grpo", "fp32_stress", "scoring", "tiny"],
+                    help="dense_rl: N 16384 H 4096 V 131072 (the metric); packed_grpo: "
+                         "N 16384 H 4096 V 151936; fp32_stress: N 16384 H 2560 V 151936; "
+                         "scoring: N 262144 H 5120 V 152064, forward only; tiny: N 128 H 512 V 8192")
     ap.add_argument("--keep", type=float, default=1.0)
     ap.add_argument("--token-chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -351,7 +353,7 @@ def main():
     torch.cuda.set_device(dev)
 
     t0 = time.time()
-    w = make_workload(args.config, args.keep)
+    w = make_workload(args.workload, args.keep)
     log(f"workload {w.name} generated in {time.time() - t0:.1f}s")
     N, H, V = w.N, w.H, w.V
     X = torch.from_numpy(w.hidden.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -451,9 +453,9 @@ def main():
         log(f"mfma probe {probe}")
 
     sweep = None
-    if not args.no_keep_sweep and args.config == 2:
+    if not args.no_keep_sweep and args.workload == "dense_rl":
         import workloads as wl
-        masks = wl.config2_masks(wl.KEEP_SWEEP, N=N)
+        masks = wl.dense_rl_masks(wl.KEEP_SWEEP, N=N)
         fr, ms, kept = [], [], []
         for f in wl.KEEP_SWEEP:
             m_dev = torch.from_numpy(masks[f]).to(dev)
@@ -480,17 +482,17 @@ def main():
         }
 
     shard = None
-    if not args.no_shard and args.config == 2 and do_bwd:
+    if not args.no_shard and args.workload == "dense_rl" and do_bwd:
         shard = shard_leg(lmh, X, W, t, glp, gh, erg, stream, dev, max(args.sweep_steps, 5))
         log(f"tp shard {shard}")
 
     logits = None
-    if not args.no_logits and args.config == 2:
+    if not args.no_logits and args.workload == "dense_rl":
         logits = logits_leg(lmh, stream, dev, max(args.sweep_steps, 5))
         log(f"logits entry {logits}")
 
     bsp = None
-    if not args.no_blocksparse and args.config == 2:
+    if not args.no_blocksparse and args.workload == "dense_rl":
         bsp = blocksparse_leg(lmh, stream, dev, 3)
         log(f"block-sparse vs compacting forward {bsp}")
 

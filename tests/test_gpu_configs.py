@@ -69,20 +69,20 @@ def _full_check(w, sample_seed, backward=True, blocksparse=False, token_chunk=0)
 
 
 @pytest.mark.parametrize("frac,chunk", [(1.0, 0), (0.23, 0), (1.0, 8192)])
-def test_config2_dense_rl(frac, chunk):
+def test_dense_rl_full_size(frac, chunk):
     # chunk 8192: the pages' default token chunk, two chunks with dW added in order
-    say(f"case: config2 N16384 H4096 V131072 keep {frac} token chunk {chunk or 'default'}")
-    _full_check(wl.config2(frac), 2, token_chunk=chunk)
+    say(f"case: dense_rl N16384 H4096 V131072 keep {frac} token chunk {chunk or 'default'}")
+    _full_check(wl.dense_rl(frac), 2, token_chunk=chunk)
 
 
-def test_config3_packed_grpo():
-    say("case: config3 packed GRPO N16384 H4096 V151936 (metric-only entropy)")
-    _full_check(wl.config3(), 3)
+def test_packed_grpo_full_size():
+    say("case: packed_grpo packed GRPO N16384 H4096 V151936 (metric-only entropy)")
+    _full_check(wl.packed_grpo(), 3)
 
 
-def test_config4_fp32_stress():
-    say("case: config4 fp32 stress N16384 H2560 V151936")
-    _full_check(wl.config4(), 4)
+def test_fp32_stress_full_size():
+    say("case: fp32_stress fp32 stress N16384 H2560 V151936")
+    _full_check(wl.fp32_stress(), 4)
 
 
 def _blocksparse_check(w, g):
@@ -102,9 +102,9 @@ def _blocksparse_check(w, g):
     gc.collect()
 
 
-def test_config5_scoring_forward():
-    say("case: config5 scoring N262144 H5120 V152064 forward only, compacting and block-sparse")
-    _full_check(wl.config5(), 5, backward=False, blocksparse=True)
+def test_scoring_forward_full_size():
+    say("case: scoring scoring N262144 H5120 V152064 forward only, compacting and block-sparse")
+    _full_check(wl.scoring(), 5, backward=False, blocksparse=True)
 
 
 def test_compaction_many_chunks():
@@ -134,8 +134,8 @@ def test_full_size_runs_are_bitwise_reproducible():
     """Two runs at the bench shape, keep 0.64 (tile queues with stealing hand
     tiles to different CUs each run, and the dX tail is split): every output
     bit-identical."""
-    say("case: config2 keep 0.64, two runs, bitwise")
-    w = wl.config2(0.64)
+    say("case: dense_rl keep 0.64, two runs, bitwise")
+    w = wl.dense_rl(0.64)
     a = run(w)
     b = run(w)
     for k in ("logp", "entropy", "dX", "dW"):

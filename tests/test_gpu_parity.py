@@ -52,13 +52,13 @@ def check_against_oracle(w, g, keep=_WORKLOAD_MASK, erg=None, backward=True, wha
     return {}
 
 
-def test_config1_full_parity():
-    say("case: config1 tiny N128 H512 V8192 fwd+bwd")
-    w = wl.config1()
+def test_tiny_batch_full_parity():
+    say("case: tiny_batch tiny N128 H512 V8192 fwd+bwd")
+    w = wl.tiny_batch()
     g = run(w)
     assert g["status"] == 0
-    errs = check_against_oracle(w, g, what="config1")
-    say(f"config1 grad errors {errs}")
+    errs = check_against_oracle(w, g, what="tiny_batch")
+    say(f"tiny_batch grad errors {errs}")
 
 
 @pytest.mark.parametrize("N,H,V,seed", [

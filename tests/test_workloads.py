@@ -33,16 +33,16 @@ def test_bf16_rounding_matches_torch_rne():
 
 
 def test_same_seed_same_bits():
-    a = wl.config1()
-    b = wl.config1()
+    a = wl.tiny_batch()
+    b = wl.tiny_batch()
     for f in ("hidden", "weight", "targets", "keep", "g_logp", "g_entropy"):
         np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
-    c = wl.config1(seed=11)
+    c = wl.tiny_batch(seed=11)
     assert not np.array_equal(a.hidden, c.hidden)
 
 
-def test_config1_shape_and_distribution():
-    w = wl.config1()
+def test_tiny_batch_shape_and_distribution():
+    w = wl.tiny_batch()
     assert (w.N, w.H, w.V) == (128, 512, 8192)
     X = wl.bf16_bits_to_f32(w.hidden)
     W = wl.bf16_bits_to_f32(w.weight)
@@ -58,20 +58,20 @@ def test_keep_sweep_is_the_pages_table():
     assert tuple(g["skyrl_active_fractions"]) == wl.KEEP_SWEEP
 
 
-def test_config2_masks_nested_and_fractions():
+def test_dense_rl_masks_nested_and_fractions():
     # reduced sizes, same rules as the full config
-    ms = [wl.config2(f, N=20000, H=64, V=256).keep for f in wl.KEEP_SWEEP]
+    ms = [wl.dense_rl(f, N=20000, H=64, V=256).keep for f in wl.KEEP_SWEEP]
     for f, m in zip(wl.KEEP_SWEEP, ms):
         assert abs(m.mean() - f) < 0.015
     for hi, lo in zip(ms, ms[1:]):
         assert np.all(lo <= hi)  # lower fraction is a subset
-    assert wl.config2(1.0, N=64, H=64, V=256, mask=False).keep is None
+    assert wl.dense_rl(1.0, N=64, H=64, V=256, mask=False).keep is None
 
 
-def test_config2_masks_helper_matches_config2():
-    masks = wl.config2_masks(wl.KEEP_SWEEP, N=5000)
+def test_dense_rl_masks_helper_matches_dense_rl():
+    masks = wl.dense_rl_masks(wl.KEEP_SWEEP, N=5000)
     for f in wl.KEEP_SWEEP:
-        assert np.array_equal(masks[f], wl.config2(f, N=5000, H=64, V=256).keep)
+        assert np.array_equal(masks[f], wl.dense_rl(f, N=5000, H=64, V=256).keep)
 
 
 def test_packed_grpo_layout_rules():
@@ -93,8 +93,8 @@ def test_packed_grpo_layout_rules():
             assert 0.4 * L - 2 <= n_keep <= 0.8 * L + 1
 
 
-def test_config3_bias_makes_target_logits_peaked():
-    w = wl.config3(N=2048, H=256, V=4096)
+def test_packed_grpo_bias_makes_target_logits_peaked():
+    w = wl.packed_grpo(N=2048, H=256, V=4096)
     X = wl.bf16_bits_to_f32(w.hidden).astype(np.float64)
     W = wl.bf16_bits_to_f32(w.weight).astype(np.float64)
     kept = np.flatnonzero(w.keep)
@@ -107,8 +107,8 @@ def test_config3_bias_makes_target_logits_peaked():
     assert not w.entropy_requires_grad and w.return_entropy
 
 
-def test_config4_row_scales():
-    w = wl.config4(N=4096, H=128, V=512)
+def test_fp32_stress_row_scales():
+    w = wl.fp32_stress(N=4096, H=128, V=512)
     s = w.meta["row_scale"]
     assert s.min() >= 0.5 - 1e-6 and s.max() <= 8.0 + 1e-5
     X = wl.bf16_bits_to_f32(w.hidden)
@@ -117,7 +117,7 @@ def test_config4_row_scales():
     assert w.keep.all()
 
 
-def test_config5_spans():
+def test_scoring_spans():
     rng = np.random.default_rng(2)
     keep = wl.span_keep(262144, rng)
     assert 0.35 < keep.mean() < 0.65

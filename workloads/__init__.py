@@ -134,7 +134,7 @@ def _upstream(st, N):
     return g_lp, g_h
 
 
-def config1(seed: int = 1) -> Workload:
+def tiny_batch(seed: int = 1) -> Workload:
     """Tiny forward+backward: N=128, H=512, V=8192, keep ~ Bernoulli(0.7).
 
     hidden ~ N(0, 1); weight ~ N(0, std 1/sqrt(H)), giving unit-std logits.
@@ -147,10 +147,10 @@ def config1(seed: int = 1) -> Workload:
     keep = (_gen(st["keep"]).random(N) < 0.7).astype(np.uint8)
     g_lp, g_h = _upstream(st, N)
     return Workload("tiny N128 H512 V8192", X, W, t, keep, g_lp, g_h,
-                    meta=dict(config=1, seed=seed, keep_fraction=0.7))
+                    meta=dict(workload="tiny_batch", seed=seed, keep_fraction=0.7))
 
 
-def config2(keep_fraction: float = 1.0, seed: int = 2, N: int = 16384,
+def dense_rl(keep_fraction: float = 1.0, seed: int = 2, N: int = 16384,
             H: int = 4096, V: int = 131072, mask: bool = True) -> Workload:
     """Dense RL shape: N=16384, H=4096, V=131072, Bernoulli keep mask.
 
@@ -167,11 +167,11 @@ def config2(keep_fraction: float = 1.0, seed: int = 2, N: int = 16384,
     g_lp, g_h = _upstream(st, N)
     return Workload(f"dense RL N{N} H{H} V{V} keep{keep_fraction:.2f}", X, W, t,
                     keep, g_lp, g_h,
-                    meta=dict(config=2, seed=seed, keep_fraction=keep_fraction))
+                    meta=dict(workload="dense_rl", seed=seed, keep_fraction=keep_fraction))
 
 
-def config2_masks(fractions=KEEP_SWEEP, seed: int = 2, N: int = 16384) -> dict:
-    """The keep masks ``config2(f).keep`` for each fraction f, from the same
+def dense_rl_masks(fractions=KEEP_SWEEP, seed: int = 2, N: int = 16384) -> dict:
+    """The keep masks ``dense_rl(f).keep`` for each fraction f, from the same
     uniform draw, without generating X and W again."""
     u = _gen(_streams(seed)["keep"]).random(N)
     return {f: (u < f).astype(np.uint8) for f in fractions}
@@ -200,7 +200,7 @@ def packed_grpo_layout(N: int, V: int, nseq: int, rng: np.random.Generator):
     return tokens, targets, keep, starts
 
 
-def config3(seed: int = 3, N: int = 16384, H: int = 4096, V: int = 151936) -> Workload:
+def packed_grpo(seed: int = 3, N: int = 16384, H: int = 4096, V: int = 151936) -> Workload:
     """Packed GRPO batch: 16 sequences, prompt 20-60 % of each (keep 0),
     completion kept, next-token targets, and a +3 sigma bias on the weight row
     of each kept target so the logits are peaked. Entropy is metric-only.
@@ -231,11 +231,11 @@ def config3(seed: int = 3, N: int = 16384, H: int = 4096, V: int = 151936) -> Wo
     g_lp, g_h = _upstream(st, N)
     return Workload(f"packed GRPO N{N} H{H} V{V}", X, W, t, keep, g_lp, g_h,
                     return_entropy=True, entropy_requires_grad=False,
-                    meta=dict(config=3, seed=seed, seq_starts=starts,
+                    meta=dict(workload="packed_grpo", seed=seed, seq_starts=starts,
                               keep_fraction=float(keep.mean())))
 
 
-def config4(seed: int = 4, N: int = 16384, H: int = 2560, V: int = 151936) -> Workload:
+def fp32_stress(seed: int = 4, N: int = 16384, H: int = 2560, V: int = 151936) -> Workload:
     """fp32-accuracy stress: per-row scale s_i ~ LogUniform(0.5, 8) on the
     hidden state before bf16 rounding; every row kept; entropy grad on."""
     st = _streams(seed)
@@ -246,7 +246,7 @@ def config4(seed: int = 4, N: int = 16384, H: int = 2560, V: int = 151936) -> Wo
     keep = np.ones(N, dtype=np.uint8)
     g_lp, g_h = _upstream(st, N)
     return Workload(f"fp32 stress N{N} H{H} V{V}", X, W, t, keep, g_lp, g_h,
-                    meta=dict(config=4, seed=seed, keep_fraction=1.0, row_scale=s))
+                    meta=dict(workload="fp32_stress", seed=seed, keep_fraction=1.0, row_scale=s))
 
 
 def span_keep(N: int, rng: np.random.Generator, lo: int = 64, hi: int = 2048,
@@ -262,7 +262,7 @@ def span_keep(N: int, rng: np.random.Generator, lo: int = 64, hi: int = 2048,
     return keep
 
 
-def config5(seed: int = 5, N: int = 262144, H: int = 5120, V: int = 152064) -> Workload:
+def scoring(seed: int = 5, N: int = 262144, H: int = 5120, V: int = 152064) -> Workload:
     """Reference-model scoring, forward only: keep mask in contiguous spans."""
     st = _streams(seed)
     X = _normal_bf16(st["hidden"], N, H, 1.0)
@@ -272,13 +272,13 @@ def config5(seed: int = 5, N: int = 262144, H: int = 5120, V: int = 152064) -> W
     g_lp, g_h = _upstream(st, N)
     return Workload(f"scoring N{N} H{H} V{V}", X, W, t, keep, g_lp, g_h,
                     return_entropy=True, entropy_requires_grad=False, backward=False,
-                    meta=dict(config=5, seed=seed, keep_fraction=float(keep.mean())))
+                    meta=dict(workload="scoring", seed=seed, keep_fraction=float(keep.mean())))
 
 
 def small(N: int, H: int, V: int, seed: int = 0, keep_fraction: float = 0.7,
           x_std: float = 1.0, w_std: float | None = None, mask: bool = True,
           return_entropy: bool = True, entropy_requires_grad: bool = True) -> Workload:
-    """Arbitrary small shape with config-1 style distributions (for edge cases)."""
+    """Arbitrary small shape with the tiny batch's distributions (for edge cases)."""
     st = _streams(seed)
     if w_std is None:
         w_std = 1.0 / math.sqrt(H)
@@ -309,4 +309,5 @@ def row_mask(N: int, rows: np.ndarray) -> np.ndarray:
     return m
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {"tiny": tiny_batch, "dense_rl": dense_rl, "packed_grpo": packed_grpo,
+             "fp32_stress": fp32_stress, "scoring": scoring}
