@@ -336,7 +336,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the op runs on one GPU; --gpus {args.gpus} is not supported "
               "(the op shards by rows or vocabulary, but no multi-GPU path is built)",
               file=sys.stderr)
         sys.exit(2)
