@@ -27,6 +27,9 @@ CASES = [
     (300, 192, 3000, [(0, 1000), (1000, 2256), (2256, 3000)], 31),
     (257, 256, 2049, [(1024, 2049), (0, 1024)], 32),
     (130, 704, 700, [(600, 700), (0, 1), (1, 600)], 33),
+    # slices of at least 16384 rows: each shard backward splits its dX tail
+    # (8 pieces for the 16384-row slice, 4 for the 23617-row one)
+    (300, 128, 40001, [(16384, 40001), (0, 16384)], 34),
 ]
 
 
