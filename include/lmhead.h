@@ -48,7 +48,9 @@
  *    before anything is enqueued; a failing call enqueues nothing.
  *  - Sizes: N >= 0, V >= 1, H >= 64 with H % 64 == 0 (else
  *    LMHEAD_ERR_UNSUPPORTED). N and V are otherwise arbitrary up to
- *    N <= 2^28, V <= 2^22, H <= 2^20.
+ *    N <= 2^24, V <= 2^22, H <= 2^20 (else LMHEAD_ERR_UNSUPPORTED): within
+ *    them every matrix the kernels read is addressed through 32-bit buffer
+ *    offsets that stay below 2^31 bytes, and every tile index fits int32.
  *  - Results are bitwise reproducible run to run for the same inputs and
  *    arguments (fixed reduction orders, no floating-point atomics).
  */
@@ -85,12 +87,13 @@ size_t lmhead_saved_bytes(int64_t N);
  * ([H][N rounded up to 64]). Returns 0 on invalid sizes. */
 size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V);
 
-/* Workspace bytes lmhead_bwd needs: 32 tile-queue counters per token chunk,
- * 20 bytes per kept row (N rounded up to 256 entries) of logit-gradient
- * coefficients and targets, a bf16 transposed copy of the kept rows of X
- * ([H][N rounded up to 64]), the bf16 logit gradient dZ of one chunk
- * of C rows ([C][V rounded up to 256], token-major), where C = token_chunk
- * rounded up to a multiple of 256 (at most N rounded up to 256), and, for
+/* Workspace bytes lmhead_bwd needs: a 256-byte checked copy of the saved
+ * header, 32 tile-queue counters per token chunk, 20 bytes per kept row (N
+ * rounded up to 256 entries) of logit-gradient coefficients and targets, a
+ * bf16 transposed copy of one chunk's kept rows of X ([H][C]), the bf16 logit
+ * gradient dZ of one chunk of C rows ([C][V rounded up to 256], token-major),
+ * where C = token_chunk rounded up to a multiple of 256, at most N rounded up
+ * to 256 and at most 2^22 (a larger request is clamped to 2^22), and, for
  * V >= 16384, fp32 partial dX tiles: when the dX tiles of a chunk past its
  * last whole round of workgroups number at most 256 (S - 1) / S, each is
  * computed as S pieces of the vocabulary range that the whole device runs,
@@ -116,7 +119,7 @@ size_t lmhead_bwd_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t token
  *  entropy    fp32 [N] out, fully written; must be NULL iff !return_entropy
  *             (not checked when N == 0, where any output may be NULL)
  *  entropy_requires_grad  requires return_entropy (else INVALID_ARG); it is
- *             recorded in `saved` and selects the backward's entropy term.
+ *             recorded in `saved`, and lmhead_bwd must pass the same value.
  *  saved      device buffer of >= lmhead_saved_bytes(N) bytes, out
  *  workspace  device buffer of >= lmhead_fwd_workspace_bytes(N, H, V) bytes;
  *             free for reuse once the enqueued work has completed.
@@ -160,7 +163,14 @@ int lmhead_fwd_blocksparse(const void* hidden, const void* weight, const int32_t
  *
  *  hidden, weight, targets, N, H, V: exactly as passed to lmhead_fwd
  *  entropy_requires_grad: as passed to lmhead_fwd
- *  saved      the buffer lmhead_fwd filled, unmodified
+ *  saved      the buffer lmhead_fwd filled. Its header records the forward's
+ *             N, H, V and entropy_requires_grad; the backward compares them
+ *             with its own arguments on the device (it cannot read them
+ *             without synchronising). On a mismatch it computes nothing from
+ *             the saved state: grad_hidden and grad_weight are written with
+ *             +0.0 everywhere, and lmhead_check_status(saved) then returns
+ *             LMHEAD_ERR_INVALID_ARG. The backward writes one word of `saved`,
+ *             that verdict (LMHEAD_OK for a consistent call), and nothing else.
  *  grad_logp  fp32 [N]; skipped rows are not read
  *  grad_entropy fp32 [N]; must be NULL iff !entropy_requires_grad (N > 0)
  *  grad_hidden fp32 [N, H] out, fully overwritten (+0.0 rows where skipped)
@@ -235,6 +245,11 @@ int lmhead_merge_partials(const float* partials, int64_t P, int64_t N,
  *  hidden, targets, N, H, entropy_requires_grad, grad_logp, grad_entropy,
  *             token_chunk: as for lmhead_bwd
  *  weight_shard, V_shard, vocab_start: as passed to lmhead_fwd_partial
+ *  saved      completed by lmhead_merge_partials (its entropy_requires_grad
+ *             is the one this call must pass); checked as in lmhead_bwd, with
+ *             the shard's range required to lie inside the forward's
+ *             vocabulary. A state that lmhead_merge_partials never completed
+ *             is rejected the same way (+0.0 gradients, INVALID_ARG status).
  *  grad_hidden fp32 [N, H] out, fully overwritten (+0.0 rows where skipped)
  *  grad_weight_shard fp32 [V_shard, H] out, fully overwritten
  *  workspace  >= lmhead_bwd_workspace_bytes(N, H, V_shard, token_chunk) bytes
@@ -293,8 +308,9 @@ int lmhead_logits_bwd(const void* logits, int dtype, int64_t N, int64_t V,
 int lmhead_read_n_kept(const void* saved, int64_t* n_kept_host, void* stream);
 
 /* Syncs `stream`, then returns LMHEAD_ERR_TARGET_RANGE if the forward that
- * filled `saved` met a kept row whose target is outside [0, V), else
- * LMHEAD_OK. */
+ * filled `saved` met a kept row whose target is outside [0, V); else
+ * LMHEAD_ERR_INVALID_ARG if the last backward on `saved` found it
+ * inconsistent with its arguments (see lmhead_bwd); else LMHEAD_OK. */
 int lmhead_check_status(const void* saved, void* stream);
 
 /* Static, NUL-terminated description of a status code. */

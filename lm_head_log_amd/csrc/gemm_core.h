@@ -139,26 +139,39 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
 
 // The K-major A operand of a tile: rows m0 .. m0 + 255 of a [rows][ld] bf16
 // matrix; rows at or past `rows` (counted from m0) read as zero.
+//
+// Each wave loads 64 of the 256 rows, so each wave builds its descriptor at
+// its own first row: record counts and lane offsets then span at most
+// 64 rows, 128 ld bytes, which stays below 2^31 (and below the kOOB
+// sentinel) for every ld < 2^24. A descriptor over the whole tile would
+// span 512 ld bytes and wrap at ld = 2^22.
+constexpr int64_t kMaxALd = int64_t(1) << 24;
 struct ASrc {
   __amdgpu_buffer_rsrc_t rsrc;
   __amdgpu_buffer_rsrc_t none;         // zero records: every load reads zeros
   uint32_t off[kALoadsPerWavePair];   // per load: byte offset of this lane's chunk at k = 0
 
   // tile_base: element pointer of the tile's first row; ld: row pitch
-  // (elements, multiple of 8; every row holds the K range rounded up to 64).
+  // (elements, multiple of 8, below kMaxALd; every row holds the K range
+  // rounded up to 64).
   __device__ __forceinline__ void init(const uint16_t* tile_base, int64_t ld, int rows) {
-    rows = rows < 0 ? 0 : (rows > kBM ? kBM : rows);
-    const int bytes = __builtin_amdgcn_readfirstlane((int)((int64_t)rows * ld * 2));
-    void* base = reinterpret_cast<void*>(uniform_u64(reinterpret_cast<uint64_t>(tile_base)));
+    const int lane = lane_fresh();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int kWaveRows = kBM / 4;
+    int wrows = rows - wave * kWaveRows;  // rows of this wave's 64 that exist
+    wrows = wrows < 0 ? 0 : (wrows > kWaveRows ? kWaveRows : wrows);
+    const int bytes = __builtin_amdgcn_readfirstlane((int)((int64_t)wrows * ld * 2));
+    void* base = reinterpret_cast<void*>(
+        uniform_u64(reinterpret_cast<uint64_t>(tile_base + (int64_t)wave * kWaveRows * ld)));
     rsrc = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, kRsrcWord3);
     none = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0, kRsrcWord3);
-    const int lane = lane_fresh();
-    const int wave = wave_fresh();
 #pragma unroll
     for (int j = 0; j < kALoadsPerWavePair; ++j) {
-      const int row = wave * (kBM / 4) + j * kARowsPerLoad + lane / kAChunks;
-      const int c = (lane % kAChunks) ^ ((row >> 1) & (kAChunks - 1));
-      off[j] = row < rows ? (uint32_t)(row * ld * 2 + c * 16) : kOOB;
+      const int wr = j * kARowsPerLoad + lane / kAChunks;  // row within the wave's 64
+      // the LDS swizzle follows the row within the tile; wave * 64 leaves
+      // (row >> 1) & 7 unchanged
+      const int c = (lane % kAChunks) ^ ((wr >> 1) & (kAChunks - 1));
+      off[j] = wr < wrows ? (uint32_t)(wr * ld * 2 + c * 16) : kOOB;
     }
   }
   // Issue half h (loads 4 h .. 4 h + 3) of this wave's loads of k pair p into
@@ -190,38 +203,47 @@ struct ASrc {
 // The MN-major B operand of a tile: columns n0 .. n0 + 255 of the k rows of a
 // [k_rows][ld] bf16 matrix (n contiguous); k rows at or past k_rows and
 // columns at or past n_valid (counted from n0) read as zero.
+//
+// Each wave loads 8 of a stage's 32 k rows, and its descriptor starts at its
+// own first row of the stage: record counts and offsets span at most 8 rows,
+// 16 ld bytes, below 2^31 for every ld < 2^27.
+constexpr int64_t kMaxBLd = int64_t(1) << 27;
 struct BSrc {
-  uint64_t base;                        // byte address of (k 0, n0); wave-uniform
+  uint64_t base;                        // byte address of (k = 8 wave, n0); wave-uniform
   int64_t pitch;                        // bytes per k row; wave-uniform
-  int k_valid;                          // wave-uniform
+  int k_valid;                          // k rows at or past the wave's first; wave-uniform
   uint32_t off[kBLoadsPerWaveStage];   // per load: byte offset of this lane's chunk in a stage
 
   __device__ __forceinline__ void init(const uint16_t* col_base, int64_t ld, int k_rows,
                                        int n_valid) {
-    base = uniform_u64(reinterpret_cast<uint64_t>(col_base));
+    constexpr int kWaveRows = kBK / 4;  // 8 k rows of each stage per wave
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    base = uniform_u64(reinterpret_cast<uint64_t>(col_base + (int64_t)wave * kWaveRows * ld));
     pitch = (int64_t)uniform_u64((uint64_t)(ld * 2));
-    k_valid = __builtin_amdgcn_readfirstlane(k_rows < 0 ? 0 : k_rows);
+    k_valid = __builtin_amdgcn_readfirstlane((k_rows < 0 ? 0 : k_rows) - wave * kWaveRows);
     const int lane = lane_fresh();
-    const int wave = wave_fresh();
     const int e = (lane >> 2) & 3;     // k row inside the group
     const int blk = lane >> 4;         // 32-wide n block inside the half
     const int cq = lane & 3;           // 16-byte chunk inside the piece
 #pragma unroll
     for (int j = 0; j < kBLoadsPerWaveStage; ++j) {
-      // load j fills half (j & 1) of group 2 wave + j / 2 of the stage
-      const int row = (wave * 2 + (j >> 1)) * 4 + e;
+      // load j fills half (j & 1) of group 2 wave + j / 2 of the stage; its
+      // k row relative to the wave's first row of the stage:
+      const int row = (j >> 1) * 4 + e;
       const int col = ((j & 1) * 4 + blk) * 32 + cq * 8;
       off[j] = col < n_valid ? (uint32_t)(row * pitch + col * 2) : kOOB;
     }
   }
   // Issue this wave's loads of stage kt into the B slot at `dst`. The
-  // descriptor is rebased to the stage's first k row, and its record count
-  // covers only the valid rows of the stage (none at or past k_valid).
+  // descriptor is rebased to the wave's first k row of the stage, and its
+  // record count covers only the valid rows among the wave's 8 (none at or
+  // past k_rows).
   __device__ __forceinline__ void issue(int kt, char* dst) const {
+    constexpr int kWaveRows = kBK / 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     char* ldsb = dst + wave * 2 * kMnGroupBytes;
     int rows = k_valid - kt * kBK;
-    rows = rows < 0 ? 0 : (rows > kBK ? kBK : rows);
+    rows = rows < 0 ? 0 : (rows > kWaveRows ? kWaveRows : rows);
     void* p = reinterpret_cast<void*>(uniform_u64(base + (uint64_t)((int64_t)kt * kBK * pitch)));
     const int bytes = __builtin_amdgcn_readfirstlane((int)(rows * pitch));
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p, (short)0, bytes,
@@ -338,8 +360,9 @@ struct TileQueue {
   // The next logical tile for the calling workgroup, or -1 when none is left.
   // Thread 0 takes it (the position taken ahead, else the next one of its
   // own XCD's queue, then the other queues when stealing) and broadcasts it
-  // through the first word of `bcast` (LDS that no load in flight writes;
-  // see the kernels); contains a workgroup barrier.
+  // through the first word of `bcast`, the ring slot bcast_slot<SHIFT>()
+  // names (no load writes it until every wave has read the index); contains
+  // a workgroup barrier.
   __device__ __forceinline__ int next(char* bcast) {
     volatile int* slot = reinterpret_cast<volatile int*>(bcast);
     if (threadIdx.x == 0) {
@@ -360,6 +383,16 @@ struct TileQueue {
 // ---------------------------------------------------------------------------
 // Main loop.
 // ---------------------------------------------------------------------------
+// The ring slot through whose first word thread 0 hands the next tile index
+// to the workgroup (TileQueue::next). The main loop's prologue loads B slots
+// SHIFT, SHIFT + 1 and SHIFT + 2 (mod 4) and both A slots of pairs 0 and 1
+// before its first barrier; B slot SHIFT + 3 is loaded only after it, by
+// which point every wave has read the index. Epilogues stage through A slots
+// only. (Only wave 0 writes the first bytes of any slot, and its loads have
+// landed when a main loop returns.)
+template <int SHIFT>
+__host__ __device__ constexpr int bcast_slot() { return (SHIFT + 3) % 4; }
+
 struct Ring {
   char* a[3];
   char* b[4];
@@ -495,6 +528,9 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
   // loads (A pair 1's second half, B stage 2, pair 2's first half).
   constexpr int a0 = (SHIFT / 2) % 3, a1 = (SHIFT / 2 + 1) % 3;
   constexpr int b0 = SHIFT % 4, b1 = (SHIFT + 1) % 4, b2 = (SHIFT + 2) % 4;
+  static_assert(b0 != bcast_slot<SHIFT>() && b1 != bcast_slot<SHIFT>() &&
+                    b2 != bcast_slot<SHIFT>(),
+                "the prologue must not load the tile-index slot before its first barrier");
   A.issue_half(0, np, 0, R.a[a0]);
   A.issue_half(0, np, 1, R.a[a0]);
   B.issue(0, R.b[b0]);

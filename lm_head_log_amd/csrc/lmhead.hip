@@ -46,6 +46,7 @@
 
 #include "../../include/lmhead.h"
 #include "gemm_core.h"
+#include "launch.h"
 
 #define LMH_API extern "C" __attribute__((visibility("default")))
 
@@ -66,10 +67,15 @@ constexpr int kVersion = 300;  // 0.3.0: block-sparse forward, MFMA ceiling prob
 // ---------------------------------------------------------------------------
 struct SavedHeader {
   int32_t n_kept;
-  int32_t status;  // lmhead_status of the forward's device-side checks
-  int32_t N, H, V;
-  int32_t flags;   // bit 0: return_entropy, bit 1: entropy_requires_grad
+  int32_t status;      // lmhead_status of the forward's device-side checks
+  int32_t N, H, V;     // of the forward call (V: the whole vocabulary)
+  int32_t flags;       // kFlag* below
+  int32_t bwd_status;  // lmhead_status of the last backward's consistency check
 };
+constexpr int kFlagReturnEntropy = 1;
+constexpr int kFlagEntropyGrad = 2;
+constexpr int kFlagBlockSparse = 4;
+constexpr int kFlagComplete = 8;  // LSE and entropy of every kept row are written
 constexpr size_t kHeaderBytes = 1024;
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -99,7 +105,29 @@ static inline SavedView saved_view(void* base, int64_t N) {
 }
 
 static inline int n_vtiles(int64_t V) { return (int)((V + kBM - 1) / kBM); }
-static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+static __host__ __device__ constexpr int64_t round_up(int64_t x, int64_t m) {
+  return (x + m - 1) / m * m;
+}
+
+// Size limits. Every GEMM operand is addressed through per-wave buffer
+// descriptors whose record counts and offsets must stay below 2^31 bytes:
+// a K-major operand's row pitch below kMaxALd elements, an MN-major one's
+// below kMaxBLd (gemm_core.h). The operands and their pitches:
+//   W [V][H]            pitch H               (A of the logit GEMMs, B of dX)
+//   X_c^T, forward      pitch N rounded to 64 (B of the logit GEMM)
+//   X_c^T, backward     pitch C, the chunk    (B of dZ, A of dW)
+//   dZ [C][ldz]         pitch V rounded to 256 (A of dX, B of dW)
+// so H <= 2^20, V <= 2^22, N <= 2^24 and C <= 2^22 keep every pitch inside
+// its bound, and every tile count inside int32: (V / 256) (N / 256) <= 2^30.
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxH = int64_t(1) << 20;
+constexpr int64_t kMaxV = int64_t(1) << 22;
+constexpr int64_t kMaxChunk = int64_t(1) << 22;
+static_assert(kMaxH < kMaxALd && round_up(kMaxV, 256) < kMaxALd && kMaxChunk < kMaxALd,
+              "K-major operand pitches");
+static_assert(round_up(kMaxN, 64) < kMaxBLd && kMaxH < kMaxBLd && kMaxChunk < kMaxBLd,
+              "MN-major operand pitches");
+static_assert((kMaxV / 256) * (kMaxN / 256) < (int64_t(1) << 31), "tile indices");
 
 // Pitch of the transposed kept rows X_c^T [H][ldc].
 static inline int64_t ldc_of(int64_t N) { return round_up(N, 64); }
@@ -140,6 +168,7 @@ static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
     want = kDefaultDzBudget / (2 * round_up(V, 256)) / 256 * 256;
     if (want < 256) want = 256;
   }
+  want = std::min(want, kMaxChunk);  // a memory knob: results do not depend on it
   g.C = N > 0 ? std::min(round_up(want, 256), round_up(N, 256)) : 0;
   g.ldz = round_up(V, 256);
   return g;
@@ -172,13 +201,13 @@ static inline int dx_tail_max(int64_t C, int64_t H, int64_t V) {
   return (int)std::min<int64_t>(256 * (S - 1) / S, dx_tiles_per_chunk(C, H));
 }
 
-// Backward workspace: tile-queue counters (four launches per chunk) | per-row
-// dZ coefficients (float4) and compact targets [tile_rows] | X_c^T [H][ldc] |
-// dZ [C][ldz], both bf16 | fp32 partial dX tiles of a split tail
-// [tail max x pieces][256][256].
+// Backward workspace: the checked copy of the saved header | tile-queue
+// counters (four launches per chunk) | per-row dZ coefficients (float4) and
+// compact targets [tile_rows] | X_c^T of one chunk [H][C] | dZ [C][ldz], both
+// bf16 | fp32 partial dX tiles of a split tail [tail max x pieces][256][256].
 constexpr int kBwdQueueSets = 4;  // dz, dx, dx pieces, dw
 struct BwdWs {
-  size_t q, rc, tg, xct, dz, part, total;
+  size_t chk, q, rc, tg, xct, dz, part, total;
   int64_t nq;  // counters
 };
 static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk) {
@@ -186,11 +215,12 @@ static inline BwdWs bwd_ws(int64_t N, int64_t H, int64_t V, int64_t token_chunk)
   BwdWs w;
   const int64_t nchunks = N > 0 ? (N + g.C - 1) / g.C : 1;
   w.nq = nchunks * kBwdQueueSets * kQueueInts;
-  w.q = 0;
+  w.chk = 0;
+  w.q = w.chk + align256(sizeof(SavedHeader));
   w.rc = w.q + align256((size_t)w.nq * 4);
   w.tg = w.rc + align256((size_t)tile_rows(N) * 16);
   w.xct = w.tg + align256((size_t)tile_rows(N) * 4);
-  w.dz = w.xct + align256((size_t)H * (size_t)ldc_of(N) * 2);
+  w.dz = w.xct + align256((size_t)H * (size_t)g.C * 2);
   w.part = w.dz + align256((size_t)g.C * (size_t)g.ldz * 2);
   w.total = w.part + (size_t)dx_tail_max(g.C, H, V) * dx_pieces(V) * kBM * kBN * 4;
   return w;
@@ -317,6 +347,7 @@ __global__ __launch_bounds__(kScanThreads) void k_compact_scan(int* __restrict__
     hdr->H = H;
     hdr->V = V;
     hdr->flags = flags;
+    hdr->bwd_status = LMHEAD_OK;
   }
 }
 
@@ -392,7 +423,9 @@ __device__ __forceinline__ void stat_merge(float& m, float& s, float& b, float m
 // ---------------------------------------------------------------------------
 // Gathered transpose of the kept rows through LDS in 64 x 64 tiles (bf16),
 // zero-filled past the kept rows so that every tile reads finite values:
-//   k_gather_cols : XcT[h][c] = X[kept_idx[c]][h] (zero for n_kept <= c < ldc)
+//   k_gather_cols : XcT[h][c] = X[kept_idx[c0 + c]][h] for c < ld (zero where
+//                   c0 + c >= n_kept); the forward gathers every kept row
+//                   (c0 = 0), the backward one chunk of them at a time
 // ---------------------------------------------------------------------------
 constexpr int kTp = 64;
 constexpr int kTpPitch = kTp + 8;  // 144-byte rows: column reads hit distinct banks
@@ -430,13 +463,15 @@ __device__ __forceinline__ void tile_store_t(uint16_t (*t)[kTpPitch], uint16_t* 
 
 __global__ __launch_bounds__(256) void k_gather_cols(const uint16_t* __restrict__ X,
                                                      const SavedHeader* __restrict__ hdr,
-                                                     const int32_t* __restrict__ kept_idx, int H,
+                                                     const int32_t* __restrict__ kept_idx,
+                                                     int first, int H,
                                                      uint16_t* __restrict__ XcT, int64_t ldc) {
   __shared__ uint16_t t[kTp][kTpPitch];
   const int n_kept = hdr->n_kept;
   const int c0 = blockIdx.x * kTp, h0 = blockIdx.y * kTp;
   tile_load(t, [&](int r) -> const uint16_t* {
-    return c0 + r < n_kept ? X + (int64_t)kept_idx[c0 + r] * H + h0 : nullptr;
+    const int c = first + c0 + r;
+    return c < n_kept ? X + (int64_t)kept_idx[c] * H + h0 : nullptr;
   });
   __syncthreads();
   tile_store_t(t, XcT + (int64_t)h0 * ldc + c0, ldc);
@@ -477,9 +512,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
 
   TileQueue q(P.queue, ntiles, P.steal);
   for (;;) {
-    // B slot 3 is free here: this wave's loads into it are done, and the
-    // next tile's loads write it only after its first barrier
-    const int t = q.next(rb3);
+    const int t = q.next(ring.b[bcast_slot<SHIFT>()]);
     if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_FWD>(t, mt, nt, tm, tn);
@@ -677,7 +710,7 @@ __global__ __launch_bounds__(256) void k_merge_shards(const float4* __restrict__
                                                       float* __restrict__ logp,
                                                       float* __restrict__ entropy) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i == 0) sv.hdr->flags = flags;
+  if (i == 0) sv.hdr->flags = flags | kFlagComplete;
   if (i >= N) return;
   const int c = sv.pos[i];
   if (c < 0) {
@@ -717,11 +750,46 @@ __global__ void k_zero_ints(int* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
-__global__ void k_zero_rows(const int32_t* __restrict__ pos, int N, int H, float* __restrict__ dX) {
-  const int i = blockIdx.x;
-  if (i >= N || pos[i] >= 0) return;
-  float4* row = reinterpret_cast<float4*>(dX + (int64_t)i * H);
-  for (int k = threadIdx.x; k < H / 4; k += blockDim.x) row[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+// The backward's check of the saved state against its own arguments (the
+// saved header is on the device, and the library does not synchronise).
+// `chk` receives a copy of the header whose n_kept every backward kernel
+// reads: the saved count when the state belongs to this call, else 0, so a
+// mismatched call computes nothing from the saved state, and k_zero_rows
+// then clears every dX row (status != OK). The verdict also goes to the
+// saved header's bwd_status, which lmhead_check_status reports. The state
+// belongs to the call when N and H match, the vocabulary matches (the whole
+// vocabulary, or for a vocabulary shard a range inside the forward's
+// vocabulary), the forward completed LSE and entropy (a shard forward's
+// state only after lmhead_merge_partials), and the entropy-gradient flag
+// matches the forward's.
+__global__ void k_bwd_check(SavedHeader* __restrict__ hdr, int N, int H, int V, int vocab_start,
+                            int shard, int entropy_grad, SavedHeader* __restrict__ chk) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const int flags = hdr->flags;
+  const bool vocab_ok = shard ? (vocab_start >= 0 && (int64_t)vocab_start + V <= hdr->V)
+                              : (hdr->V == V && vocab_start == 0);
+  const bool ok = hdr->N == N && hdr->H == H && vocab_ok && (flags & kFlagComplete) &&
+                  (((flags & kFlagEntropyGrad) != 0) == (entropy_grad != 0)) &&
+                  hdr->n_kept >= 0 && hdr->n_kept <= N;
+  SavedHeader c = *hdr;
+  c.n_kept = ok ? hdr->n_kept : 0;
+  c.status = ok ? LMHEAD_OK : LMHEAD_ERR_INVALID_ARG;
+  *chk = c;
+  hdr->bwd_status = c.status;
+}
+
+// +0.0 dX rows at skipped positions, or at every row when the saved state
+// failed the backward's check. Workgroups stride over the rows (a launch may
+// hold at most 2^32 work-items, fewer than one workgroup per row at N = 2^24).
+constexpr int kZeroRowsGrid = 16384;
+__global__ void k_zero_rows(const int32_t* __restrict__ pos, const SavedHeader* __restrict__ chk,
+                            int N, int H, float* __restrict__ dX) {
+  const bool all = chk->status != LMHEAD_OK;
+  for (int i = blockIdx.x; i < N; i += gridDim.x) {
+    if (!all && pos[i] >= 0) continue;
+    float4* row = reinterpret_cast<float4*>(dX + (int64_t)i * H);
+    for (int k = threadIdx.x; k < H / 4; k += blockDim.x) row[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 }
 
 // Per compact row c, the coefficients of dz as a function of the logit z:
@@ -755,7 +823,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(SavedView sv, const int32_t* _
 
 struct DzParams {
   const uint16_t* W;    // [V][H]
-  const uint16_t* XcT;  // [H][ldc]
+  const uint16_t* XcT;  // [H][ldc]: the chunk's kept rows, transposed
   const float4* rc;     // [tile_rows] dz coefficients per compact row (k_bwd_rows)
   const int32_t* tg;    // [tile_rows] target per compact row, -1 past the kept rows
   SavedView sv;
@@ -792,9 +860,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
 
   TileQueue q(P.queue, ntiles, P.steal);
   for (;;) {
-    // B slot 3 is free here: this wave's loads into it are done, and the
-    // next tile's loads write it only after its first barrier
-    const int t = q.next(rb3);
+    const int t = q.next(ring.b[bcast_slot<SHIFT>()]);
     if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_DZ>(t, mt, nt, tm, tn);
@@ -815,7 +881,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     ASrc A;
     BSrc B;
     A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
-    B.init(P.XcT + P.c0 + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
+    B.init(P.XcT + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     f32x16_t acc[4][4];
     mainloop<SHIFT>(A, B, nk, ring, acc);
     q.claim_ahead();
@@ -950,9 +1016,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
 
   TileQueue q(P.queue, nunits, P.steal);
   for (;;) {
-    // B slot 3 is free here: this wave's loads into it are done, and the
-    // next tile's loads write it only after its first barrier
-    const int u = q.next(rb3);
+    const int u = q.next(ring.b[bcast_slot<SHIFT>()]);
     if (u < 0) break;
     int t = u, k0 = 0;
     if (P.pieces) {
@@ -1054,7 +1118,7 @@ __global__ __launch_bounds__(256) void k_dx_reduce(DxParams P) {
 // dW^T (+)= X_c^T dZ: M = H (A = X_c^T rows), N = vocab (B = dZ: k = chunk
 // rows, vocabulary contiguous), K = chunk rows; stored transposed into dW.
 struct DwParams {
-  const uint16_t* XcT;  // [H][ldc]; this chunk starts at column c0
+  const uint16_t* XcT;  // [H][ldc]: the chunk's kept rows, transposed
   const uint16_t* dZ;   // [C][ldz]
   const SavedHeader* hdr;
   int H, V;
@@ -1084,16 +1148,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
 
   TileQueue q(P.queue, ntiles, P.steal);
   for (;;) {
-    // B slot 3 is free here: this wave's loads into it are done, and the
-    // next tile's loads write it only after its first barrier
-    const int t = q.next(rb3);
+    const int t = q.next(ring.b[bcast_slot<SHIFT>()]);
     if (t < 0) break;
     int tm, tn;
     tile_coords<LMH_GM_DW>(t, mt, nt, tm, tn);
 
     ASrc A;
     BSrc B;
-    A.init(P.XcT + (int64_t)tm * kBM * P.ldc + P.c0, P.ldc, P.H - tm * kBM);
+    A.init(P.XcT + (int64_t)tm * kBM * P.ldc, P.ldc, P.H - tm * kBM);
     B.init(P.dZ + (int64_t)tn * kBN, P.ldz, rows, kBN);  // ldz covers every v of the tile
     f32x16_t acc[4][4];
     mainloop<SHIFT>(A, B, nk, ring, acc);
@@ -1189,9 +1251,7 @@ static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t
 static int check_sizes(int64_t N, int64_t H, int64_t V) {
   if (N < 0 || H <= 0 || V <= 0) return LMHEAD_ERR_INVALID_ARG;
   if (H % 64 != 0) return LMHEAD_ERR_UNSUPPORTED;
-  // int32 indexing of rows and partial offsets; a 256-row operand tile must
-  // fit one buffer descriptor (2^31 bytes)
-  if (N > (1 << 28) || H > (1 << 20) || V > (1 << 22)) return LMHEAD_ERR_UNSUPPORTED;
+  if (N > kMaxN || H > kMaxH || V > kMaxV) return LMHEAD_ERR_UNSUPPORTED;  // see kMaxN
   return LMHEAD_OK;
 }
 
@@ -1227,9 +1287,11 @@ static hipEvent_t prof_event() {
 }
 
 // Launches kernel `k` with the given configuration on stream s; returns a
-// lmhead_status. Records timing events when profiling is on.
-template <typename Kern, typename... Args>
-static int launch(int kind, Kern k, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+// lmhead_status (LMHEAD_ERR_HIP if this launch failed). Records timing events
+// when profiling is on.
+template <typename... KArgs, typename... Args>
+static int launch(int kind, void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                  Args... args) {
   hipEvent_t a = nullptr, b = nullptr;
   {
     std::lock_guard<std::mutex> g(g_prof_mu);
@@ -1239,8 +1301,7 @@ static int launch(int kind, Kern k, dim3 grid, dim3 block, hipStream_t s, Args..
     }
   }
   if (a && b && hipEventRecord(a, s) != hipSuccess) return LMHEAD_ERR_HIP;
-  hipLaunchKernelGGL(k, grid, block, 0, s, args...);
-  if (hipGetLastError() != hipSuccess) return LMHEAD_ERR_HIP;
+  if (lmh_launch::launch_kernel(k, grid, block, s, args...) != hipSuccess) return LMHEAD_ERR_HIP;
   if (a && b) {
     if (hipEventRecord(b, s) != hipSuccess) return LMHEAD_ERR_HIP;
     std::lock_guard<std::mutex> g(g_prof_mu);
@@ -1321,7 +1382,7 @@ static int fwd_impl(const void* hidden, const void* weight, const int32_t* targe
   uint16_t* XcT = reinterpret_cast<uint16_t*>(w + L.xct);
   LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(ldc / kTp), (unsigned)(H / kTp)),
                  dim3(256), s, static_cast<const uint16_t*>(hidden), (const SavedHeader*)sv.hdr,
-                 (const int32_t*)sv.kept_idx, (int)H, XcT, ldc));
+                 (const int32_t*)sv.kept_idx, 0, (int)H, XcT, ldc));
 
   FwdParams P;
   P.W = static_cast<const uint16_t*>(weight);
@@ -1382,8 +1443,10 @@ static int fwd_entry(const void* hidden, const void* weight, const int32_t* targ
   if (entropy_requires_grad && !return_entropy) return LMHEAD_ERR_INVALID_ARG;
   if (!aligned16(hidden) || !aligned16(weight) || !aligned16(saved) || !aligned16(workspace))
     return LMHEAD_ERR_INVALID_ARG;
-  const int flags = (return_entropy ? 1 : 0) | (entropy_requires_grad ? 2 : 0) |
-                    (block > 1 ? 4 : 0);
+  // this call merges the vocabulary tiles itself, so its LSE and entropy are complete
+  const int flags = (return_entropy ? kFlagReturnEntropy : 0) |
+                    (entropy_requires_grad ? kFlagEntropyGrad : 0) |
+                    (block > 1 ? kFlagBlockSparse : 0) | kFlagComplete;
   return fwd_impl(hidden, weight, targets, keep_mask, N, H, V, 0, V, flags, block, logp, entropy,
                   nullptr, saved, saved_bytes, workspace, workspace_bytes,
                   static_cast<hipStream_t>(stream));
@@ -1417,7 +1480,7 @@ LMH_API int lmhead_fwd_partial(const void* hidden, const void* weight_shard,
                                void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_sizes(N, H, V_shard);
   if (st != LMHEAD_OK) return st;
-  if (vocab_start < 0 || V_total > (1 << 22) || vocab_start + V_shard > V_total)
+  if (vocab_start < 0 || V_total > kMaxV || vocab_start + V_shard > V_total)
     return LMHEAD_ERR_INVALID_ARG;
   if (!saved || !weight_shard) return LMHEAD_ERR_INVALID_ARG;
   if (N > 0 && (!hidden || !targets || !partial)) return LMHEAD_ERR_INVALID_ARG;
@@ -1433,14 +1496,15 @@ LMH_API int lmhead_merge_partials(const float* partials, int64_t P, int64_t N,
                                   int return_entropy, int entropy_requires_grad, float* logp,
                                   float* entropy, void* saved, size_t saved_bytes,
                                   void* stream) {
-  if (P < 1 || P > 65536 || N < 0 || N > (1 << 28)) return LMHEAD_ERR_INVALID_ARG;
+  if (P < 1 || P > 65536 || N < 0 || N > kMaxN) return LMHEAD_ERR_INVALID_ARG;
   if (!saved) return LMHEAD_ERR_INVALID_ARG;
   if (N > 0 && (!partials || !logp)) return LMHEAD_ERR_INVALID_ARG;
   if (N > 0 && (return_entropy != 0) != (entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
   if (entropy_requires_grad && !return_entropy) return LMHEAD_ERR_INVALID_ARG;
   if (!aligned16(partials) || !aligned16(saved)) return LMHEAD_ERR_INVALID_ARG;
   if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
-  const int flags = (return_entropy ? 1 : 0) | (entropy_requires_grad ? 2 : 0);
+  const int flags = (return_entropy ? kFlagReturnEntropy : 0) |
+                    (entropy_requires_grad ? kFlagEntropyGrad : 0);
   SavedView sv = saved_view(saved, N);
   const unsigned blocks = (unsigned)(N > 0 ? (N + 255) / 256 : 1);
   return launch(KK_MERGE_SHARDS, k_merge_shards, dim3(blocks), dim3(256),
@@ -1452,24 +1516,28 @@ LMH_API int lmhead_merge_partials(const float* partials, int64_t P, int64_t N,
 // rows [vocab_start, vocab_start + V) (grad_weight is then the shard's rows
 // and grad_hidden this shard's share of dX).
 static int bwd_impl(const void* hidden, const void* weight, const int32_t* targets, int64_t N,
-                    int64_t H, int64_t V, int64_t vocab_start, int entropy_requires_grad,
-                    const void* saved, size_t saved_bytes, const float* grad_logp,
-                    const float* grad_entropy, float* grad_hidden, float* grad_weight,
-                    int64_t token_chunk, void* workspace, size_t workspace_bytes,
-                    hipStream_t s) {
+                    int64_t H, int64_t V, int64_t vocab_start, bool shard,
+                    int entropy_requires_grad, const void* saved, size_t saved_bytes,
+                    const float* grad_logp, const float* grad_entropy, float* grad_hidden,
+                    float* grad_weight, int64_t token_chunk, void* workspace,
+                    size_t workspace_bytes, hipStream_t s) {
   if (saved_bytes < saved_bytes_for(N)) return LMHEAD_ERR_WORKSPACE;
   const BwdWs L = bwd_ws(N, H, V, token_chunk);
   if (workspace_bytes < L.total || (L.total > 0 && !workspace)) return LMHEAD_ERR_WORKSPACE;
   const BwdGeom G = bwd_geom(N, V, token_chunk);
-  if (G.C > (1 << 22)) return LMHEAD_ERR_UNSUPPORTED;
 
-  SavedView sv = saved_view(const_cast<void*>(saved), N);
   char* w = static_cast<char*>(workspace);
+  // Every kernel below reads the kept-row count from the checked copy of the
+  // saved header (k_bwd_check), never from the saved header itself.
+  SavedHeader* chk = reinterpret_cast<SavedHeader*>(w + L.chk);
+  SavedView sv = saved_view(const_cast<void*>(saved), N);
+  LMH_TRY(launch(KK_BWD_ROWS, k_bwd_check, dim3(1), dim3(64), s, sv.hdr, (int)N, (int)H, (int)V,
+                 (int)vocab_start, (int)shard, entropy_requires_grad, chk));
+  sv.hdr = chk;
   uint16_t* XcT = reinterpret_cast<uint16_t*>(w + L.xct);
   uint16_t* dZ = reinterpret_cast<uint16_t*>(w + L.dz);
   const uint16_t* X = static_cast<const uint16_t*>(hidden);
   const uint16_t* Wt = static_cast<const uint16_t*>(weight);
-  const int64_t ldc = ldc_of(N);
   int* queues = reinterpret_cast<int*>(w + L.q);
   float4* rc = reinterpret_cast<float4*>(w + L.rc);
   int32_t* tg = reinterpret_cast<int32_t*>(w + L.tg);
@@ -1481,21 +1549,24 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
     LMH_TRY(launch(KK_BWD_ROWS, k_bwd_rows, dim3((unsigned)(nrows / 256)), dim3(256), s, sv,
                    targets, grad_logp, entropy_requires_grad ? grad_entropy : nullptr, nrows,
                    (int)vocab_start, rc, tg));
-    LMH_TRY(launch(KK_ZERO_ROWS, k_zero_rows, dim3((unsigned)N), dim3(256), s,
-                   (const int32_t*)sv.pos, (int)N, (int)H, grad_hidden));
-    LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols, dim3((unsigned)(ldc / kTp), (unsigned)(H / kTp)),
-                   dim3(256), s, X, (const SavedHeader*)sv.hdr, (const int32_t*)sv.kept_idx,
-                   (int)H, XcT, ldc));
+    LMH_TRY(launch(KK_ZERO_ROWS, k_zero_rows,
+                   dim3((unsigned)std::min<int64_t>(N, kZeroRowsGrid)), dim3(256), s,
+                   (const int32_t*)sv.pos, (const SavedHeader*)chk, (int)N, (int)H, grad_hidden));
   }
   const int nv = n_vtiles(V);
   const int64_t nchunks = N > 0 ? (N + G.C - 1) / G.C : 1;
   for (int64_t ch = 0; ch < nchunks; ++ch) {
     const int c0 = (int)(ch * G.C);
     if (N > 0) {
+      // this chunk's kept rows, transposed: X_c^T [H][C]
+      LMH_TRY(launch(KK_GATHER_COLS, k_gather_cols,
+                     dim3((unsigned)(G.C / kTp), (unsigned)(H / kTp)), dim3(256), s, X,
+                     (const SavedHeader*)chk, (const int32_t*)sv.kept_idx, c0, (int)H, XcT,
+                     G.C));
       DzParams D;
       D.W = Wt;
       D.XcT = XcT;
-      D.ldc = ldc;
+      D.ldc = G.C;
       D.rc = rc;
       D.tg = tg;
       D.sv = sv;
@@ -1566,7 +1637,7 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
     Wp.V = (int)V;
     Wp.c0 = c0;
     Wp.C = (int)G.C;
-    Wp.ldc = ldc;
+    Wp.ldc = G.C;
     Wp.ldz = G.ldz;
     Wp.accumulate = ch > 0;
     Wp.dW = grad_weight;
@@ -1608,7 +1679,7 @@ LMH_API int lmhead_bwd(const void* hidden, const void* weight, const int32_t* ta
   st = bwd_check(hidden, weight, targets, N, entropy_requires_grad, saved, grad_logp,
                  grad_entropy, grad_hidden, grad_weight, workspace);
   if (st != LMHEAD_OK) return st;
-  return bwd_impl(hidden, weight, targets, N, H, V, 0, entropy_requires_grad, saved, saved_bytes,
+  return bwd_impl(hidden, weight, targets, N, H, V, 0, false, entropy_requires_grad, saved, saved_bytes,
                   grad_logp, grad_entropy, grad_hidden, grad_weight, token_chunk, workspace,
                   workspace_bytes, static_cast<hipStream_t>(stream));
 }
@@ -1622,11 +1693,11 @@ LMH_API int lmhead_bwd_partial(const void* hidden, const void* weight_shard,
                                size_t workspace_bytes, void* stream) {
   int st = check_sizes(N, H, V_shard);
   if (st != LMHEAD_OK) return st;
-  if (vocab_start < 0 || vocab_start + V_shard > (1 << 22)) return LMHEAD_ERR_INVALID_ARG;
+  if (vocab_start < 0 || vocab_start + V_shard > kMaxV) return LMHEAD_ERR_INVALID_ARG;
   st = bwd_check(hidden, weight_shard, targets, N, entropy_requires_grad, saved, grad_logp,
                  grad_entropy, grad_hidden, grad_weight_shard, workspace);
   if (st != LMHEAD_OK) return st;
-  return bwd_impl(hidden, weight_shard, targets, N, H, V_shard, vocab_start,
+  return bwd_impl(hidden, weight_shard, targets, N, H, V_shard, vocab_start, true,
                   entropy_requires_grad, saved, saved_bytes, grad_logp, grad_entropy,
                   grad_hidden, grad_weight_shard, token_chunk, workspace, workspace_bytes,
                   static_cast<hipStream_t>(stream));
@@ -1650,7 +1721,7 @@ LMH_API int lmhead_check_status(const void* saved, void* stream) {
   if (hipMemcpyAsync(&h, saved, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
     return LMHEAD_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return LMHEAD_ERR_HIP;
-  return h.status;
+  return h.status != LMHEAD_OK ? h.status : h.bwd_status;
 }
 
 LMH_API const char* lmhead_status_string(int status) {

@@ -19,7 +19,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/lmhead.h"
+#include "launch.h"
 
 #define LMH_API extern "C" __attribute__((visibility("default")))
 
@@ -32,6 +35,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // exponential is 0 next to any real maximum while 0 * value stays finite.
 constexpr float kFloor = -1e30f;
 constexpr int kThreads = 256;
+// One workgroup per row; a launch may hold at most 2^32 work-items, so rows
+// go in launches of at most 2^22 workgroups.
+constexpr int64_t kRowsPerLaunch = int64_t(1) << 22;
 constexpr int kUnroll = 4;
 
 __device__ __forceinline__ float load_one(const uint16_t* p) {
@@ -153,7 +159,7 @@ __device__ __forceinline__ int64_t head_len(const T* row, int64_t V) {
 }
 
 template <class T>
-__global__ __launch_bounds__(kThreads) void k_logits_fwd(const T* __restrict__ logits, int64_t N,
+__global__ __launch_bounds__(kThreads) void k_logits_fwd(const T* __restrict__ logits, int64_t r0,
                                                           int64_t V,
                                                           const int32_t* __restrict__ targets,
                                                           const uint8_t* __restrict__ keep,
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void k_logits_fwd(const T* __restrict__ l
                                                           float* __restrict__ entropy,
                                                           float* __restrict__ stats) {
   __shared__ float red[3][kThreads / 64];
-  const int64_t i = blockIdx.x;
+  const int64_t i = r0 + blockIdx.x;
   const int tid = threadIdx.x;
   if (keep && keep[i] == 0) {
     if (tid == 0) {
@@ -240,10 +246,10 @@ __global__ __launch_bounds__(kThreads) void k_logits_fwd(const T* __restrict__ l
 // logits' precision (bf16 rounds to nearest even); skipped rows get +0.0.
 template <class T>
 __global__ __launch_bounds__(kThreads) void k_logits_bwd(
-    const T* __restrict__ logits, int64_t N, int64_t V, const int32_t* __restrict__ targets,
+    const T* __restrict__ logits, int64_t r0, int64_t V, const int32_t* __restrict__ targets,
     const uint8_t* __restrict__ keep, const float* __restrict__ stats,
     const float* __restrict__ g_lp, const float* __restrict__ g_h, T* __restrict__ grad) {
-  const int64_t i = blockIdx.x;
+  const int64_t i = r0 + blockIdx.x;
   const int tid = threadIdx.x;
   const T* row = logits + i * V;
   T* out = grad + i * V;
@@ -328,17 +334,20 @@ LMH_API int lmhead_logits_fwd(const void* logits, int dtype, int64_t N, int64_t 
   if (st != LMHEAD_OK) return st;
   if (N > 0 && (!targets || !logp || !saved_stats)) return LMHEAD_ERR_INVALID_ARG;
   if (N > 0 && (return_entropy != 0) != (entropy != nullptr)) return LMHEAD_ERR_INVALID_ARG;
-  if (N == 0) return LMHEAD_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == LMHEAD_DTYPE_BF16)
-    hipLaunchKernelGGL(k_logits_fwd<uint16_t>, dim3((unsigned)N), dim3(kThreads), 0, s,
-                       static_cast<const uint16_t*>(logits), N, V, targets, keep_mask, logp,
-                       entropy, saved_stats);
-  else
-    hipLaunchKernelGGL(k_logits_fwd<float>, dim3((unsigned)N), dim3(kThreads), 0, s,
-                       static_cast<const float*>(logits), N, V, targets, keep_mask, logp,
-                       entropy, saved_stats);
-  return hipGetLastError() == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_HIP;
+  for (int64_t r0 = 0; r0 < N; r0 += kRowsPerLaunch) {
+    const dim3 grid((unsigned)std::min<int64_t>(N - r0, kRowsPerLaunch));
+    const hipError_t e =
+        dtype == LMHEAD_DTYPE_BF16
+            ? lmh_launch::launch_kernel(k_logits_fwd<uint16_t>, grid, dim3(kThreads), s,
+                                        static_cast<const uint16_t*>(logits), r0, V, targets,
+                                        keep_mask, logp, entropy, saved_stats)
+            : lmh_launch::launch_kernel(k_logits_fwd<float>, grid, dim3(kThreads), s,
+                                        static_cast<const float*>(logits), r0, V, targets,
+                                        keep_mask, logp, entropy, saved_stats);
+    if (e != hipSuccess) return LMHEAD_ERR_HIP;
+  }
+  return LMHEAD_OK;
 }
 
 LMH_API int lmhead_logits_bwd(const void* logits, int dtype, int64_t N, int64_t V,
@@ -356,17 +365,21 @@ LMH_API int lmhead_logits_bwd(const void* logits, int dtype, int64_t N, int64_t 
   if ((reinterpret_cast<uintptr_t>(grad_logits) & 15) !=
       (reinterpret_cast<uintptr_t>(logits) & 15))
     return LMHEAD_ERR_INVALID_ARG;
-  if (N == 0) return LMHEAD_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == LMHEAD_DTYPE_BF16)
-    hipLaunchKernelGGL(k_logits_bwd<uint16_t>, dim3((unsigned)N), dim3(kThreads), 0, s,
-                       static_cast<const uint16_t*>(logits), N, V, targets, keep_mask,
-                       saved_stats, grad_logp, entropy_requires_grad ? grad_entropy : nullptr,
-                       static_cast<uint16_t*>(grad_logits));
-  else
-    hipLaunchKernelGGL(k_logits_bwd<float>, dim3((unsigned)N), dim3(kThreads), 0, s,
-                       static_cast<const float*>(logits), N, V, targets, keep_mask, saved_stats,
-                       grad_logp, entropy_requires_grad ? grad_entropy : nullptr,
-                       static_cast<float*>(grad_logits));
-  return hipGetLastError() == hipSuccess ? LMHEAD_OK : LMHEAD_ERR_HIP;
+  const float* gh = entropy_requires_grad ? grad_entropy : nullptr;
+  for (int64_t r0 = 0; r0 < N; r0 += kRowsPerLaunch) {
+    const dim3 grid((unsigned)std::min<int64_t>(N - r0, kRowsPerLaunch));
+    const hipError_t e =
+        dtype == LMHEAD_DTYPE_BF16
+            ? lmh_launch::launch_kernel(k_logits_bwd<uint16_t>, grid, dim3(kThreads), s,
+                                        static_cast<const uint16_t*>(logits), r0, V, targets,
+                                        keep_mask, saved_stats, grad_logp, gh,
+                                        static_cast<uint16_t*>(grad_logits))
+            : lmh_launch::launch_kernel(k_logits_bwd<float>, grid, dim3(kThreads), s,
+                                        static_cast<const float*>(logits), r0, V, targets,
+                                        keep_mask, saved_stats, grad_logp, gh,
+                                        static_cast<float*>(grad_logits));
+    if (e != hipSuccess) return LMHEAD_ERR_HIP;
+  }
+  return LMHEAD_OK;
 }

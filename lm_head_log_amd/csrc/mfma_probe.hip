@@ -18,6 +18,7 @@
 
 #include "../../include/lmhead.h"
 #include "gemm_core.h"
+#include "launch.h"
 
 #define LMH_API extern "C" __attribute__((visibility("default")))
 
@@ -137,11 +138,11 @@ LMH_API int lmhead_mfma_probe(const void* a, int64_t a_elems, const void* b, int
   std::vector<unsigned long long> host(grid);
   if (hipEventRecord(e0, s) != hipSuccess) st = LMHEAD_ERR_HIP;
   if (st == LMHEAD_OK) {
-    hipLaunchKernelGGL(k_mfma_probe, dim3(grid), dim3(kThreads), 0, s,
-                       reinterpret_cast<const uint16_t*>(a), groups_of(a_elems),
-                       reinterpret_cast<const uint16_t*>(b), groups_of(b_elems), (int)iters,
-                       cycles, sink);
-    if (hipGetLastError() != hipSuccess) st = LMHEAD_ERR_HIP;
+    if (lmh_launch::launch_kernel(k_mfma_probe, dim3(grid), dim3(kThreads), s,
+                                  reinterpret_cast<const uint16_t*>(a), groups_of(a_elems),
+                                  reinterpret_cast<const uint16_t*>(b), groups_of(b_elems),
+                                  (int)iters, cycles, sink) != hipSuccess)
+      st = LMHEAD_ERR_HIP;
   }
   if (st == LMHEAD_OK && hipEventRecord(e1, s) != hipSuccess) st = LMHEAD_ERR_HIP;
   if (st == LMHEAD_OK && hipEventSynchronize(e1) != hipSuccess) st = LMHEAD_ERR_HIP;

@@ -44,6 +44,18 @@ int main(void) {
   CHECK(lmhead_mfma_probe(fake, 64, NULL, 64, 10, fake, 1 << 20, NULL, NULL, NULL, NULL) ==
         LMHEAD_ERR_INVALID_ARG);
 
+  /* size limits: N <= 2^24, H <= 2^20, V <= 2^22 */
+  const int64_t max_n = (int64_t)1 << 24;
+  CHECK(lmhead_fwd_workspace_bytes(max_n, 64, 1000) > 0);
+  CHECK(lmhead_fwd_workspace_bytes(max_n + 1, 64, 1000) == 0);
+  CHECK(lmhead_bwd_workspace_bytes(max_n + 1, 64, 1000, 0) == 0);
+  CHECK(lmhead_fwd(fake, fake, fake, NULL, max_n + 1, 64, 100, 1, 1, ffake, ffake, fake, 1 << 20,
+                   fake, 1 << 30, NULL) == LMHEAD_ERR_UNSUPPORTED);
+  CHECK(lmhead_bwd(fake, fake, fake, max_n + 1, 64, 100, 0, fake, 1 << 20, ffake, NULL, ffake,
+                   ffake, 0, fake, 1 << 30, NULL) == LMHEAD_ERR_UNSUPPORTED);
+  CHECK(lmhead_fwd(fake, fake, fake, NULL, 8, 64, ((int64_t)1 << 22) + 1, 1, 1, ffake, ffake, fake,
+                   1 << 20, fake, 1 << 30, NULL) == LMHEAD_ERR_UNSUPPORTED);
+
   if (failures == 0) printf("abi client: all checks passed\n");
   return failures == 0 ? 0 : 1;
 }

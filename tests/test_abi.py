@@ -86,9 +86,13 @@ def _fwd_ws(N, H, V):
             + _align(H * up64(N) * 2))
 
 
+MAX_N, MAX_H, MAX_V, MAX_CHUNK = 1 << 24, 1 << 20, 1 << 22, 1 << 22
+
+
 def _bwd_ws(N, H, V, chunk):
     up = lambda x, m: (x + m - 1) // m * m
     want = chunk if chunk > 0 else max(256, (8 << 30) // (2 * up(V, 256)) // 256 * 256)
+    want = min(want, MAX_CHUNK)
     C = min(up(want, 256), up(N, 256)) if N > 0 else 0
     nchunks = (N + C - 1) // C if N > 0 else 1
     rows = up(N, 256)
@@ -98,8 +102,10 @@ def _bwd_ws(N, H, V, chunk):
     if V >= 16384:
         pieces = 8 if 8 * up(-(-V // 8), 64) <= up(V, 256) else 4
     tail = min(256 * (pieces - 1) // pieces, C // 256 * up(H, 256) // 256) if pieces > 1 else 0
-    return (_align(nchunks * 4 * 32) + _align(16 * rows) + _align(4 * rows)
-            + _align(H * up(N, 64) * 2) + _align(C * up(V, 256) * 2)
+    # checked copy of the saved header | queues | dz coefficients | targets |
+    # one chunk of X_c^T | dZ of one chunk | partial dX tiles
+    return (256 + _align(nchunks * 4 * 32) + _align(16 * rows) + _align(4 * rows)
+            + _align(H * C * 2) + _align(C * up(V, 256) * 2)
             + tail * pieces * 256 * 256 * 4)
 
 
@@ -113,15 +119,42 @@ def test_workspace_sizes(lib):
     # V = 131072 (4 GiB)
     N, H, V = 16384, 4096, 131072
     assert _bwd_ws(N, H, V, 0) == _bwd_ws(N, H, V, 16384)
-    # the 4096-row chunking has four chunks' tile-queue counters instead of one
+    # the 4096-row chunking holds one chunk of dZ and of X_c^T instead of the
+    # whole batch's, and four chunks' tile-queue counters instead of one
     queues = _align(4 * 4 * 32) - _align(1 * 4 * 32)
-    assert _bwd_ws(N, H, V, 0) - _bwd_ws(N, H, V, 4096) == (16384 - 4096) * V * 2 - queues
+    assert (_bwd_ws(N, H, V, 0) - _bwd_ws(N, H, V, 4096)
+            == (16384 - 4096) * (V + H) * 2 - queues)
     assert _bwd_ws(262144, 4096, 152064, 0) == _bwd_ws(262144, 4096, 152064, 28160)
     # invalid sizes
     assert lib.lmhead_fwd_workspace_bytes(10, 100, 1000) == 0
     assert lib.lmhead_fwd_workspace_bytes(-1, 64, 1000) == 0
     assert lib.lmhead_bwd_workspace_bytes(10, 64, 0, 0) == 0
     assert lib.lmhead_fwd_workspace_bytes(10, 64, (1 << 22) + 1) == 0
+
+
+def test_size_limits(lib):
+    """N <= 2^24, H <= 2^20, V <= 2^22: every operand's buffer descriptors then
+    stay below 2^31 bytes and every tile index inside int32; past them the
+    size queries return 0 and the calls return LMHEAD_ERR_UNSUPPORTED."""
+    assert lib.lmhead_fwd_workspace_bytes(MAX_N, 64, 1000) == _fwd_ws(MAX_N, 64, 1000)
+    assert lib.lmhead_fwd_workspace_bytes(MAX_N + 1, 64, 1000) == 0
+    assert lib.lmhead_fwd_workspace_bytes(16, MAX_H, 1000) > 0
+    assert lib.lmhead_fwd_workspace_bytes(16, MAX_H + 64, 1000) == 0
+    assert lib.lmhead_fwd_workspace_bytes(16, 64, MAX_V) > 0
+    assert lib.lmhead_fwd_workspace_bytes(16, 64, MAX_V + 1) == 0
+    assert lib.lmhead_bwd_workspace_bytes(MAX_N, 256, 1000, 0) == _bwd_ws(MAX_N, 256, 1000, 0)
+    assert lib.lmhead_bwd_workspace_bytes(MAX_N + 1, 256, 1000, 0) == 0
+    # the token chunk is clamped to 2^22 rows, whatever is asked for
+    assert _bwd_ws(MAX_N, 256, 256, 0) == _bwd_ws(MAX_N, 256, 256, MAX_CHUNK)
+    assert (lib.lmhead_bwd_workspace_bytes(MAX_N, 256, 256, 1 << 23)
+            == lib.lmhead_bwd_workspace_bytes(MAX_N, 256, 256, MAX_CHUNK))
+    assert _fwd(lib, N=MAX_N + 1) == 2
+    assert _fwd(lib, entry="lmhead_fwd_blocksparse", N=MAX_N + 1) == 2
+    assert _fwd(lib, V=MAX_V + 1) == 2
+    assert _bwd(lib, N=MAX_N + 1) == 2
+    assert _fwdp(lib, N=MAX_N + 1) == 2
+    assert _bwdp(lib, N=MAX_N + 1) == 2
+    assert _merge(lib, N=MAX_N + 1) == 1
 
 
 FAKE = ctypes.c_void_p(0x10000)   # 16-byte aligned, never dereferenced

@@ -209,3 +209,31 @@ def test_logits_entry_against_the_pages_accuracy_table():
     say(f"bf16 logits: grad err {e_g:.2e} vs the unrounded reference (exact path on the "
         f"same bf16 logits: {e_best:.2e}; page 7.2e-3 on its logits)")
     assert e_g <= e_best + float(_bf16_ulp(1.0))
+
+
+def test_logits_entry_rows_past_one_launch():
+    """More rows than one launch takes (the rows go in launches of 2^22
+    workgroups): N = 2^22 + 5 rows of V = 5 fp32 logits, with a mask. Every
+    row is checked against the oracle, in float64 on the host."""
+    N, V = (1 << 22) + 5, 5
+    say(f"case: logits N{N} V{V} fp32, two launches")
+    z, t, keep, g_lp, g_h = _case(N, V, 47)
+    host, dev = _device_logits(z, torch.float32)
+    td = torch.from_numpy(t).cuda()
+    km = torch.from_numpy(keep).cuda()
+    glp = torch.from_numpy(g_lp).cuda()
+    gh = torch.from_numpy(g_h).cuda()
+    lp, ent, stats = lmh.lmhead_logits_fwd(dev, td, km, True)
+    gz = lmh.lmhead_logits_bwd(dev, td, stats, glp, gh, True, km)
+    torch.cuda.synchronize()
+    kept = np.flatnonzero(keep)
+    ref = oracle.logits_input_fwd_bwd(host[kept], t[kept], g_lp[kept], g_h[kept], True)
+    lp_h, ent_h = lp.cpu().numpy(), ent.cpu().numpy()
+    e_lp = np.abs(lp_h[kept] - ref["logp"]).max()
+    e_h = np.abs(ent_h[kept] - ref["entropy"]).max()
+    eg = rel_fro(_grad_to_f64(gz)[kept], ref["dlogits"])
+    say(f"rows past one launch: logp {e_lp:.2e} entropy {e_h:.2e} grad {eg:.2e}")
+    assert e_lp <= TOL_LOGP and e_h <= TOL_ENT and eg <= TOL_GRAD_REL
+    skipped = np.flatnonzero(keep == 0)
+    assert_pos_zero(lp_h[skipped], "logp skipped")
+    assert_pos_zero(gz.cpu().numpy()[skipped], "grad skipped")
