@@ -1,9 +1,17 @@
 // gemm_core.h - bf16 MFMA tile engine for gfx950 (CDNA4).
 //
 // One workgroup of 256 threads (4 wave64s arranged 2 x 2) computes a 256 x 256
-// fp32 tile C[m][n] = sum_k A[m][k] * B[n][k] with v_mfma_f32_32x32x16_bf16.
-// Each wave owns a 128 x 128 sub-tile held as 4 x 4 MFMA accumulator blocks
-// (256 AGPRs).
+// fp32 tile C[m][n] = sum_k A[m][k] * B[n][k] with v_mfma_f32_16x16x32_bf16.
+// Each wave owns a 128 x 128 sub-tile held as 8 x 8 MFMA accumulator blocks
+// of 16 x 16 (256 AGPRs).
+//
+// Why 16 x 16 x 32: under this load the chip runs at the clock its power
+// limit allows, and at equal flops the 16 x 16 x 32 instruction draws less
+// power than 32 x 32 x 16 (it moves half the accumulator bytes per flop).
+// With operands in registers and the bench batch's bit statistics, measured
+// on MI355X: 16 x 16 x 32 reaches 2.05 PFLOP/s at 2.00 GHz, 32 x 32 x 16
+// 1.81 PFLOP/s at 1.73 GHz. Per k step of 32 the two shapes read the same
+// operand bytes from LDS.
 //
 // Operand layouts in global memory, one of each per GEMM:
 //   A : K-major, [m][ld] with k contiguous (e.g. W[v][h] for Z = W X^T);
@@ -14,13 +22,13 @@
 // Both operands are loaded straight from global memory into LDS with
 // buffer_load_dwordx4 ... lds (no VGPR staging); a buffer descriptor's record
 // count zero-fills rows past the end of a matrix. K advances in stages of
-// kBK = 32; each stage issues four loads per wave for each operand, spread
-// over the stage's MFMAs (one load per four MFMAs): a CU moves about 150 GB/s
-// through these loads, twice what its MFMAs consume on average, so loads
-// bunched into part of a stage stall the issuing wave. One barrier per stage
-// publishes stage k + 1 and releases the LDS of stage k - 1. MFMA fragments
-// are double-buffered in registers: the fragments of the next 16-wide k step
-// are read from LDS while the current step's 16 MFMAs issue.
+// kBK = 32, one MFMA k step of 64 MFMAs per wave; each stage issues four
+// loads per wave for each operand, spread over the stage's MFMAs. MFMA
+// fragments are double-buffered in registers: while a stage's 64 MFMAs
+// issue, the fragments of the next stage are read from LDS, spread over the
+// stage. One barrier per stage, at its start, publishes the next stage (whose
+// fragments the stage reads) and releases the LDS of the current one (whose
+// fragments were read during the previous stage).
 //
 // LDS (160 KiB, all of it):
 //   A ring: three slots of one k pair (64 k, two stages), 32 KiB each. A row
@@ -28,27 +36,29 @@
 //     bytes at a time would split every line across two requests, and the L2
 //     fetches each 64-byte sector on its own miss. The 16-byte chunk index
 //     is XOR-swizzled with (row >> 1) & 7, which keeps the fragment reads
-//     (ds_read_b128, lane l: row l % 32, chunk 2 kq + l / 32) free of bank
-//     conflicts. The loads of pair p + 2 go into the slot pair p - 1
-//     released, half in each stage of pair p.
+//     (ds_read_b128, lane l: row l % 16, chunk 4 sub + l / 16) free of bank
+//     conflicts. The loads of pair p + 2 go into the slot of pair p - 1,
+//     half in each stage of pair p.
 //   B ring: four slots of one stage (32 k rows of 256 n, 512 bytes each:
 //     whole lines), 16 KiB each, laid out as 8 groups of 4 consecutive k rows,
-//     2 KiB per group. Inside a group the 64-byte piece (32 n values) of k row
-//     e in 32-wide n block s sits at byte (4 s + e) * 64. Fragments are read
-//     with ds_read_b64_tr_b16, which hands lane i of each 16-lane group element
-//     i % 4 of the 8 bytes addressed by lane 4 e + i / 4 as its element e:
-//     pointing lane 4 e + q at k row k0 + e, n n0 + 4 q gives lane i the
-//     values (n n0 + i, k k0 .. k0 + 3), the MFMA fragment shape; two such
-//     reads give the 8 k of a fragment. A half wave reads 4 whole pieces that
-//     are adjacent in LDS (256 contiguous bytes): no bank conflicts. The loads
-//     of stage k + 3 go into the slot stage k - 1 released.
-// A transpose read moves half the bytes of a ds_read_b128 in about the same
-// LDS time, so the engine reads one operand (A) with ds_read_b128.
+//     2 KiB per group. Inside group G the 64-byte piece (32 n values) of k row
+//     e in 32-wide n block s sits at byte (4 s + e) * 64, and its two 32-byte
+//     halves (16 n values each) are swapped when bit 1 of G is set. Fragments
+//     are read with ds_read_b64_tr_b16, which hands lane i of each 16-lane
+//     group element i % 4 of the 8 bytes addressed by lane 4 e + i / 4 as its
+//     element e: pointing lane 4 e + q at k row k0 + e, n n0 + 4 q gives lane
+//     i the values (n n0 + i, k k0 .. k0 + 3); two such reads (groups 2 g and
+//     2 g + 1) give the 8 k of a fragment. The two 16-lane groups of a half
+//     wave read the same 16 columns of groups 2 g and 2 g + 2 (g = 0, 1),
+//     whose swapped halves put them on disjoint banks: 256 bytes over all 64
+//     banks, no conflicts. The loads of stage t + 4 go into the slot of stage
+//     t, free once the barrier that starts stage t has passed.
 //
-// MFMA 32x32x16 bf16 register layout (lane l of 64):
-//   A fragment: row  l % 32, k = 8 * (l / 32) + [0..7]
-//   B fragment: col  l % 32, k = 8 * (l / 32) + [0..7]
-//   D (16 fp32): col l % 32, row = 8 * (r / 4) + 4 * (l / 32) + (r % 4)
+// MFMA 16x16x32 bf16 register layout (lane l of 64, g = l / 16):
+//   A fragment: row  l % 16, k = 8 g + [0..7] (16-byte chunk g of the stage)
+//   B fragment: col  l % 16, k = 8 g + [0..7]
+//   D (4 fp32): col  l % 16, row = 4 g + r
+// (The k order inside a fragment only has to agree between A and B.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -58,7 +68,6 @@ namespace lmh {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
@@ -174,9 +183,9 @@ struct ASrc {
       off[j] = wr < wrows ? (uint32_t)(wr * ld * 2 + c * 16) : kOOB;
     }
   }
-  // Issue half h (loads 4 h .. 4 h + 3) of this wave's loads of k pair p into
-  // the A slot at `dst`; pairs at or past np read as zeros.
-  __device__ __forceinline__ void issue_half(int p, int np, int h, char* dst) const {
+  // Issue load j (0..7) of this wave's loads of k pair p into the A slot at
+  // `dst`; pairs at or past np read as zeros.
+  __device__ __forceinline__ void issue_one(int p, int np, int j, char* dst) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     char* base = dst + wave * (kBM / 4) * kARowBytes;
     // the k offset rides in the scalar soffset field; rows past the end keep
@@ -184,19 +193,21 @@ struct ASrc {
     const bool live = p < np;
     const int koff = __builtin_amdgcn_readfirstlane(live ? p * kARowBytes : 0);
     const __amdgpu_buffer_rsrc_t r = live ? rsrc : none;
-#pragma unroll
-    for (int jj = 0; jj < kALoadsPerWavePair / 2; ++jj) {
-      const int j = h * (kALoadsPerWavePair / 2) + jj;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + j * 1024), 16, off[j], koff,
-                                               0, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + j * 1024), 16, off[j], koff, 0,
+                                             0);
   }
-  // Fragment of 16-wide k step kq (0..3) of the pair, 32-row block i of the
+  __device__ __forceinline__ void issue_pair(int p, int np, char* dst) const {
+#pragma unroll
+    for (int j = 0; j < kALoadsPerWavePair; ++j) issue_one(p, np, j, dst);
+  }
+  // Fragment of stage `sub` (0, 1) of the pair, 16-row block i (0..7) of the
   // wave's 128-row half `half`.
-  static __device__ __forceinline__ bf16x8_t frag(const char* slot, int kq, int lane, int half,
+  static __device__ __forceinline__ bf16x8_t frag(const char* slot, int sub, int lane, int half,
                                                   int i) {
-    const int o = a_lds_off(lane & 31, kq * 2 + (lane >> 5));  // swizzle depends on lane & 31 only
-    return *reinterpret_cast<const bf16x8_t*>(slot + (half * 128 + i * 32) * kARowBytes + o);
+    // the swizzle depends on lane & 15 only: 16-row blocks start at rows
+    // that are multiples of 16
+    const int o = a_lds_off(lane & 15, 4 * sub + (lane >> 4));
+    return *reinterpret_cast<const bf16x8_t*>(slot + (half * 128 + i * 16) * kARowBytes + o);
   }
 };
 
@@ -224,7 +235,9 @@ struct BSrc {
     const int lane = lane_fresh();
     const int e = (lane >> 2) & 3;     // k row inside the group
     const int blk = lane >> 4;         // 32-wide n block inside the half
-    const int cq = lane & 3;           // 16-byte chunk inside the piece
+    // 16-byte chunk inside the piece: the wave fills groups 2 wave and
+    // 2 wave + 1, whose bit 1 is wave & 1; there the 32-byte halves swap
+    const int cq = (lane & 3) ^ ((wave & 1) << 1);
 #pragma unroll
     for (int j = 0; j < kBLoadsPerWaveStage; ++j) {
       // load j fills half (j & 1) of group 2 wave + j / 2 of the stage; its
@@ -234,38 +247,41 @@ struct BSrc {
       off[j] = col < n_valid ? (uint32_t)(row * pitch + col * 2) : kOOB;
     }
   }
-  // Issue this wave's loads of stage kt into the B slot at `dst`. The
-  // descriptor is rebased to the wave's first k row of the stage, and its
-  // record count covers only the valid rows among the wave's 8 (none at or
-  // past k_rows).
-  __device__ __forceinline__ void issue(int kt, char* dst) const {
+  // The descriptor of this wave's loads of stage kt: rebased to the wave's
+  // first k row of the stage, its record count covering only the valid rows
+  // among the wave's 8 (none at or past k_rows).
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(int kt) const {
     constexpr int kWaveRows = kBK / 4;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    char* ldsb = dst + wave * 2 * kMnGroupBytes;
     int rows = k_valid - kt * kBK;
     rows = rows < 0 ? 0 : (rows > kWaveRows ? kWaveRows : rows);
     void* p = reinterpret_cast<void*>(uniform_u64(base + (uint64_t)((int64_t)kt * kBK * pitch)));
     const int bytes = __builtin_amdgcn_readfirstlane((int)(rows * pitch));
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p, (short)0, bytes,
-                                                                       kRsrcWord3);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, bytes, kRsrcWord3);
+  }
+  // Issue load j (0..3) of a stage with descriptor r into the B slot at `dst`.
+  __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t r, int j, char* dst) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    char* ldsb = dst + wave * 2 * kMnGroupBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_ptr_t)(ldsb + (j >> 1) * kMnGroupBytes + (j & 1) * 1024), 16, off[j], 0, 0, 0);
+  }
+  __device__ __forceinline__ void issue(int kt, char* dst) const {
+    const __amdgpu_buffer_rsrc_t r = stage_rsrc(kt);
 #pragma unroll
-    for (int j = 0; j < kBLoadsPerWaveStage; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (lds_ptr_t)(ldsb + (j >> 1) * kMnGroupBytes + (j & 1) * 1024), 16, off[j], 0, 0, 0);
+    for (int j = 0; j < kBLoadsPerWaveStage; ++j) issue_one(r, j, dst);
   }
   static __device__ __forceinline__ bf16x4_t tr_read(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(lds_ptr_t)(p));
   }
-  // Fragment of k step kk (0..1) of the stage, 32-wide n block i of the
-  // wave's 128 half `half`.
-  static __device__ __forceinline__ bf16x8_t frag(const char* slot, int kk, int lane, int half,
-                                                  int i) {
-    // lane 16 g + 4 e + q reads k row 16 kk + 8 (g >> 1) + 4 h + e at n
-    // 128 half + 32 i + 16 (g & 1) + 4 q, for the two halves h of the fragment
+  // Fragment of 16-column block j (0..7) of the wave's 128-column half `half`.
+  static __device__ __forceinline__ bf16x8_t frag(const char* slot, int lane, int half, int j) {
+    // lane 16 g + 4 e + q reads k rows 8 g + e (group 2 g) and 8 g + 4 + e
+    // (group 2 g + 1) at n = 128 half + 16 j + 4 q: 32-wide block
+    // 4 half + j / 2, 32-byte half (j & 1) ^ (g & 1) of the piece
     const int g = lane >> 4;
-    const int lane_part = (g >> 1) * 2 * kMnGroupBytes + ((lane >> 2) & 3) * kMnPieceBytes +
-                          (g & 1) * 32 + (lane & 3) * 8;
-    const char* p = slot + kk * 4 * kMnGroupBytes + (half * 4 + i) * 4 * kMnPieceBytes + lane_part;
+    const int lane_part = g * 2 * kMnGroupBytes + ((lane >> 2) & 3) * kMnPieceBytes +
+                          (((j & 1) ^ (g & 1)) << 5) + (lane & 3) * 8;
+    const char* p = slot + (half * 4 + (j >> 1)) * 4 * kMnPieceBytes + lane_part;
     const bf16x4_t lo = tr_read(p);
     const bf16x4_t hi = tr_read(p + kMnGroupBytes);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -411,89 +427,146 @@ struct Ring {
   __shared__ __attribute__((aligned(1024))) char rb3[lmh::kBSlotBytes];    \
   const lmh::Ring ring = {{ra0, ra1, ra2}, {rb0, rb1, rb2, rb3}}
 
+// The fragments of one stage: A blocks a[i] (16 rows each) and B blocks b[j]
+// (16 columns each) of the wave's 128 x 128 sub-tile.
 struct Frags {
-  bf16x8_t a[4], b[4];
+  bf16x8_t a[8], b[8];
 };
 
-// Fragments of one 16-wide k step: A data is k step kq (0..3) of the pair in
-// slot `as`, B data is k step kk (0..1) of the stage in slot `bs`.
-__device__ __forceinline__ void read_frags(const char* as, int kq, const char* bs, int kk,
-                                           int lane, int wm, int wn, Frags& f) {
-  // first-use order of mfma_step: a0 with b0..b3, then a1, a2, a3
-  f.a[0] = ASrc::frag(as, kq, lane, wm, 0);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = BSrc::frag(bs, kk, lane, wn, j);
-#pragma unroll
-  for (int i = 1; i < 4; ++i) f.a[i] = ASrc::frag(as, kq, lane, wm, i);
-}
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef f32x4_t Acc[8][8];  // the wave's accumulators, block (i, j) at acc[i][j]
 
-__device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][4]) {
+// Fragments of the stage held in A slot `as` (stage `sub` of its pair) and
+// B slot `bs`. B and A reads alternate so that the slower transposing reads
+// start early.
+__device__ __forceinline__ void read_frags(const char* as, int sub, const char* bs, int lane,
+                                           int wm, int wn, Frags& f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-}
-
-// sched_group_barrier masks
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmemRead = 0x020;
-constexpr int kSchedDsRead = 0x100;
-constexpr int kReadsPerStep = 4 * 1 + 4 * 2;  // A: one ds_read_b128, B: two transpose reads
-
-// Interleaves the 16 MFMAs of a k step with its 12 LDS reads (one after each
-// of the first 12 MFMAs) and its 4 loads (one per four MFMAs).
-template <int ID>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, ID);
-    if (i % 4 == 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, ID);
-    if (i < kReadsPerStep) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, ID);
+  for (int j = 0; j < 8; ++j) {
+    f.b[j] = BSrc::frag(bs, lane, wn, j);
+    f.a[j] = ASrc::frag(as, sub, lane, wm, j);
   }
-  __builtin_amdgcn_sched_barrier(0);
 }
 
-// Stage s = s0 + U of the main loop (s0 a multiple of 12, so every slot
-// index below is a compile-time constant). On entry f0 holds stage s's
-// kk = 0 fragments. Step 1 runs kk = 0 while reading kk = 1 into f1 and
-// issuing half of pair s / 2 + 2's A loads (into the slot pair s / 2 - 1
-// released). Then every wave waits for its loads of stage s + 1 (at most the
-// 8 loads of stage s - 1 and the 4 just issued may remain) and for its LDS
-// reads, and the barrier publishes stage s + 1 and releases stage s's B slot
-// and, after the pair's second stage, its A slot. Step 2 runs kk = 1 while
-// reading stage s + 1's kk = 0 fragments and issuing stage s + 3's B loads
-// (into the slot stage s - 1 released).
+// One MFMA accumulating in place into the AGPR quad that holds c. The
+// builtin form lets the compiler pick a separate destination quad, and with
+// 64 accumulators filling the AGPRs it then shuttles results through vector
+// registers (hundreds of copies per stage); tied in place, every accumulator
+// keeps its quad. The compiler does not see this as an MFMA, so it inserts no
+// hazard waits for it: an accumulator is used again only 64 MFMAs later, and
+// acc_fence (below) separates the last MFMA from any other read.
+__device__ __forceinline__ void mfma16(f32x4_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Every accumulator quad of the wave as an in/out AGPR operand of an asm
+// statement.
+#define LMH_ACC_OPERANDS(c) \
+    "+a"(c[0][0]), "+a"(c[0][1]), "+a"(c[0][2]), "+a"(c[0][3]), "+a"(c[0][4]), \
+    "+a"(c[0][5]), "+a"(c[0][6]), "+a"(c[0][7]), "+a"(c[1][0]), "+a"(c[1][1]), \
+    "+a"(c[1][2]), "+a"(c[1][3]), "+a"(c[1][4]), "+a"(c[1][5]), "+a"(c[1][6]), \
+    "+a"(c[1][7]), "+a"(c[2][0]), "+a"(c[2][1]), "+a"(c[2][2]), "+a"(c[2][3]), \
+    "+a"(c[2][4]), "+a"(c[2][5]), "+a"(c[2][6]), "+a"(c[2][7]), "+a"(c[3][0]), \
+    "+a"(c[3][1]), "+a"(c[3][2]), "+a"(c[3][3]), "+a"(c[3][4]), "+a"(c[3][5]), \
+    "+a"(c[3][6]), "+a"(c[3][7]), "+a"(c[4][0]), "+a"(c[4][1]), "+a"(c[4][2]), \
+    "+a"(c[4][3]), "+a"(c[4][4]), "+a"(c[4][5]), "+a"(c[4][6]), "+a"(c[4][7]), \
+    "+a"(c[5][0]), "+a"(c[5][1]), "+a"(c[5][2]), "+a"(c[5][3]), "+a"(c[5][4]), \
+    "+a"(c[5][5]), "+a"(c[5][6]), "+a"(c[5][7]), "+a"(c[6][0]), "+a"(c[6][1]), \
+    "+a"(c[6][2]), "+a"(c[6][3]), "+a"(c[6][4]), "+a"(c[6][5]), "+a"(c[6][6]), \
+    "+a"(c[6][7]), "+a"(c[7][0]), "+a"(c[7][1]), "+a"(c[7][2]), "+a"(c[7][3]), \
+    "+a"(c[7][4]), "+a"(c[7][5]), "+a"(c[7][6]), "+a"(c[7][7])
+
+// The compiler treats the asm MFMAs as opaque, so it cannot honour their
+// hazards: a VALU write of an accumulator (its zeroing) must not be placed
+// right before the first MFMA that reads it, and no read may follow the last
+// MFMA too closely. acc_pin, after the zeroing, makes every accumulator live
+// in its AGPR at that point; being volatile it stays ahead of the main loop's
+// prologue (loads, barrier, fragment reads), which keeps the zeroing writes
+// far from the first MFMAs. (Sunk next to their MFMAs they corrupted the
+// first and last register of some quads.)
+__device__ __forceinline__ void acc_pin(Acc& c) { asm volatile("" : LMH_ACC_OPERANDS(c)); }
+
+// 24 wait states, more than an MFMA's write-to-read distance, depending on
+// every accumulator: no read of an accumulator (ours or the compiler's) can be
+// placed between the main loop's last MFMAs and this.
+__device__ __forceinline__ void acc_fence(Acc& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : LMH_ACC_OPERANDS(c));
+}
+
+constexpr int kMfmaPerStage = 64;
+// The next stage's fragment reads go out as 16 units (B block u / 2 -- two
+// transposing reads -- for even u, A block u / 2 for odd u), unit u after
+// MFMA (7 u) / 2: spread over the first 53 MFMAs so that the last reads land
+// well before the next barrier. The slower transposing reads go first.
+constexpr int kReadUnits = 16;
+__host__ __device__ constexpr int read_slot(int u) { return (7 * u) / 2; }
+__host__ __device__ constexpr int read_unit_at(int m) {
+  const int u = (2 * m + 6) / 7;  // the one unit whose slot can be m
+  return (u < kReadUnits && read_slot(u) == m) ? u : -1;
+}
+__host__ __device__ constexpr int count_read_slots() {
+  int n = 0;
+  for (int m = 0; m < 64; ++m) n += read_unit_at(m) >= 0;
+  return n;
+}
+static_assert(count_read_slots() == kReadUnits && read_slot(kReadUnits - 1) < kMfmaPerStage,
+              "every read unit has exactly one MFMA slot");
+// The stage's 8 loads go out after MFMAs 4, 12, .., 60: A loads first, then B.
+__host__ __device__ constexpr int load_at(int m) { return m % 8 == 4 ? m / 8 : -1; }
+
+// Stage t (U = t + SHIFT mod 12, a compile-time stage of the 12-stage
+// period, so every slot index below is a compile-time constant). On entry
+// `cur` holds stage t's fragments (read during stage t - 1) and stage t + 1's
+// operands are landing. Every wave waits for its loads of stage t + 1 and for
+// its fragment reads of stage t; the barrier then publishes stage t + 1 and
+// releases stage t's B slot (and, after the pair's second stage, its A slot).
+// The 64 MFMAs of stage t run on `cur` while stage t + 1's fragments are read
+// into `nxt`, half of pair t / 2 + 2's A loads go into the slot pair
+// t / 2 - 1 released, and stage t + 4's B loads go into stage t's slot. The
+// order is fixed by hand (sched_barrier after every MFMA): the compiler's
+// scheduler does not see the asm MFMAs as MFMAs.
+//
+// Loads issued per stage, in order: 4 of A, then 4 of B. At the start of
+// stage t the loads needed are B stage t + 1 (issued in stage t - 3) and,
+// when t + 1 starts a pair, that pair's second half (issued in stage t - 2,
+// before its B loads); the loads issued after them number 16 (t even) or
+// 12 (t odd).
 template <int U>
-__device__ __forceinline__ void k_stage(const ASrc& A, const BSrc& B, int s, int np,
+__device__ __forceinline__ void k_stage(const ASrc& A, const BSrc& B, int t, int np,
                                         const Ring& R, int lane, int wm, int wn, Frags& f0,
-                                        Frags& f1, f32x16_t (&acc)[4][4]) {
-  static_assert(kLoadsPerWaveStage == 8, "the wait below assumes 8 loads per stage");
-  constexpr int a_cur = (U / 2) % 3, a_nxt = ((U + 1) / 2) % 3, a_fre = (U / 2 + 2) % 3;
-  constexpr int b_cur = U % 4, b_nxt = (U + 1) % 4, b_fre = (U + 3) % 4;
-  constexpr int sub = U % 2, sub_nxt = (U + 1) % 2;
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags(R.a[a_cur], 2 * sub + 1, R.b[b_cur], 1, lane, wm, wn, f1);
-  A.issue_half(s / 2 + 2, np, sub, R.a[a_fre]);
-  mfma_step(f0, acc);
-  interleave<0>();
-  wait_vmcnt<kLoadsPerWaveStage + kALoadsPerWavePair / 2>();
+                                        Frags& f1, Acc& acc) {
+  static_assert(kLoadsPerWaveStage == 8, "the waits below assume 8 loads per stage");
+  constexpr int a_nxt = ((U + 1) / 2) % 3, sub_nxt = (U + 1) % 2;
+  constexpr int a_fre = (U / 2 + 2) % 3, b_nxt = (U + 1) % 4, b_fre = U % 4;
+  Frags& cur = (U % 2) ? f1 : f0;
+  Frags& nxt = (U % 2) ? f0 : f1;
+  wait_vmcnt<(U % 2) ? 12 : 16>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_frags(R.a[a_nxt], 2 * sub_nxt, R.b[b_nxt], 0, lane, wm, wn, f0);
-  B.issue(s + 3, R.b[b_fre]);
-  mfma_step(f1, acc);
-  interleave<1>();
+  const __amdgpu_buffer_rsrc_t brs = B.stage_rsrc(t + 4);
+  const int pair = t / 2 + 2;
+#pragma unroll
+  for (int m = 0; m < kMfmaPerStage; ++m) {
+    mfma16(acc[m / 8][m % 8], cur.a[m / 8], cur.b[m % 8]);
+    const int q = load_at(m);
+    if (q >= 0 && q < 4) A.issue_one(pair, np, (U % 2) * 4 + q, R.a[a_fre]);
+    if (q >= 4) B.issue_one(brs, q - 4, R.b[b_fre]);
+    const int u = read_unit_at(m);
+    if (u >= 0 && u % 2 == 0) nxt.b[u / 2] = BSrc::frag(R.b[b_nxt], lane, wn, u / 2);
+    if (u >= 0 && u % 2 == 1) nxt.a[u / 2] = ASrc::frag(R.a[a_nxt], sub_nxt, lane, wm, u / 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Accumulates the tile over nk stages of kBK. The caller must have made the
 // LDS free (barrier) before the call; on return every wave has finished its
 // LDS reads and no load is in flight. The slots are distinct __shared__
 // objects and the loop is unrolled by 12 (the periods of the two rings are
-// 6 and 4 stages), so every LDS access names a fixed slot: the compiler can
-// then see that fragment reads never alias the direct-to-LDS loads in flight
-// into other slots, and inserts no waits of its own.
+// 6 and 4 stages, of the fragment sets 2), so every LDS access names a fixed
+// slot: the compiler can then see that fragment reads never alias the
+// direct-to-LDS loads in flight into other slots, and inserts no waits of
+// its own.
 //
 // SHIFT (even, 0..10) starts the slot rotation at virtual stage SHIFT: the
 // first 12 - SHIFT stages run as straight-line copies of bodies SHIFT..11
@@ -504,7 +577,7 @@ __device__ __forceinline__ void k_stage(const ASrc& A, const BSrc& B, int s, int
 // fragments inside the loop).
 template <int SHIFT = 0>
 __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, const Ring& R,
-                                         f32x16_t (&acc)[4][4]) {
+                                         Acc& acc) {
   static_assert(SHIFT % 2 == 0 && SHIFT >= 0 && SHIFT < 12, "A pairs must stay aligned");
   constexpr int kPeel = (12 - SHIFT) % 12;
   // fresh per call: the fragment addresses derived from them are computed per
@@ -515,35 +588,33 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
   const int wn = wave & 1;
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+  acc_pin(acc);
   if (nk <= 0) return;
   const int np = (nk + 1) / 2;
 
-  // Issue order matters: each stage's wait counts loads issued after the ones
-  // it needs. At stage 0's wait, B stage 1 must be older than the last 12
-  // loads (A pair 1's second half, B stage 2, pair 2's first half).
+  // Prologue: pairs 0 and 1, stages 0..3. Stage 3 goes into the B slot that
+  // carries the tile index (bcast_slot) and so only after the first barrier.
   constexpr int a0 = (SHIFT / 2) % 3, a1 = (SHIFT / 2 + 1) % 3;
-  constexpr int b0 = SHIFT % 4, b1 = (SHIFT + 1) % 4, b2 = (SHIFT + 2) % 4;
-  static_assert(b0 != bcast_slot<SHIFT>() && b1 != bcast_slot<SHIFT>() &&
-                    b2 != bcast_slot<SHIFT>(),
-                "the prologue must not load the tile-index slot before its first barrier");
-  A.issue_half(0, np, 0, R.a[a0]);
-  A.issue_half(0, np, 1, R.a[a0]);
+  constexpr int b0 = SHIFT % 4, b1 = (SHIFT + 1) % 4, b2 = (SHIFT + 2) % 4, b3 = (SHIFT + 3) % 4;
+  static_assert(b3 == bcast_slot<SHIFT>(), "the tile-index slot is loaded after the barrier");
+  A.issue_pair(0, np, R.a[a0]);
   B.issue(0, R.b[b0]);
   B.issue(1, R.b[b1]);
-  A.issue_half(1, np, 0, R.a[a1]);
-  A.issue_half(1, np, 1, R.a[a1]);
+  A.issue_pair(1, np, R.a[a1]);
   B.issue(2, R.b[b2]);
   // pair 0 and stage 0 landed: only stage 1, pair 1 and stage 2 may remain
-  wait_vmcnt<kALoadsPerWavePair + 2 * kBLoadsPerWaveStage>();
+  wait_vmcnt<2 * kBLoadsPerWaveStage + kALoadsPerWavePair>();
   __builtin_amdgcn_s_barrier();
+  B.issue(3, R.b[b3]);
 
   Frags f0, f1;
-  read_frags(R.a[a0], 0, R.b[b0], 0, lane, wm, wn, f0);
+  // stage 0 is fragment set SHIFT % 2 = 0
+  read_frags(R.a[a0], 0, R.b[b0], lane, wm, wn, f0);
   if constexpr (kPeel > 0) {
 #define LMH_PEEL(U) \
   if constexpr (U >= SHIFT) k_stage<U>(A, B, sgpr_fresh(U - SHIFT), np, R, lane, wm, wn, f0, f1, acc);
@@ -557,24 +628,24 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
     LMH_STAGE(6) LMH_STAGE(7) LMH_STAGE(8) LMH_STAGE(9) LMH_STAGE(10) LMH_STAGE(11)
 #undef LMH_STAGE
   }
-  // stages and pairs past the end issued loads that nobody reads; let them land
+  // stages and pairs past the end issued loads and fragment reads that
+  // nobody uses; let them land
   wait_vmcnt<0>();
   wait_lgkm0();
+  acc_fence(acc);
 }
 
 // Epilogue reads of the accumulators. The compiler, left to itself, copies
 // every accumulator block to vector registers right after the main loop (the
 // copies land in the loop's exit block, ahead of the epilogue's branches),
 // which fills the register file and serialises the epilogue. acc_read moves
-// one accumulator register where its value is used. The hardware does not
-// interlock an accumulator read on an MFMA still writing it, and the compiler
-// does not see into the asm, so every acc_read takes the token of an
-// acc_read_fence (24 wait states, more than the write-to-read distance of
-// even a 16-pass MFMA) issued after the main loop: no read is scheduled
-// above it.
+// one accumulator register where its value is used. Every acc_read takes the
+// token of an acc_read_fence issued after the main loop, so none is scheduled
+// above it; the main loop itself ends with acc_fence, which keeps every read
+// of an accumulator the MFMA write-to-read distance away from the last MFMA.
 __device__ __forceinline__ int acc_read_fence() {
   int tok;
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_mov_b32 %0, 0" : "=s"(tok) : : "memory");
+  asm volatile("s_mov_b32 %0, 0" : "=s"(tok) : : "memory");
   return tok;
 }
 __device__ __forceinline__ float acc_read(float x, int tok) {
@@ -590,9 +661,7 @@ __host__ __device__ constexpr int stage_shift(int nk) { return (12 - nk % 12) % 
 // block i: acc_row_fixed(i, r) + acc_row_lane(lane). Epilogues compare the
 // compile-time part against a per-tile lane bound, so the compiler has no
 // per-register lane values to keep live across the tile loop.
-__host__ __device__ constexpr int acc_row_fixed(int i, int r) {
-  return i * 32 + 8 * (r >> 2) + (r & 3);
-}
-__device__ __forceinline__ int acc_row_lane(int lane) { return 4 * (lane >> 5); }
+__host__ __device__ constexpr int acc_row_fixed(int i, int r) { return i * 16 + r; }
+__device__ __forceinline__ int acc_row_lane(int lane) { return 4 * (lane >> 4); }
 
 }  // namespace lmh

@@ -517,20 +517,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     int tm, tn;
     tile_coords<LMH_GM_FWD>(t, mt, nt, tm, tn);
 
-    // targets of this lane's four tokens, loaded before the main loop so that
-    // their latency is hidden under it
-    int tgt[4];
+    // targets of this lane's eight tokens (columns 16 j + lane % 16 of the
+    // wave's 128), loaded before the main loop so that their latency is
+    // hidden under it
+    int tgt[8];
     {
-      const int* tp = P.tg + tn * kBN + (wave_fresh() & 1) * 128 + (lane_fresh() & 31);
+      const int* tp = P.tg + tn * kBN + (wave_fresh() & 1) * 128 + (lane_fresh() & 15);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) tgt[j] = tp[j * 32];
+      for (int j = 0; j < 8; ++j) tgt[j] = tp[j * 16];
     }
 
     ASrc A;
     BSrc B;
     A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
     B.init(P.XcT + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
-    f32x16_t acc[4][4];
+    Acc acc;
     mainloop<SHIFT>(A, B, nk, ring, acc);
     q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
@@ -543,42 +544,43 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     const int vlim = P.V - vbase - acc_row_lane(lane);  // rows acc_row_fixed < vlim are valid
     __syncthreads();  // every wave is done reading the ring
     const int fence = acc_read_fence();
-    // Per token (column j of this lane): m = max y, s = sum 2^(y - m) and
-    // b = sum 2^(y - m) (y - m) over this lane's 64 vocabulary rows, merged
-    // with the other half of the wave (the other 64 rows) and staged in LDS
-    // for the merge of the two wave rows; then the target pick. The masked
+    // Per token (column 16 j + lane % 16 of the wave): m = max y,
+    // s = sum 2^(y - m) and b = sum 2^(y - m) (y - m) over this lane's 32
+    // vocabulary rows (16 i + 4 (lane / 16) + r), merged with the three other
+    // lanes that hold the token's other rows of the wave's 128 and staged in
+    // LDS for the merge of the two wave rows; then the target pick. The masked
     // form leaves out rows at or past V, which only the last vocabulary tile
     // has; a lane with no valid row gives the empty partial (-inf, 0, 0).
     auto columns = [&](auto masked_t) {
       constexpr bool kMasked = decltype(masked_t)::value;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int cl = wn * 128 + j * 32 + (lane & 31);  // token inside the tile
+      for (int j = 0; j < 8; ++j) {
+        const int cl = wn * 128 + j * 16 + (lane & 15);  // token inside the tile
         const int c = tn * kBN + cl;                     // compact row
-        // this lane's 64 logits of the token, each accumulator read once; the
+        // this lane's 32 logits of the token, each accumulator read once; the
         // masked form replaces rows at or past V by a large finite negative
         // logit, whose 2^(y - m) is exactly 0 next to any real maximum while
         // 0 * y stays finite
-        // (the row limit is made opaque per column so that the 64 row masks
+        // (the row limit is made opaque per column so that the 32 row masks
         // are recomputed, not kept in scalar registers across columns)
         int vl = vlim;
         if (kMasked) asm volatile("" : "+v"(vl));
-        float v[64];
+        float v[32];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            v[i * 16 + r] =
+          for (int r = 0; r < 4; ++r)
+            v[i * 4 + r] =
                 (!kMasked || acc_row_fixed(i, r) < vl) ? acc_read(acc[i][j][r], fence) : -1e30f;
         float mx = v[0];
 #pragma unroll
-        for (int k = 1; k < 64; ++k) mx = fmaxf(mx, v[k]);
+        for (int k = 1; k < 32; ++k) mx = fmaxf(mx, v[k]);
         if (kMasked && vlim <= 0) mx = -INFINITY;  // no valid row: the empty partial
         float m = (mx == -INFINITY) ? -INFINITY : mx * kLog2e;
         float s = 0.f, b = 0.f;
         if (mx != -INFINITY) {
 #pragma unroll
-          for (int k = 0; k < 64; ++k) {
+          for (int k = 0; k < 32; ++k) {
             // y = z log2 e - m: 0 up to the rounding of m at the maximum
             const float y = fmaf(v[k], kLog2e, -m);
             const float e = __builtin_amdgcn_exp2f(y);
@@ -586,25 +588,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
             b = fmaf(e, y, b);
           }
         }
-        const float mo = __shfl_xor(m, 32);
-        const float so = __shfl_xor(s, 32);
-        const float bo = __shfl_xor(b, 32);
-        stat_merge(m, s, b, mo, so, bo);
-        if (lane < 32) {
+#pragma unroll
+        for (int x = 16; x <= 32; x <<= 1) {
+          const float mo = __shfl_xor(m, x);
+          const float so = __shfl_xor(s, x);
+          const float bo = __shfl_xor(b, x);
+          stat_merge(m, s, b, mo, so, bo);
+        }
+        if (lane < 16) {
           red[wm][0][cl] = m;
           red[wm][1][cl] = s;
           red[wm][2][cl] = b;
         }
         // exactly one lane in the grid holds z[t] for a kept token (the
-        // target of a token past the kept rows is -1 and never hits)
+        // target of a token past the kept rows is -1 and never hits): row
+        // local = 16 i + 4 g + r of the wave's 128 sits in lane group g
         const int local = tgt[j] - vbase;
-        const int w = local & 31;
-        const bool hit = local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
+        const bool hit = local >= 0 && local < 128 && ((local >> 2) & 3) == (lane >> 4);
         if (hit) {
-          const int want = (local >> 5) * 16 + ((w >> 3) << 2) + (w & 3);
+          const int want = (local >> 4) * 4 + (local & 3);
           float z = 0.f;
 #pragma unroll
-          for (int k = 0; k < 64; ++k) z = (want == k) ? v[k] : z;
+          for (int k = 0; k < 32; ++k) z = (want == k) ? v[k] : z;
           P.zt[c] = z;
         }
         // one column at a time: keeps the copies of the accumulators out of
@@ -837,7 +842,6 @@ struct DzParams {
 };
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // bf16 pairs: (__bf16)x rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
@@ -865,16 +869,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     int tm, tn;
     tile_coords<LMH_GM_DZ>(t, mt, nt, tm, tn);
 
-    // coefficients and targets of this lane's four tokens, loaded before the
-    // main loop so that their latency is hidden under it
-    float4 rcv[4];
-    int tgt[4];
+    // coefficients and targets of this lane's eight tokens (columns
+    // 16 j + lane % 16 of the wave's 128), loaded before the main loop so that
+    // their latency is hidden under it
+    float4 rcv[8];
+    int tgt[8];
     {
-      const int c = P.c0 + tn * kBN + (wave_fresh() & 1) * 128 + (lane_fresh() & 31);
+      const int c = P.c0 + tn * kBN + (wave_fresh() & 1) * 128 + (lane_fresh() & 15);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        rcv[j] = P.rc[c + j * 32];
-        tgt[j] = P.tg[c + j * 32];
+      for (int j = 0; j < 8; ++j) {
+        rcv[j] = P.rc[c + j * 16];
+        tgt[j] = P.tg[c + j * 16];
       }
     }
 
@@ -882,7 +887,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     BSrc B;
     A.init(P.W + (int64_t)tm * kBM * P.H, P.H, P.V - tm * kBM);
     B.init(P.XcT + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
-    f32x16_t acc[4][4];
+    Acc acc;
     mainloop<SHIFT>(A, B, nk, ring, acc);
     q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
@@ -897,61 +902,63 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     // columns of dZ hold finite values that no consumer uses (dX = dZ W reads
     // W rows at or past V as zero; dW^T never stores columns at or past V).
     //
-    // dZ leaves through LDS: a lane's registers hold 4 consecutive entries of
-    // 32 different token rows, so direct stores would write 8-byte pieces of
-    // 32 rows per instruction. Each wave stages its 32 tokens x 128 entries
-    // of one column block j (8 KiB, a private quarter of ring slot 0) and
-    // stores them back in row order, four 256-byte row segments per
+    // dZ leaves through LDS: a lane's registers hold, per token, runs of 4
+    // consecutive vocabulary entries (rows 16 i + 4 (lane / 16) + 0..3), so
+    // direct stores would write 8-byte pieces. Each wave stages 32 tokens x
+    // 128 entries (two column blocks j, 8 KiB: a private quarter of ring slot
+    // 0) and stores them back in row order, four 256-byte row segments per
     // instruction. Staging layout: token t (0..31) at t * 256 bytes, its
     // 16-byte chunk q (8 entries) at chunk q ^ (t & 15), so both the
-    // register-order writes and the row-order reads are free of bank
-    // conflicts. A wave's LDS accesses are performed in order, so the region
-    // is reused for every j without a barrier.
+    // register-order writes (32 lanes: 16 tokens x 2 halves of a chunk) and
+    // the row-order reads are free of bank conflicts. A wave's LDS accesses
+    // are performed in order, so the region is reused for every pair of
+    // column blocks without a barrier.
     __syncthreads();  // every wave is done reading the ring
     char* stage = ring.a[0] + wave * 8192;
+    const int g = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 k = rcv[j];  // {LSE log2 e, ca - cb LSE, cb, g_lp}
-      const int local = tgt[j] - vbase;
-      const int w = local & 31;
-      const bool hit = local >= 0 && local < 128 && ((w >> 2) & 1) == (lane >> 5);
-      const int want = (local >> 5) * 16 + ((w >> 3) << 2) + (w & 3);
-      const int t = lane & 31;  // this lane's token in the wave's block
-      char* trow = stage + t * 256 + (lane >> 5) * 8;
+    for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float d[16];
+      for (int jh = 0; jh < 2; ++jh) {
+        const int j = 2 * jj + jh;
+        const float4 k = rcv[j];  // {LSE log2 e, ca - cb LSE, cb, g_lp}
+        const int local = tgt[j] - vbase;
+        const bool hit = local >= 0 && local < 128 && ((local >> 2) & 3) == g;
+        const int want = (local >> 4) * 4 + (local & 3);  // i * 4 + r of the target
+        const int t = 16 * jh + (lane & 15);  // this lane's token in the staged 32
+        char* trow = stage + t * 256 + (g & 1) * 8;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float z = acc_read(acc[i][j][r], fence);
-          const float p = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -k.x));
-          d[r] = kEntGrad ? p * fmaf(k.z, z, k.y) : p * k.y;
-        }
-        // the one-hot term of the target, in the one lane that holds it
-        if (hit && (want >> 4) == i) {
+        for (int i = 0; i < 8; ++i) {
+          float d[4];
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if ((want & 15) == r) d[r] += k.w;
-        }
-        // register group g: entries i * 32 + 8 g + 4 (lane >> 5) + 0..3 of the wave's 128
+          for (int r = 0; r < 4; ++r) {
+            const float z = acc_read(acc[i][j][r], fence);
+            const float p = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -k.x));
+            d[r] = kEntGrad ? p * fmaf(k.z, z, k.y) : p * k.y;
+          }
+          // the one-hot term of the target, in the one lane that holds it
+          if (hit && (want >> 2) == i) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int q = i * 4 + g;
-          const bf16x2_t lo = {(__bf16)d[4 * g + 0], (__bf16)d[4 * g + 1]};
-          const bf16x2_t hi = {(__bf16)d[4 * g + 2], (__bf16)d[4 * g + 3]};
+            for (int r = 0; r < 4; ++r)
+              if ((want & 3) == r) d[r] += k.w;
+          }
+          // entries 16 i + 4 g + 0..3: half (g & 1) of chunk 2 i + g / 2
+          const int q = 2 * i + (g >> 1);
+          const bf16x2_t lo = {(__bf16)d[0], (__bf16)d[1]};
+          const bf16x2_t hi = {(__bf16)d[2], (__bf16)d[3]};
           *reinterpret_cast<uint2*>(trow + ((q ^ (t & 15)) << 4)) =
               make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
         }
-        // one register block at a time (bounds the live copies)
+        // one column block at a time (bounds the live copies)
         __builtin_amdgcn_sched_barrier(0);
       }
-      // rows 4 u .. 4 u + 3 of the block per instruction, 16 lanes a row
+      // rows 4 u .. 4 u + 3 of the 32 per instruction, 16 lanes a row
       const int q = lane & 15;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int tr = 4 * u + (lane >> 4);
         const uint4 x = *reinterpret_cast<const uint4*>(stage + tr * 256 + ((q ^ (tr & 15)) << 4));
-        const int c = tn * kBN + wn * 128 + j * 32 + tr;  // chunk row
+        const int c = tn * kBN + wn * 128 + jj * 32 + tr;  // chunk row
         // non-temporal: 4 GiB of dZ streams past the caches the operand panels use
         const u32x4_t v = {x.x, x.y, x.z, x.w};
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(P.dZ + (int64_t)c * P.ldz + vbase + q * 8));
@@ -1033,7 +1040,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     A.init(P.dZ + (int64_t)tm * kBM * P.ldz + k0, P.ldz, rows - tm * kBM);
     B.init(P.W + (int64_t)k0 * P.H + (int64_t)tn * kBN, P.H,
            P.pieces ? min(P.kp, P.V - k0) : P.V, P.H - tn * kBN);
-    f32x16_t acc[4][4];
+    Acc acc;
     mainloop<SHIFT>(A, B, nk, ring, acc);
     q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
@@ -1041,39 +1048,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     const int lane = lane_fresh(), wave = wave_fresh();
     const int wm = wave >> 1, wn = wave & 1;
 
-    // dX rows leave through LDS: a lane holds, per register, one column of
-    // a row, so direct stores wrote 4-byte pieces (and looked up the row's
-    // original position once per register). Each wave stages one 32-row block
-    // of its 128 x 128 (16 KiB, a private half of ring slot 0 or 1) and
-    // stores whole 512-byte row segments, two rows per instruction, looking
-    // up each row's position once.
+    // dX rows leave through LDS: a lane holds, per register, one column of a
+    // row (row 16 i + 4 (lane / 16) + r, column 16 j + lane % 16), so direct
+    // stores would write 4-byte pieces. Each wave stages the 16 rows x 128
+    // columns of one row block i (8 KiB, a private quarter of ring slot 0;
+    // row t at t * 512 bytes, 16-byte chunk q at chunk q ^ t) and stores whole
+    // 512-byte row segments, two rows per instruction, looking up each row's
+    // position once. The writes (4 rows x 16 columns per instruction) and the
+    // row reads are free of bank conflicts.
     const int fence = acc_read_fence();
     __syncthreads();  // every wave is done reading the ring
-    float* stage = reinterpret_cast<float*>((wave < 2 ? ra0 : ra1) + (wave & 1) * 16384);
+    float* stage = reinterpret_cast<float*>(ra0 + wave * 8192);
     const int m0 = tm * kBM + wm * 128;  // first chunk row of the wave's block
     const int n0 = tn * kBN + wn * 128;  // first h of the wave's block
+    const int g = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // row 8 (r / 4) + 4 (lane / 32) + r % 4 of the block, column j * 32 + lane % 32;
-      // rows of 128 floats, 16-byte chunk q of row t at chunk q ^ (t & 31)
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * g + r;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = j * 32 + (lane & 31);
-          stage[t * 128 + ((((col >> 2) ^ (t & 31))) << 2) + (col & 3)] =
-              acc_read(acc[i][j][r], fence);
+        for (int j = 0; j < 8; ++j) {
+          const int col = j * 16 + (lane & 15);
+          stage[t * 128 + (((col >> 2) ^ t) << 2) + (col & 3)] = acc_read(acc[i][j][r], fence);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
       const int q = lane & 31;  // 16-byte chunk of the row
 #pragma unroll
-      for (int uu = 0; uu < 16; ++uu) {
+      for (int uu = 0; uu < 8; ++uu) {
         const int t = 2 * uu + (lane >> 5);
-        const int m = m0 + i * 32 + t;
+        const int m = m0 + i * 16 + t;
         const int h = n0 + q * 4;
-        const float4 x = *reinterpret_cast<const float4*>(stage + t * 128 + ((q ^ (t & 31)) << 2));
+        const float4 x = *reinterpret_cast<const float4*>(stage + t * 128 + ((q ^ t) << 2));
         if (P.pieces)  // the whole partial tile, row-major
           *reinterpret_cast<float4*>(P.part + (int64_t)u * (kBM * kBN) +
                                      (m - tm * kBM) * kBN + (h - tn * kBN)) = x;
@@ -1157,7 +1164,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     BSrc B;
     A.init(P.XcT + (int64_t)tm * kBM * P.ldc, P.ldc, P.H - tm * kBM);
     B.init(P.dZ + (int64_t)tn * kBN, P.ldz, rows, kBN);  // ldz covers every v of the tile
-    f32x16_t acc[4][4];
+    Acc acc;
     mainloop<SHIFT>(A, B, nk, ring, acc);
     q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
@@ -1165,36 +1172,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     const int lane = lane_fresh(), wave = wave_fresh();
     const int wm = wave >> 1, wn = wave & 1;
 
-    // dW leaves through LDS the way dZ does in k_dz_tiles: each wave stages
-    // its 32 vocabulary rows x 128 h of column block j (16 KiB, a private
-    // half of ring slot 0 or 1; row t at t * 512 bytes, 16-byte chunk q (4 h)
-    // at chunk q ^ t) and stores two 512-byte row segments per instruction.
+    // dW leaves through LDS the way dZ does in k_dz_tiles. A lane holds, per
+    // vocabulary row 16 j + lane % 16, runs of 4 consecutive h (16 i +
+    // 4 (lane / 16) + 0..3): one 16-byte chunk of the row. Each wave stages
+    // the 16 vocabulary rows x 128 h of one column block j (8 KiB, a private
+    // quarter of ring slot 0; row t at t * 512 bytes, chunk q at chunk q ^ t)
+    // and stores two 512-byte row segments per instruction.
     const int fence = acc_read_fence();
     __syncthreads();  // every wave is done reading the ring
-    char* stage = (wave < 2 ? ra0 : ra1) + (wave & 1) * 16384;
+    char* stage = ra0 + wave * 8192;
     const int h0 = tm * kBM + wm * 128;  // first h of the wave's rows
+    const int g = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = lane & 31;  // this lane's vocabulary row in the wave's block
+    for (int j = 0; j < 8; ++j) {
+      const int t = lane & 15;  // this lane's vocabulary row in the wave's block
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          // register group g: h = i * 32 + 8 g + 4 (lane >> 5) + 0..3 of the wave's 128
-          const int q = i * 8 + 2 * g + (lane >> 5);
-          const float4 x = make_float4(
-              acc_read(acc[i][j][4 * g], fence), acc_read(acc[i][j][4 * g + 1], fence),
-              acc_read(acc[i][j][4 * g + 2], fence), acc_read(acc[i][j][4 * g + 3], fence));
-          *reinterpret_cast<float4*>(stage + t * 512 + ((q ^ t) << 4)) = x;
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 8; ++i) {
+        const int q = i * 4 + g;  // h = 4 q .. 4 q + 3 of the wave's 128
+        const float4 x = make_float4(
+            acc_read(acc[i][j][0], fence), acc_read(acc[i][j][1], fence),
+            acc_read(acc[i][j][2], fence), acc_read(acc[i][j][3], fence));
+        *reinterpret_cast<float4*>(stage + t * 512 + ((q ^ t) << 4)) = x;
       }
+      __builtin_amdgcn_sched_barrier(0);
       // rows 2 u, 2 u + 1 of the block per instruction, 32 lanes a row
       const int q = lane & 31;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int tr = 2 * u + (lane >> 5);
-        const int v = tn * kBN + wn * 128 + j * 32 + tr;
+        const int v = tn * kBN + wn * 128 + j * 16 + tr;
         const int h = h0 + q * 4;
         if (v < P.V && h < P.H) {  // H is a multiple of 4: a chunk is whole
           float4 x = *reinterpret_cast<const float4*>(stage + tr * 512 + ((q ^ tr) << 4));

@@ -1,10 +1,10 @@
 // mfma_probe.hip - benchmark-only measurement of the MFMA ceiling the GEMM
 // kernels run against on the device at hand.
 //
-// The GEMMs of the op issue v_mfma_f32_32x32x16_bf16 in 4 x 4 blocks per
-// wave, four waves per CU, one workgroup per CU. This kernel issues exactly
-// that step with every operand already in registers: no loads, no LDS, no
-// barriers, no epilogue. Its rate is therefore the most the GEMM engine could
+// The GEMMs of the op issue v_mfma_f32_16x16x32_bf16 in 8 x 8 blocks per
+// wave (the engine's in-place form), four waves per CU, one workgroup per CU.
+// This kernel issues exactly that step with every operand already in
+// registers: no loads, no LDS, no barriers, no epilogue. Its rate is therefore the most the GEMM engine could
 // reach at the clock the chip holds under that MFMA load. The chip lowers its
 // clock with the power the matrix cores draw, and that power depends on how
 // often operand bits change, so the operands can be taken from the caller's
@@ -25,7 +25,7 @@
 namespace lmh {
 namespace {
 
-constexpr int kProbeSets = 4;  // fragment sets cycled through, one per k step
+constexpr int kProbeSets = 2;  // fragment sets cycled through, one per k step
 constexpr int kProbeWavesPerGroup = kThreads / 64;
 constexpr int64_t kProbeMaxIters = int64_t(1) << 24;
 
@@ -50,19 +50,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_mfma_probe(
 #pragma unroll
   for (int s = 0; s < kProbeSets; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       // a distinct 16-byte piece of each source per (wave, set, fragment, lane)
-      const uint32_t slot = ((gw * kProbeSets + s) * 4 + i) * 64 + lane;
+      const uint32_t slot = ((gw * kProbeSets + s) * 8 + i) * 64 + lane;
       f[s].a[i] = probe_frag(a, a_groups, slot);
       f[s].b[i] = probe_frag(b, b_groups, slot);
     }
-  f32x16_t acc[4][4];
+  Acc acc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+  acc_pin(acc);
 
   __syncthreads();  // the fragments of every wave are in registers
   __builtin_amdgcn_sched_barrier(0);
@@ -70,8 +71,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_mfma_probe(
   __builtin_amdgcn_sched_barrier(0);
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int s = 0; s < kProbeSets; ++s) mfma_step(f[s], acc);
+    for (int s = 0; s < kProbeSets; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mfma16(acc[i][j], f[s].a[i], f[s].b[j]);
   }
+  acc_fence(acc);
   __builtin_amdgcn_sched_barrier(0);
   const unsigned long long t1 = __builtin_amdgcn_s_memtime();
   __builtin_amdgcn_sched_barrier(0);
@@ -79,11 +85,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mfma_probe(
   // keep every product live: one sum per thread
   float x = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x += acc[i][j][r];
+      for (int r = 0; r < 4; ++r) x += acc[i][j][r];
   sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = x;
   if (threadIdx.x == 0) cycles[blockIdx.x] = t1 - t0;
 }
@@ -156,9 +162,9 @@ LMH_API int lmhead_mfma_probe(const void* a, int64_t a_elems, const void* b, int
   (void)hipEventDestroy(e1);
   if (st != LMHEAD_OK) return st;
 
-  // 16 MFMAs of 2 * 32 * 32 * 16 flops per set and iteration, per wave
-  const double fl = (double)grid * kProbeWavesPerGroup * (double)iters * kProbeSets * 16.0 *
-                    (2.0 * 32 * 32 * 16);
+  // 64 MFMAs of 2 * 16 * 16 * 32 flops per set and iteration, per wave
+  const double fl = (double)grid * kProbeWavesPerGroup * (double)iters * kProbeSets * 64.0 *
+                    (2.0 * 16 * 16 * 32);
   double cyc = 0.0;
   for (int i = 0; i < grid; ++i) cyc += (double)host[i];
   cyc /= grid;
