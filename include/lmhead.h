@@ -156,6 +156,31 @@ int lmhead_fwd_blocksparse(const void* hidden, const void* weight, const int32_t
                            void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). It is lmhead_fwd with its workspace in a device array built
+ * into the library: LMHEAD_NOALLOC_SCRATCH_BYTES bytes on each GPU the
+ * library runs on, held until the process ends. The call allocates nothing
+ * (no hipMalloc, no hipFree, no allocating library routine, no timing events
+ * while lmhead_profile_begin is on). Same arguments, outputs and saved state
+ * as lmhead_fwd, without the workspace; the backward is lmhead_bwd.
+ *  Errors: as lmhead_fwd, plus LMHEAD_ERR_WORKSPACE when
+ *  lmhead_fwd_workspace_bytes(N, H, V) exceeds LMHEAD_NOALLOC_SCRATCH_BYTES
+ *  (e.g. N 8192, H 4096, V 131072 fits; N 16384 at that H and V does not),
+ *  and LMHEAD_ERR_HIP if the array's device address cannot be obtained.
+ * Every call on a GPU uses that GPU's one array, which keeps the last call's
+ * contents (each call rewrites what it reads). Calls that overlap on one GPU
+ * -- on different streams, or from host threads whose work is not ordered
+ * on one stream -- race; calls in one stream's order do not.
+ */
+#define LMHEAD_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int lmhead_fwd_noalloc(const void* hidden, const void* weight, const int32_t* targets,
+                       const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V,
+                       int return_entropy, int entropy_requires_grad,
+                       float* logp, float* entropy,
+                       void* saved, size_t saved_bytes,
+                       void* stream);
+
 /* Backward: per chunk of `token_chunk` kept rows, recompute the logit tile,
  * form dZ (above) in bf16, then dX rows = dZ W (scattered back to the rows'
  * original positions) and dW (+)= dZ^T X. The first chunk writes dW, later

@@ -24,7 +24,8 @@ from ._lib import LMHeadError, check
 
 __all__ = [
     "lmhead_saved_bytes", "lmhead_fwd_workspace_bytes", "lmhead_bwd_workspace_bytes",
-    "lmhead_fwd", "lmhead_fwd_blocksparse", "lmhead_bwd", "lmhead_read_n_kept",
+    "lmhead_fwd", "lmhead_fwd_blocksparse", "lmhead_fwd_noalloc", "lmhead_bwd",
+    "lmhead_read_n_kept", "NOALLOC_SCRATCH_BYTES",
     "lmhead_check_status",
     "lmhead_status_string", "lmhead_version", "fused_logprobs", "LMHeadError",
     "DEFAULT_TOKEN_CHUNK", "lmhead_kernel_name", "lmhead_profile_begin", "lmhead_profile_end",
@@ -121,13 +122,15 @@ def lmhead_fwd(hidden, weight, targets, keep_mask=None, return_entropy=False,
     sb = int(L.lmhead_saved_bytes(N))
     if saved is None:
         saved = torch.empty(sb, dtype=torch.uint8, device=dev)
-    wb = int(L.lmhead_fwd_workspace_bytes(N, H, V))
-    if workspace is None:
-        workspace = torch.empty(max(wb, 1), dtype=torch.uint8, device=dev)
-    st = getattr(L, _entry)(_ptr(hidden), _ptr(weight), _ptr(targets), _ptr(keep_mask), N, H,
-                            V, int(bool(return_entropy)), int(bool(entropy_requires_grad)),
-                            _ptr(logp), _ptr(entropy), _ptr(saved), saved.numel(),
-                            _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    args = [_ptr(hidden), _ptr(weight), _ptr(targets), _ptr(keep_mask), N, H, V,
+            int(bool(return_entropy)), int(bool(entropy_requires_grad)), _ptr(logp),
+            _ptr(entropy), _ptr(saved), saved.numel()]
+    if _entry != "lmhead_fwd_noalloc":
+        wb = int(L.lmhead_fwd_workspace_bytes(N, H, V))
+        if workspace is None:
+            workspace = torch.empty(max(wb, 1), dtype=torch.uint8, device=dev)
+        args += [_ptr(workspace), workspace.numel()]
+    st = getattr(L, _entry)(*args, _stream(stream, dev))
     check(_entry, st)
     return logp, entropy, saved
 
@@ -141,6 +144,21 @@ def lmhead_fwd_blocksparse(hidden, weight, targets, keep_mask=None, return_entro
     return lmhead_fwd(hidden, weight, targets, keep_mask, return_entropy, entropy_requires_grad,
                       logp=logp, entropy=entropy, saved=saved, workspace=workspace,
                       stream=stream, _entry="lmhead_fwd_blocksparse")
+
+
+def lmhead_fwd_noalloc(hidden, weight, targets, keep_mask=None, return_entropy=False,
+                       entropy_requires_grad=False, *, logp=None, entropy=None, saved=None,
+                       stream=None):
+    """Allocation-free forward: as lmhead_fwd, with the workspace in the
+    library's built-in device array (LMHEAD_NOALLOC_SCRATCH_BYTES per GPU).
+    The C call allocates nothing; pass `logp`, `entropy` and `saved` to keep
+    this wrapper from allocating them with torch."""
+    return lmhead_fwd(hidden, weight, targets, keep_mask, return_entropy, entropy_requires_grad,
+                      logp=logp, entropy=entropy, saved=saved, stream=stream,
+                      _entry="lmhead_fwd_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # LMHEAD_NOALLOC_SCRATCH_BYTES in include/lmhead.h
 
 
 def lmhead_bwd(hidden, weight, targets, saved, grad_logp, grad_entropy=None,

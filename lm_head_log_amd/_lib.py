@@ -24,6 +24,8 @@ SIGNATURES = {
                            c_vp, c_vp, c_vp, c_size, c_vp, c_size, c_vp]),
     "lmhead_fwd_blocksparse": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int,
                                        c_int, c_vp, c_vp, c_vp, c_size, c_vp, c_size, c_vp]),
+    "lmhead_fwd_noalloc": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_int,
+                                   c_vp, c_vp, c_vp, c_size, c_vp]),
     "lmhead_bwd": (c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_size,
                            c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_size, c_vp]),
     "lmhead_fwd_partial": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,

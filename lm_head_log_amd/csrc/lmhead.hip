@@ -1278,6 +1278,9 @@ struct ProfRec {
 };
 static std::mutex g_prof_mu;
 static bool g_prof_on = false;
+// Set for the duration of an allocation-free call: its launches create no
+// timing events (event creation allocates).
+static thread_local bool t_no_events = false;
 static std::vector<ProfRec> g_prof_recs;
 static std::vector<hipEvent_t> g_prof_pool;
 
@@ -1301,7 +1304,7 @@ static int launch(int kind, void (*k)(KArgs...), dim3 grid, dim3 block, hipStrea
   hipEvent_t a = nullptr, b = nullptr;
   {
     std::lock_guard<std::mutex> g(g_prof_mu);
-    if (g_prof_on) {
+    if (g_prof_on && !t_no_events) {
       a = prof_event();
       b = prof_event();
     }
@@ -1477,6 +1480,55 @@ LMH_API int lmhead_fwd_blocksparse(const void* hidden, const void* weight,
   return fwd_entry(hidden, weight, targets, keep_mask, N, H, V, return_entropy,
                    entropy_requires_grad, logp, entropy, saved, saved_bytes, workspace,
                    workspace_bytes, stream, kBlockSparseRows);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: lmhead_fwd with its workspace in a file-scope
+// device array, for callers that cannot allocate. Host code never names the
+// array as an address (its host-side name is a stand-in); the device address
+// comes from hipGetSymbolAddress, once per device, with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = LMHEAD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on its first use).
+static int noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LMHEAD_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return LMHEAD_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LMHEAD_OK;
+}
+
+LMH_API int lmhead_fwd_noalloc(const void* hidden, const void* weight, const int32_t* targets,
+                               const uint8_t* keep_mask, int64_t N, int64_t H, int64_t V,
+                               int return_entropy, int entropy_requires_grad, float* logp,
+                               float* entropy, void* saved, size_t saved_bytes, void* stream) {
+  const int st = check_sizes(N, H, V);
+  if (st != LMHEAD_OK) return st;
+  if (fwd_ws(N, H, V).total > kNoAllocScratchBytes) return LMHEAD_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int sst = noalloc_scratch(&ws);
+  if (sst != LMHEAD_OK) return sst;
+  struct NoEvents {
+    NoEvents() { t_no_events = true; }
+    ~NoEvents() { t_no_events = false; }
+  } no_events;
+  // the tile-queue counters in the scratch are zeroed by a kernel each call;
+  // every other workspace entry the kernels read is written earlier in the call
+  return fwd_entry(hidden, weight, targets, keep_mask, N, H, V, return_entropy,
+                   entropy_requires_grad, logp, entropy, saved, saved_bytes, ws,
+                   kNoAllocScratchBytes, stream, 1);
 }
 
 LMH_API int lmhead_fwd_partial(const void* hidden, const void* weight_shard,
