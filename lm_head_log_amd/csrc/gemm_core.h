@@ -115,6 +115,18 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
+// A workgroup barrier that orders LDS accesses only. __syncthreads() also
+// fences global memory, so it waits for every vector-memory operation the
+// wave has in flight (epilogue stores, the tile-queue atomic). The tile
+// kernels pass data between waves through LDS alone, and direct-to-LDS
+// loads are waited for explicitly (vmcnt) before their slots are read or
+// reused.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // This thread's lane and wave, opaque to the optimiser. Per-tile setup derives
 // many per-lane values (load offsets, epilogue indices) that do not depend on
 // the tile; hoisted out of a persistent tile loop they stay live across the
@@ -378,9 +390,13 @@ struct TileQueue {
   // own XCD's queue, then the other queues when stealing) and broadcasts it
   // through the first word of `bcast`, the ring slot bcast_slot<SHIFT>()
   // names (no load writes it until every wave has read the index); contains
-  // a workgroup barrier.
+  // a workgroup barrier (LDS only: the atomics are thread 0's own).
   __device__ __forceinline__ int next(char* bcast) {
-    volatile int* slot = reinterpret_cast<volatile int*>(bcast);
+    // an LDS pointer, so the exchange is a ds_write / ds_read pair (through a
+    // generic pointer it is a flat access, which also waits for the stores
+    // of the epilogue before it)
+    volatile __attribute__((address_space(3))) int* slot =
+        (volatile __attribute__((address_space(3))) int*)bcast;
     if (threadIdx.x == 0) {
       const int x = xcd_id();
       int t = tile_at(x, ahead != kNone ? ahead : take(x));
@@ -391,7 +407,7 @@ struct TileQueue {
       }
       *slot = t;
     }
-    __syncthreads();
+    lds_barrier();
     return *slot;
   }
 };

@@ -542,7 +542,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     const int vbase = tm * kBM + wm * 128;
     const bool full = vbase + 128 <= P.V;
     const int vlim = P.V - vbase - acc_row_lane(lane);  // rows acc_row_fixed < vlim are valid
-    __syncthreads();  // every wave is done reading the ring
+    lds_barrier();  // every wave is done reading the ring
     const int fence = acc_read_fence();
     // Per token (column 16 j + lane % 16 of the wave): m = max y,
     // s = sum 2^(y - m) and b = sum 2^(y - m) (y - m) over this lane's 32
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
       columns(std::false_type{});
     else
       columns(std::true_type{});
-    __syncthreads();
+    lds_barrier();  // both wave rows have staged their partials
     {
       const int cl = tid;  // one token per thread
       const int c = tn * kBN + cl;
@@ -913,7 +913,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     // the row-order reads are free of bank conflicts. A wave's LDS accesses
     // are performed in order, so the region is reused for every pair of
     // column blocks without a barrier.
-    __syncthreads();  // every wave is done reading the ring
+    lds_barrier();  // every wave is done reading the ring
     char* stage = ring.a[0] + wave * 8192;
     const int g = lane >> 4;
 #pragma unroll
@@ -1040,6 +1040,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     A.init(P.dZ + (int64_t)tm * kBM * P.ldz + k0, P.ldz, rows - tm * kBM);
     B.init(P.W + (int64_t)k0 * P.H + (int64_t)tn * kBN, P.H,
            P.pieces ? min(P.kp, P.V - k0) : P.V, P.H - tn * kBN);
+    // original positions of the wave's 128 rows (m0 + lane and m0 + 64 +
+    // lane), loaded before the main loop: the epilogue takes each row's from
+    // these by lane index instead of waiting on a load per stored row
+    int krow[2];
+    {
+      const int m = tm * kBM + (wave_fresh() >> 1) * 128 + lane_fresh();
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        krow[h] = (!P.pieces && m + 64 * h < rows) ? kidx[m + 64 * h] : 0;
+    }
     Acc acc;
     mainloop<SHIFT>(A, B, nk, ring, acc);
     q.claim_ahead();
@@ -1057,7 +1067,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     // position once. The writes (4 rows x 16 columns per instruction) and the
     // row reads are free of bank conflicts.
     const int fence = acc_read_fence();
-    __syncthreads();  // every wave is done reading the ring
+    lds_barrier();  // every wave is done reading the ring
     float* stage = reinterpret_cast<float*>(ra0 + wave * 8192);
     const int m0 = tm * kBM + wm * 128;  // first chunk row of the wave's block
     const int n0 = tn * kBN + wn * 128;  // first h of the wave's block
@@ -1081,11 +1091,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
         const int m = m0 + i * 16 + t;
         const int h = n0 + q * 4;
         const float4 x = *reinterpret_cast<const float4*>(stage + t * 128 + ((q ^ t) << 2));
+        // the row's position: wave row i * 16 + 2 uu for lanes 0..31, the
+        // next one for lanes 32..63 (compile-time lanes of krow)
+        const int rr = i * 16 + 2 * uu;
+        const int plo = __builtin_amdgcn_readlane(krow[i >> 2], rr & 63);
+        const int phi = __builtin_amdgcn_readlane(krow[i >> 2], (rr + 1) & 63);
+        const int pos = (lane >> 5) ? phi : plo;
         if (P.pieces)  // the whole partial tile, row-major
           *reinterpret_cast<float4*>(P.part + (int64_t)u * (kBM * kBN) +
                                      (m - tm * kBM) * kBN + (h - tn * kBN)) = x;
         else if (m < rows && h < P.H)  // H is a multiple of 4: a chunk is whole
-          *reinterpret_cast<float4*>(P.dX + (int64_t)kidx[m] * P.H + h) = x;
+          *reinterpret_cast<float4*>(P.dX + (int64_t)pos * P.H + h) = x;
       }
     }
   }
@@ -1179,12 +1195,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     // quarter of ring slot 0; row t at t * 512 bytes, chunk q at chunk q ^ t)
     // and stores two 512-byte row segments per instruction.
     const int fence = acc_read_fence();
-    __syncthreads();  // every wave is done reading the ring
+    lds_barrier();  // every wave is done reading the ring
     char* stage = ra0 + wave * 8192;
     const int h0 = tm * kBM + wm * 128;  // first h of the wave's rows
     const int g = lane >> 4;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      // rows 2 u, 2 u + 1 of the block per store instruction, 32 lanes a row
+      const int q = lane & 31;
+      const int h = h0 + q * 4;
+      // accumulating: the block's previous values, all eight loads issued
+      // before the staging so that one wait covers them
+      float4 old[8];
+      if (P.accumulate) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int v = tn * kBN + wn * 128 + j * 16 + 2 * u + (lane >> 5);
+          old[u] = (v < P.V && h < P.H)
+                       ? *reinterpret_cast<const float4*>(P.dW + (int64_t)v * P.H + h)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
       const int t = lane & 15;  // this lane's vocabulary row in the wave's block
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -1195,22 +1226,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
         *reinterpret_cast<float4*>(stage + t * 512 + ((q ^ t) << 4)) = x;
       }
       __builtin_amdgcn_sched_barrier(0);
-      // rows 2 u, 2 u + 1 of the block per instruction, 32 lanes a row
-      const int q = lane & 31;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int tr = 2 * u + (lane >> 5);
         const int v = tn * kBN + wn * 128 + j * 16 + tr;
-        const int h = h0 + q * 4;
         if (v < P.V && h < P.H) {  // H is a multiple of 4: a chunk is whole
           float4 x = *reinterpret_cast<const float4*>(stage + tr * 512 + ((q ^ tr) << 4));
           float* dst = P.dW + (int64_t)v * P.H + h;
           if (P.accumulate) {
-            const float4 o = *reinterpret_cast<const float4*>(dst);
-            x.x += o.x;
-            x.y += o.y;
-            x.z += o.z;
-            x.w += o.w;
+            x.x += old[u].x;
+            x.y += old[u].y;
+            x.z += old[u].z;
+            x.w += old[u].w;
           }
           const f32x4_t v = {x.x, x.y, x.z, x.w};
           __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(dst));
