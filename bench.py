@@ -77,12 +77,17 @@ def cpu_baseline(w, rows_n: int):
     batch (forward + backward including those rows' dW)."""
     import oracle
     import workloads as wl
+    host_cpus = os.cpu_count() or 1
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [os.cpu_count() or 1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in pools] or [host_cpus])
+        if pools:
+            blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version') or ''}".strip()
+                                     for i in pools}))
     except Exception:
-        threads = os.cpu_count() or 1
+        threads = host_cpus
     rows = wl.sample_rows(w.kept_rows(), rows_n, 99)
     t0 = time.perf_counter()
     oracle.rows_fwd_bwd(w.hidden, w.weight, w.targets, rows, w.g_logp, w.g_entropy,
@@ -92,6 +97,8 @@ def cpu_baseline(w, rows_n: int):
         "value": round(len(rows) / dt, 3),
         "unit": "tokens/s",
         "cores": int(threads),
+        "host_cpus": int(host_cpus),
+        "blas": blas,
         "kind": "oracle",
         "sample": (f"{len(rows)} kept rows of the same batch, float64 numpy, "
                    f"forward{' + backward incl. dW' if w.backward else ''}, "
@@ -297,7 +304,7 @@ def probe_leg(lmh, W, X, stream, step_tflops, kernel_tflops, iters=200000):
                 "ms": round(r["ms"], 3), "frac_of_bf16_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4)}
 
     return {
-        "what": "v_mfma_f32_32x32x16_bf16, 4x4 blocks per wave, 4 waves per CU, one workgroup "
+        "what": "v_mfma_f32_16x16x32_bf16, 8x8 blocks per wave, 4 waves per CU, one workgroup "
                 "per CU, operands in registers (no loads, LDS, barriers or epilogue)",
         "operands_from_batch": rec(data),
         "zero_operands": rec(zero),

@@ -590,7 +590,7 @@ __device__ __forceinline__ void k_stage(const ASrc& A, const BSrc& B, int t, int
 // padding stage. Any other count runs up to 11 stages past nk, which read
 // zeros and add nothing (an early exit instead would be a branch out of the
 // unrolled body, and any such branch makes the register allocator spill
-// fragments inside the loop).
+// fragments inside the loop). nk <= 0 is allowed and yields zeros.
 template <int SHIFT = 0>
 __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, const Ring& R,
                                          Acc& acc) {
@@ -603,15 +603,7 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
-  acc_pin(acc);
-  if (nk <= 0) return;
-  const int np = (nk + 1) / 2;
+  const int np = (nk + 1) / 2;  // nk <= 0: the prologue's loads read zeros
 
   // Prologue: pairs 0 and 1, stages 0..3. Stage 3 goes into the B slot that
   // carries the tile index (bcast_slot) and so only after the first barrier.
@@ -623,6 +615,17 @@ __device__ __forceinline__ void mainloop(const ASrc& A, const BSrc& B, int nk, c
   B.issue(1, R.b[b1]);
   A.issue_pair(1, np, R.a[a1]);
   B.issue(2, R.b[b2]);
+  // the accumulators are zeroed while those loads are in flight (256 VALU
+  // writes, hidden under their latency)
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+  acc_pin(acc);
+  // (nk <= 0 takes no early exit: a branch here makes the register allocator
+  // spill; the peel stages below then run over zero-filled loads)
   // pair 0 and stage 0 landed: only stage 1, pair 1 and stage 2 may remain
   wait_vmcnt<2 * kBLoadsPerWaveStage + kALoadsPerWavePair>();
   __builtin_amdgcn_s_barrier();

@@ -500,8 +500,12 @@ struct FwdParams {
 template <int SHIFT>
 __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
   LMH_DECLARE_RING;
-  // per-token partials of the two wave rows; reuses ring slot 0 after the main loop
-  float (*red)[3][kBN] = reinterpret_cast<float (*)[3][kBN]>(ra0);
+  // per-token partials of the two wave rows x four lane groups; reuses ring
+  // slot 0 after the main loop (rows padded to 272 floats: the four lane
+  // groups of a write then fall in different banks)
+  constexpr int kRedPitch = kBN + 16;
+  static_assert(8 * 3 * kRedPitch * 4 <= kASlotBytes, "the partials fit one A slot");
+  float (*red)[3][kRedPitch] = reinterpret_cast<float (*)[3][kRedPitch]>(ra0);
 
   const int rows = P.hdr->n_kept;
   const int mt = P.n_vt;
@@ -546,11 +550,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     const int fence = acc_read_fence();
     // Per token (column 16 j + lane % 16 of the wave): m = max y,
     // s = sum 2^(y - m) and b = sum 2^(y - m) (y - m) over this lane's 32
-    // vocabulary rows (16 i + 4 (lane / 16) + r), merged with the three other
-    // lanes that hold the token's other rows of the wave's 128 and staged in
-    // LDS for the merge of the two wave rows; then the target pick. The masked
-    // form leaves out rows at or past V, which only the last vocabulary tile
-    // has; a lane with no valid row gives the empty partial (-inf, 0, 0).
+    // vocabulary rows (16 i + 4 (lane / 16) + r), staged in LDS with the
+    // token's seven other partials (the three other lanes of the wave that
+    // hold its rows, and the other wave row) for one merge per token; then
+    // the target pick. The masked form leaves out rows at or past V, which
+    // only the last vocabulary tile has; a lane with no valid row gives the
+    // empty partial (-inf, 0, 0).
     auto columns = [&](auto masked_t) {
       constexpr bool kMasked = decltype(masked_t)::value;
 #pragma unroll
@@ -588,17 +593,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
             b = fmaf(e, y, b);
           }
         }
-#pragma unroll
-        for (int x = 16; x <= 32; x <<= 1) {
-          const float mo = __shfl_xor(m, x);
-          const float so = __shfl_xor(s, x);
-          const float bo = __shfl_xor(b, x);
-          stat_merge(m, s, b, mo, so, bo);
-        }
-        if (lane < 16) {
-          red[wm][0][cl] = m;
-          red[wm][1][cl] = s;
-          red[wm][2][cl] = b;
+        {
+          const int pset = wm * 4 + (lane >> 4);  // wave row, lane group
+          red[pset][0][cl] = m;
+          red[pset][1][cl] = s;
+          red[pset][2][cl] = b;
         }
         // exactly one lane in the grid holds z[t] for a kept token (the
         // target of a token past the kept rows is -1 and never hits): row
@@ -621,12 +620,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
       columns(std::false_type{});
     else
       columns(std::true_type{});
-    lds_barrier();  // both wave rows have staged their partials
+    lds_barrier();  // every lane has staged its partials
     {
       const int cl = tid;  // one token per thread
       const int c = tn * kBN + cl;
-      float m = red[0][0][cl], s = red[0][1][cl], b = red[0][2][cl];
-      stat_merge(m, s, b, red[1][0][cl], red[1][1][cl], red[1][2][cl]);
+      // the token's eight partials in a fixed order: their maximum first,
+      // then the sums rescaled to it; an empty partial adds nothing
+      float pm8[8], ps8[8], pb8[8];
+      float m = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pm8[k] = red[k][0][cl];
+        ps8[k] = red[k][1][cl];
+        pb8[k] = red[k][2][cl];
+        m = fmaxf(m, pm8[k]);
+      }
+      float s = 0.f, b = 0.f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (pm8[k] != -INFINITY) {
+            const float d = pm8[k] - m;
+            const float a = __builtin_amdgcn_exp2f(d);
+            s = fmaf(a, ps8[k], s);
+            b = fmaf(a, fmaf(d, ps8[k], pb8[k]), b);
+          }
+        }
+      }
       if (c < rows) {
         const int64_t o = (int64_t)tm * P.ldp + c;
         P.pm[o] = m;
@@ -926,7 +946,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
         const bool hit = local >= 0 && local < 128 && ((local >> 2) & 3) == g;
         const int want = (local >> 4) * 4 + (local & 3);  // i * 4 + r of the target
         const int t = 16 * jh + (lane & 15);  // this lane's token in the staged 32
-        char* trow = stage + t * 256 + (g & 1) * 8;
+        // byte offset of the lane's 8 bytes for row block i: half (g & 1) of
+        // chunk q = 2 i + g / 2 at chunk q ^ (t & 15) of row t. Bits 5..7 hold
+        // (q >> 1) ^ ((lane >> 1) & 7) and nothing else does, so block i is
+        // block 0's offset XOR (i << 5)
+        const int off0 = t * 256 + (g & 1) * 8 + ((((g >> 1) ^ lane) & 1) << 4) + ((lane & 14) << 4);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           float d[4];
@@ -942,11 +966,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
             for (int r = 0; r < 4; ++r)
               if ((want & 3) == r) d[r] += k.w;
           }
-          // entries 16 i + 4 g + 0..3: half (g & 1) of chunk 2 i + g / 2
-          const int q = 2 * i + (g >> 1);
+          // entries 16 i + 4 g + 0..3
           const bf16x2_t lo = {(__bf16)d[0], (__bf16)d[1]};
           const bf16x2_t hi = {(__bf16)d[2], (__bf16)d[3]};
-          *reinterpret_cast<uint2*>(trow + ((q ^ (t & 15)) << 4)) =
+          *reinterpret_cast<uint2*>(stage + (off0 ^ (i << 5))) =
               make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
         }
         // one column block at a time (bounds the live copies)
