@@ -33,9 +33,11 @@ def hipcc() -> str:
     return p
 
 
-def build(verbose: bool = False, asm: bool = False) -> str:
-    """Compile liblmhead.so next to this file and return its path."""
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", LIB + ".tmp", *SRCS]
+def build(verbose: bool = False, asm: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile liblmhead.so next to this file (or to `out`, with the extra
+    preprocessor `defines`, e.g. an instrumented build) and return its path."""
+    cmd = [hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
+           "-o", out + ".tmp", *SRCS]
     if asm:
         cmd.insert(1, "-save-temps=obj")
     if verbose:
@@ -48,8 +50,8 @@ def build(verbose: bool = False, asm: bool = False) -> str:
             if "packed-fp32-ops" not in l and l.strip()]
     if verbose and errs:
         sys.stderr.write("\n".join(errs) + "\n")
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

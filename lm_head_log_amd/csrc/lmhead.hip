@@ -421,6 +421,55 @@ __device__ __forceinline__ void stat_merge(float& m, float& s, float& b, float m
 }
 
 // ---------------------------------------------------------------------------
+// Per-tile phase clocks of the four tile kernels, compiled in only with
+// LMHEAD_TILE_CLOCKS (an instrumented build for measurement; the default
+// build contains none of it). Each workgroup reads the shader clock
+// (s_memtime) and the constant 100 MHz clock (s_memrealtime) when it has
+// taken a tile, after the tile's main loop and after its epilogue, and
+// thread 0 adds the totals into per-kernel device counters when the
+// workgroup exits: main-loop and epilogue time and cycles, time spent taking
+// tiles, and the tile count. lmhead_tile_clocks (same build only) reads them.
+// ---------------------------------------------------------------------------
+enum { kClkFwd = 0, kClkDz = 1, kClkDx = 2, kClkDw = 3 };
+#ifdef LMHEAD_TILE_CLOCKS
+__device__ unsigned long long g_tile_clock[4][8];
+struct TileClock {
+  uint64_t r_end, r_a = 0, r_b = 0, c_a = 0, c_b = 0;
+  uint64_t main = 0, epi = 0, next = 0, n = 0, cmain = 0, cepi = 0;
+  __device__ TileClock() : r_end(__builtin_amdgcn_s_memrealtime()) {}
+  __device__ void tile_start() {
+    r_a = __builtin_amdgcn_s_memrealtime();
+    c_a = __builtin_amdgcn_s_memtime();
+    next += r_a - r_end;
+  }
+  __device__ void main_done() {
+    r_b = __builtin_amdgcn_s_memrealtime();
+    c_b = __builtin_amdgcn_s_memtime();
+    main += r_b - r_a;
+    cmain += c_b - c_a;
+  }
+  __device__ void tile_done() {
+    r_end = __builtin_amdgcn_s_memrealtime();
+    epi += r_end - r_b;
+    cepi += __builtin_amdgcn_s_memtime() - c_b;
+    ++n;
+  }
+  __device__ void flush(int k) {
+    if (threadIdx.x != 0) return;
+    const unsigned long long v[7] = {main, epi, next, n, cmain, cepi, 1};
+    for (int i = 0; i < 7; ++i) atomicAdd(&g_tile_clock[k][i], v[i]);
+  }
+};
+#else
+struct TileClock {
+  __device__ void tile_start() {}
+  __device__ void main_done() {}
+  __device__ void tile_done() {}
+  __device__ void flush(int) {}
+};
+#endif
+
+// ---------------------------------------------------------------------------
 // Gathered transpose of the kept rows through LDS in 64 x 64 tiles (bf16),
 // zero-filled past the kept rows so that every tile reads finite values:
 //   k_gather_cols : XcT[h][c] = X[kept_idx[c0 + c]][h] for c < ld (zero where
@@ -515,9 +564,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
   const int nk = P.H / kBK;
 
   TileQueue q(P.queue, ntiles, P.steal);
+  TileClock clk;
   for (;;) {
     const int t = q.next(ring.b[bcast_slot<SHIFT>()]);
     if (t < 0) break;
+    clk.tile_start();
     int tm, tn;
     tile_coords<LMH_GM_FWD>(t, mt, nt, tm, tn);
 
@@ -537,6 +588,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
     B.init(P.XcT + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     Acc acc;
     mainloop<SHIFT>(A, B, nk, ring, acc);
+    clk.main_done();
     q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
@@ -654,7 +706,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd_tiles(FwdParams P) {
         P.pb[o] = b;
       }
     }
+    clk.tile_done();
   }
+  clk.flush(kClkFwd);
 }
 
 // ---------------------------------------------------------------------------
@@ -883,9 +937,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
   const int nk = P.H / kBK;
 
   TileQueue q(P.queue, ntiles, P.steal);
+  TileClock clk;
   for (;;) {
     const int t = q.next(ring.b[bcast_slot<SHIFT>()]);
     if (t < 0) break;
+    clk.tile_start();
     int tm, tn;
     tile_coords<LMH_GM_DZ>(t, mt, nt, tm, tn);
 
@@ -909,6 +965,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
     B.init(P.XcT + (int64_t)tn * kBN, P.ldc, P.H, rows - tn * kBN);
     Acc acc;
     mainloop<SHIFT>(A, B, nk, ring, acc);
+    clk.main_done();
     q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
@@ -987,7 +1044,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(P.dZ + (int64_t)c * P.ldz + vbase + q * 8));
       }
     }
+    clk.tile_done();
   }
+  clk.flush(kClkDz);
 }
 
 // dX[kept rows] = dZ W: M = chunk rows (A = dZ rows), N = H (B = W: k = v
@@ -1045,9 +1104,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   const int32_t* kidx = P.sv.kept_idx + P.c0;
 
   TileQueue q(P.queue, nunits, P.steal);
+  TileClock clk;
   for (;;) {
     const int u = q.next(ring.b[bcast_slot<SHIFT>()]);
     if (u < 0) break;
+    clk.tile_start();
     int t = u, k0 = 0;
     if (P.pieces) {
       t = tail.full + u % tail.R;
@@ -1075,6 +1136,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     }
     Acc acc;
     mainloop<SHIFT>(A, B, nk, ring, acc);
+    clk.main_done();
     q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
@@ -1127,7 +1189,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
           *reinterpret_cast<float4*>(P.dX + (int64_t)pos * P.H + h) = x;
       }
     }
+    clk.tile_done();
   }
+  clk.flush(kClkDx);
 }
 
 // The split tail's dX tiles: the S partial tiles of each are summed in piece
@@ -1193,9 +1257,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
   const int nk = (rows + kBK - 1) / kBK;  // dZ rows past `rows` read as zero
 
   TileQueue q(P.queue, ntiles, P.steal);
+  TileClock clk;
   for (;;) {
     const int t = q.next(ring.b[bcast_slot<SHIFT>()]);
     if (t < 0) break;
+    clk.tile_start();
     int tm, tn;
     tile_coords<LMH_GM_DW>(t, mt, nt, tm, tn);
 
@@ -1205,6 +1271,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     B.init(P.dZ + (int64_t)tn * kBN, P.ldz, rows, kBN);  // ldz covers every v of the tile
     Acc acc;
     mainloop<SHIFT>(A, B, nk, ring, acc);
+    clk.main_done();
     q.claim_ahead();
     // per-tile lane values (see lane_fresh): nothing lane-derived is hoisted
     // out of the tile loop to be spilled across the main loop
@@ -1267,7 +1334,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
         }
       }
     }
+    clk.tile_done();
   }
+  clk.flush(kClkDw);
 }
 
 // ---------------------------------------------------------------------------
@@ -1845,6 +1914,24 @@ LMH_API const char* lmhead_status_string(int status) {
 }
 
 LMH_API int lmhead_version(void) { return kVersion; }
+
+#ifdef LMHEAD_TILE_CLOCKS
+// Instrumented builds only (not declared in the public header): copies the
+// per-kernel tile clocks (4 kernels x 8 counters, in the order TileClock
+// adds them; counter 6 counts workgroups) to host memory after a device
+// synchronisation; reset != 0 then zeroes them. Returns 0 or 1 on a HIP error.
+LMH_API int lmhead_tile_clocks(unsigned long long* out, int reset) {
+  if (!out || hipDeviceSynchronize() != hipSuccess) return 1;
+  if (hipMemcpyFromSymbol(out, HIP_SYMBOL(g_tile_clock), sizeof(g_tile_clock)) != hipSuccess)
+    return 1;
+  if (reset) {
+    static const unsigned long long z[4 * 8] = {};
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_tile_clock), z, sizeof(z)) != hipSuccess) return 1;
+    if (hipDeviceSynchronize() != hipSuccess) return 1;
+  }
+  return 0;
+}
+#endif
 
 LMH_API const char* lmhead_kernel_name(int kind) {
   return (kind >= 0 && kind < KK_COUNT) ? kKernelNames[kind] : nullptr;
