@@ -477,7 +477,15 @@ struct TileClock {
 //                   (c0 = 0), the backward one chunk of them at a time
 // ---------------------------------------------------------------------------
 constexpr int kTp = 64;
-constexpr int kTpPitch = kTp + 8;  // 144-byte rows: column reads hit distinct banks
+constexpr int kTpPitch = kTp + 8;  // 144-byte rows
+
+// LDS layout of the tile: element (r, c) sits in 8-element chunk
+// (c / 8) ^ (r / 8) of row r. A thread of the transposed read below takes
+// one column c at 8 rows r spaced 1 apart within one 8-row group g = r / 8,
+// and the 8 lanes that share c read the groups g = 0..7; unswizzled, those
+// groups lie 8 rows = 288 dwords apart, the same bank for every group, while
+// the swizzle moves group g to chunk (c / 8) ^ g, 4 banks further per group.
+__device__ __forceinline__ int tile_col(int r, int c) { return (((c >> 3) ^ (r >> 3)) << 3) | (c & 7); }
 
 // Loads rows r (< 64) of the tile as 8-element chunks: src(r) is the row's
 // first element, or null for a zero row.
@@ -490,7 +498,7 @@ __device__ __forceinline__ void tile_load(uint16_t (*t)[kTpPitch], RowPtr src) {
     const int ch = tid % 8;
     const uint16_t* p = src(r);
     const uint4 x = p ? *reinterpret_cast<const uint4*>(p + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(&t[r][ch * 8]) = x;
+    *reinterpret_cast<uint4*>(&t[r][tile_col(r, ch * 8)]) = x;
   }
 }
 
@@ -502,10 +510,11 @@ __device__ __forceinline__ void tile_store_t(uint16_t (*t)[kTpPitch], uint16_t* 
   for (int it = 0; it < 2; ++it) {
     const int h = tid / 8 + 32 * it;
     const int ch = tid % 8;
+    const int col = tile_col(ch * 8, h);  // rows ch * 8 .. ch * 8 + 7 share it
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)t[ch * 8 + 2 * e][h] | ((uint32_t)t[ch * 8 + 2 * e + 1][h] << 16);
+      w[e] = (uint32_t)t[ch * 8 + 2 * e][col] | ((uint32_t)t[ch * 8 + 2 * e + 1][col] << 16);
     *reinterpret_cast<uint4*>(out + (int64_t)h * ld_out + ch * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
