@@ -1017,24 +1017,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz_tiles(DzParams P) {
         // (q >> 1) ^ ((lane >> 1) & 7) and nothing else does, so block i is
         // block 0's offset XOR (i << 5)
         const int off0 = t * 256 + (g & 1) * 8 + ((((g >> 1) ^ lane) & 1) << 4) + ((lane & 14) << 4);
+        // the column's 32 entries first, as one straight run (no branch
+        // between row blocks, so their chains interleave)
+        float d[32];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float d[4];
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float z = acc_read(acc[i][j][r], fence);
             const float p = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -k.x));
-            d[r] = kEntGrad ? p * fmaf(k.z, z, k.y) : p * k.y;
+            d[i * 4 + r] = kEntGrad ? p * fmaf(k.z, z, k.y) : p * k.y;
           }
-          // the one-hot term of the target, in the one lane that holds it
-          if (hit && (want >> 2) == i) {
+        // the one-hot term of the target, in the one lane that holds it
+        // (added before the rounding to bf16, as for every other term)
+        if (hit) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if ((want & 3) == r) d[r] += k.w;
-          }
+          for (int e = 0; e < 32; ++e)
+            if (want == e) d[e] += k.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
           // entries 16 i + 4 g + 0..3
-          const bf16x2_t lo = {(__bf16)d[0], (__bf16)d[1]};
-          const bf16x2_t hi = {(__bf16)d[2], (__bf16)d[3]};
+          const bf16x2_t lo = {(__bf16)d[i * 4 + 0], (__bf16)d[i * 4 + 1]};
+          const bf16x2_t hi = {(__bf16)d[i * 4 + 2], (__bf16)d[i * 4 + 3]};
           *reinterpret_cast<uint2*>(stage + (off0 ^ (i << 5))) =
               make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
         }
