@@ -1330,21 +1330,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
         *reinterpret_cast<float4*>(stage + t * 512 + ((q ^ t) << 4)) = x;
       }
       __builtin_amdgcn_sched_barrier(0);
+      // the block's eight row pieces read back together (the reads stay in
+      // the wave's region whatever the bounds, so one wait covers them), then
+      // stored where the row and h exist
+      float4 x[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int tr = 2 * u + (lane >> 5);
-        const int v = tn * kBN + wn * 128 + j * 16 + tr;
+        x[u] = *reinterpret_cast<const float4*>(stage + tr * 512 + ((q ^ tr) << 4));
+      }
+      if (P.accumulate) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          x[u].x += old[u].x;
+          x[u].y += old[u].y;
+          x[u].z += old[u].z;
+          x[u].w += old[u].w;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = tn * kBN + wn * 128 + j * 16 + 2 * u + (lane >> 5);
         if (v < P.V && h < P.H) {  // H is a multiple of 4: a chunk is whole
-          float4 x = *reinterpret_cast<const float4*>(stage + tr * 512 + ((q ^ tr) << 4));
-          float* dst = P.dW + (int64_t)v * P.H + h;
-          if (P.accumulate) {
-            x.x += old[u].x;
-            x.y += old[u].y;
-            x.z += old[u].z;
-            x.w += old[u].w;
-          }
-          const f32x4_t v = {x.x, x.y, x.z, x.w};
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(dst));
+          const f32x4_t o = {x[u].x, x[u].y, x[u].z, x[u].w};
+          __builtin_nontemporal_store(o, reinterpret_cast<f32x4_t*>(P.dW + (int64_t)v * P.H + h));
         }
       }
     }
