@@ -195,7 +195,7 @@ int lmhead_fwd_noalloc(const void* hidden, const void* weight, const int32_t* ta
  *             the saved state: grad_hidden and grad_weight are written with
  *             +0.0 everywhere, and lmhead_check_status(saved) then returns
  *             LMHEAD_ERR_INVALID_ARG. The backward writes one word of `saved`,
- *             that verdict (LMHEAD_OK for a consistent call), and nothing else.
+ *             the check's result (LMHEAD_OK for a consistent call), and nothing else.
  *  grad_logp  fp32 [N]; skipped rows are not read
  *  grad_entropy fp32 [N]; must be NULL iff !entropy_requires_grad (N > 0)
  *  grad_hidden fp32 [N, H] out, fully overwritten (+0.0 rows where skipped)
