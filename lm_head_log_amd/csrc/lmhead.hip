@@ -105,6 +105,10 @@ static inline SavedView saved_view(void* base, int64_t N) {
 }
 
 static inline int n_vtiles(int64_t V) { return (int)((V + kBM - 1) / kBM); }
+
+// The stage shift for nk stages: the rotation runs pairs of stages, so an
+// odd count gets one padding stage.
+__host__ __device__ constexpr int shift_for(int nk) { return stage_shift(nk + (nk & 1)); }
 static __host__ __device__ constexpr int64_t round_up(int64_t x, int64_t m) {
   return (x + m - 1) / m * m;
 }
@@ -1255,20 +1259,11 @@ struct DwParams {
 };
 
 template <int SHIFT>
-__global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
-  LMH_DECLARE_RING;
-
-  const int n_kept = P.hdr->n_kept;
-  int rows = min(P.C, n_kept - P.c0);
-  if (rows <= 0) {
-    if (P.accumulate) return;  // nothing to add
-    rows = 0;                  // first chunk with no kept rows: write zeros
-  }
+__device__ __forceinline__ void dw_tile_loop(const DwParams& P, const Ring& ring, int rows, int nk) {
   const int mt = (P.H + kBM - 1) / kBM;
   const int nt = (P.V + kBN - 1) / kBN;
   const int ntiles = mt * nt;
   const int tid = threadIdx.x;
-  const int nk = (rows + kBK - 1) / kBK;  // dZ rows past `rows` read as zero
 
   TileQueue q(P.queue, ntiles, P.steal);
   TileClock clk;
@@ -1300,7 +1295,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     // and stores two 512-byte row segments per instruction.
     const int fence = acc_read_fence();
     lds_barrier();  // every wave is done reading the ring
-    char* stage = ra0 + wave * 8192;
+    char* stage = ring.a[0] + wave * 8192;
     const int h0 = tm * kBM + wm * 128;  // first h of the wave's rows
     const int g = lane >> 4;
 #pragma unroll
@@ -1360,6 +1355,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     clk.tile_done();
   }
   clk.flush(kClkDw);
+}
+
+// K of dW is the chunk's kept rows, a count only the device has (the saved
+// header): the kernel takes the instance whose stage shift runs exactly that
+// many stages, where a shift chosen on the host from the chunk capacity ran
+// up to 11 padding stages per tile (at 23 % kept rows, 11 of 128).
+__global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
+  LMH_DECLARE_RING;
+
+  const int n_kept = P.hdr->n_kept;
+  int rows = min(P.C, n_kept - P.c0);
+  if (rows <= 0) {
+    if (P.accumulate) return;  // nothing to add
+    rows = 0;                  // first chunk with no kept rows: write zeros
+  }
+  const int nk = (rows + kBK - 1) / kBK;  // dZ rows past `rows` read as zero
+  switch (shift_for(nk)) {
+    case 0: dw_tile_loop<0>(P, ring, rows, nk); break;
+    case 2: dw_tile_loop<2>(P, ring, rows, nk); break;
+    case 4: dw_tile_loop<4>(P, ring, rows, nk); break;
+    case 6: dw_tile_loop<6>(P, ring, rows, nk); break;
+    case 8: dw_tile_loop<8>(P, ring, rows, nk); break;
+    default: dw_tile_loop<10>(P, ring, rows, nk); break;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1471,9 +1490,6 @@ static int launch_shifted(int kind, int shift, dim3 grid, hipStream_t s, const P
   return launch(kind, table[shift / 2], grid, dim3(kThreads), s, p);
 }
 
-// The stage shift for nk stages: the rotation runs pairs of stages, so an
-// odd count gets one padding stage.
-static int shift_for(int nk) { return stage_shift(nk + (nk & 1)); }
 
 
 #define LMH_TRY(expr)                  \
@@ -1845,11 +1861,7 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
     const int dw_grid = persistent_grid(dw_tiles);
     Wp.queue = queues + (ch * kBwdQueueSets + 3) * kQueueInts;
     Wp.steal = steal_for(dw_tiles, dw_grid);
-    // the shift of a full chunk; a shorter last chunk runs a few padding
-    // stages, which read zeros
-    LMH_TRY(launch_shifted(KK_DW, shift_for((int)(G.C / kBK)), dim3(dw_grid), s, Wp,
-                           k_dw_tiles<0>, k_dw_tiles<2>, k_dw_tiles<4>, k_dw_tiles<6>,
-                           k_dw_tiles<8>, k_dw_tiles<10>));
+    LMH_TRY(launch(KK_DW, k_dw_tiles, dim3(dw_grid), dim3(kThreads), s, Wp));
   }
   return LMHEAD_OK;
 }
