@@ -122,6 +122,23 @@ def test_token_chunk_invariance():
         assert rel_fro(g["dW"], base["dW"]) <= 1e-3, chunk
 
 
+# dW's K is a chunk's kept-row count, which only the device has; its kernel
+# enters the stage-shift instance for that count. Kept-row counts whose stage
+# counts (rows / 32 rounded up: 2, 4, 6, 7, 8, 10, 12, 12, 14) reach every
+# shift, odd counts included, and a two-chunk backward (256 + 161 rows).
+@pytest.mark.parametrize("rows,chunk", [(33, 0), (97, 0), (161, 0), (200, 0), (225, 0),
+                                        (289, 0), (353, 0), (383, 0), (417, 0), (417, 256)])
+def test_dw_every_stage_shift(rows, chunk):
+    N, H, V = rows + 45, 128, 600
+    say(f"case: dW stage shift, {rows} kept rows of N{N} H{H} V{V}, chunk {chunk}")
+    w = wl.small(N, H, V, seed=90 + rows, keep_fraction=1.0)
+    keep = np.zeros(N, np.uint8)
+    keep[np.random.default_rng(rows).choice(N, rows, replace=False)] = 1
+    g = run(w, keep=keep, token_chunk=chunk)
+    assert g["n_kept"] == rows
+    check_against_oracle(w, g, keep=keep, what=f"{rows} kept rows, chunk {chunk}")
+
+
 def test_metric_only_entropy_is_bitwise_the_differentiable_one():
     say("case: metric-only vs differentiable entropy")
     w = wl.small(700, 128, 5000, seed=41)
