@@ -847,7 +847,7 @@ __global__ void k_zero_ints(int* __restrict__ p, int n) {
 // `chk` receives a copy of the header whose n_kept every backward kernel
 // reads: the saved count when the state belongs to this call, else 0, so a
 // mismatched call computes nothing from the saved state, and k_zero_rows
-// then clears every dX row (status != OK). The verdict also goes to the
+// then clears every dX row (status != OK). The outcome is also written to the
 // saved header's bwd_status, which lmhead_check_status reports. The state
 // belongs to the call when N and H match, the vocabulary matches (the whole
 // vocabulary, or for a vocabulary shard a range inside the forward's
