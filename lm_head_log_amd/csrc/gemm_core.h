@@ -510,6 +510,16 @@ __device__ __forceinline__ void acc_fence(Acc& c) {
 }
 
 constexpr int kMfmaPerStage = 64;
+// The stage's MFMAs run A block by A block (row i of the wave's 8 x 8
+// blocks), the B blocks of odd rows in reverse, so that consecutive MFMAs
+// change one operand only (the row's last B block starts the next row). The
+// chip's clock under MFMA load falls with the operand bits that switch from
+// one MFMA to the next: with the bench batch's operands in registers this
+// order ran 1.0 % faster than every row in ascending order, at a 1 % higher
+// clock. Each accumulator still sums its k steps in the same order.
+__host__ __device__ constexpr int mfma_col(int m) {
+  return ((m / 8) & 1) ? 7 - m % 8 : m % 8;
+}
 // The next stage's fragment reads go out as 16 units (B block u / 2 -- two
 // transposing reads -- for even u, A block u / 2 for odd u), unit u after
 // MFMA (7 u) / 2: spread over the first 53 MFMAs so that the last reads land
@@ -564,7 +574,8 @@ __device__ __forceinline__ void k_stage(const ASrc& A, const BSrc& B, int t, int
   const int pair = t / 2 + 2;
 #pragma unroll
   for (int m = 0; m < kMfmaPerStage; ++m) {
-    mfma16(acc[m / 8][m % 8], cur.a[m / 8], cur.b[m % 8]);
+    const int i = m / 8, j = mfma_col(m);
+    mfma16(acc[i][j], cur.a[i], cur.b[j]);
     const int q = load_at(m);
     if (q >= 0 && q < 4) A.issue_one(pair, np, (U % 2) * 4 + q, R.a[a_fre]);
     if (q >= 4) B.issue_one(brs, q - 4, R.b[b_fre]);

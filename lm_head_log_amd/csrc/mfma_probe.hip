@@ -75,7 +75,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mfma_probe(
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mfma16(acc[i][j], f[s].a[i], f[s].b[j]);
+        for (int c = 0; c < 8; ++c) {
+          const int j = mfma_col(i * 8 + c);  // the engine's order
+          mfma16(acc[i][j], f[s].a[i], f[s].b[j]);
+        }
   }
   acc_fence(acc);
   __builtin_amdgcn_sched_barrier(0);
