@@ -90,9 +90,11 @@ size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V);
 /* Workspace bytes lmhead_bwd needs: a 256-byte checked copy of the saved
  * header, 32 tile-queue counters per token chunk, 20 bytes per kept row (N
  * rounded up to 256 entries) of logit-gradient coefficients and targets, a
- * bf16 transposed copy of one chunk's kept rows of X ([H][C]), the bf16 logit
- * gradient dZ of one chunk of C rows ([C][V rounded up to 256], token-major),
- * where C = token_chunk rounded up to a multiple of 256, at most N rounded up
+ * bf16 transposed copy of one chunk's kept rows of X ([H][C + 64]), the bf16
+ * logit gradient dZ of one chunk of C rows ([C][V rounded up to 256, + 64],
+ * token-major; the 64 padding elements of a row keep power-of-two row pitches
+ * out of these two buffers), where C = token_chunk rounded up to a multiple
+ * of 256, at most N rounded up
  * to 256 and at most 2^22 (a larger request is clamped to 2^22), and, for
  * V >= 16384, fp32 partial dX tiles: when the dX tiles of a chunk past its
  * last whole round of workgroups number at most 256 (S - 1) / S, each is

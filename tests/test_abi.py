@@ -91,7 +91,8 @@ MAX_N, MAX_H, MAX_V, MAX_CHUNK = 1 << 24, 1 << 20, 1 << 22, 1 << 22
 
 def _bwd_ws(N, H, V, chunk):
     up = lambda x, m: (x + m - 1) // m * m
-    want = chunk if chunk > 0 else max(256, (8 << 30) // (2 * up(V, 256)) // 256 * 256)
+    ldz = up(V, 256) + 64  # dZ rows padded by 64 elements
+    want = chunk if chunk > 0 else max(256, (8 << 30) // (2 * ldz) // 256 * 256)
     want = min(want, MAX_CHUNK)
     C = min(up(want, 256), up(N, 256)) if N > 0 else 0
     nchunks = (N + C - 1) // C if N > 0 else 1
@@ -103,9 +104,10 @@ def _bwd_ws(N, H, V, chunk):
         pieces = 8 if 8 * up(-(-V // 8), 64) <= up(V, 256) else 4
     tail = min(256 * (pieces - 1) // pieces, C // 256 * up(H, 256) // 256) if pieces > 1 else 0
     # checked copy of the saved header | queues | dz coefficients | targets |
-    # one chunk of X_c^T | dZ of one chunk | partial dX tiles
+    # one chunk of X_c^T (rows padded by 64 elements) | dZ of one chunk |
+    # partial dX tiles
     return (256 + _align(nchunks * 4 * 32) + _align(16 * rows) + _align(4 * rows)
-            + _align(H * C * 2) + _align(C * up(V, 256) * 2)
+            + _align(H * (C + 64) * 2) + _align(C * ldz * 2)
             + tail * pieces * 256 * 256 * 4)
 
 
@@ -119,11 +121,12 @@ def test_workspace_sizes(lib):
     # V = 131072 (4 GiB)
     N, H, V = 16384, 4096, 131072
     assert _bwd_ws(N, H, V, 0) == _bwd_ws(N, H, V, 16384)
-    # the 4096-row chunking holds one chunk of dZ and of X_c^T instead of the
-    # whole batch's, and four chunks' tile-queue counters instead of one
+    # the 4096-row chunking holds one chunk of dZ (rows of V + 64) and of X_c^T
+    # instead of the whole batch's, and four chunks' tile-queue counters
+    # instead of one
     queues = _align(4 * 4 * 32) - _align(1 * 4 * 32)
     assert (_bwd_ws(N, H, V, 0) - _bwd_ws(N, H, V, 4096)
-            == (16384 - 4096) * (V + H) * 2 - queues)
+            == (16384 - 4096) * (V + 64 + H) * 2 - queues)
     assert _bwd_ws(262144, 4096, 152064, 0) == _bwd_ws(262144, 4096, 152064, 28160)
     # invalid sizes
     assert lib.lmhead_fwd_workspace_bytes(10, 100, 1000) == 0
