@@ -96,7 +96,7 @@ size_t lmhead_fwd_workspace_bytes(int64_t N, int64_t H, int64_t V);
  * out of these two buffers), where C = token_chunk rounded up to a multiple
  * of 256, at most N rounded up
  * to 256 and at most 2^22 (a larger request is clamped to 2^22), and, for
- * V >= 16384, fp32 partial dX tiles: when the dX tiles of a chunk past its
+ * V >= 2048, fp32 partial dX tiles: when the dX tiles of a chunk past its
  * last whole round of workgroups number at most 256 (S - 1) / S, each is
  * computed as S pieces of the vocabulary range that the whole device runs,
  * then summed in a fixed order; S = 8 when 8 pieces of a multiple of 64

@@ -195,12 +195,15 @@ static inline BwdGeom bwd_geom(int64_t N, int64_t V, int64_t token_chunk) {
 // the last whole round of the grid -- the tail -- number at most
 // 256 (S - 1) / S, each tail tile is cut into S pieces of the K range, which
 // the whole chip runs, and a fixed-order sum of the pieces writes the tile:
-// 672 tiles on 256 CUs take 2.625 tile times instead of 3. Only for
-// V >= kDxSplitMinV, where a piece is long enough to pay for its prologue and
-// epilogue. Pieces are kp = a multiple of 64 vocabulary rows, with S kp within
+// 672 tiles on 256 CUs take 2.625 tile times instead of 3, and the 2 tiles of
+// a 128-row batch at H 512 run as 16 pieces instead of on 2 CUs. Only for
+// V >= kDxSplitMinV: a piece then has at least 256 vocabulary rows (8 stages),
+// enough to pay for its prologue, epilogue and share of the sum (a piece
+// costs about 12 us of fixed work, a whole tile 0.66 us per 32 vocabulary
+// rows). Pieces are kp = a multiple of 64 vocabulary rows, with S kp within
 // the dZ row pitch (V rounded up to 256) so that no piece reads past its
 // row: S = 8 where that holds, else 4 (the pitch is a multiple of 4 x 64).
-constexpr int64_t kDxSplitMinV = 16384;
+constexpr int64_t kDxSplitMinV = 2048;
 static inline int64_t dz_pitch(int64_t V) { return round_up(V, 256); }
 static inline int dx_piece_k_for(int64_t V, int S) { return (int)round_up((V + S - 1) / S, 64); }
 static inline int dx_pieces(int64_t V) {

@@ -100,7 +100,7 @@ def _bwd_ws(N, H, V, chunk):
     # partial dX tiles of a split tail: S pieces of each of at most 256 (S - 1) / S
     # tiles; S = 8 when 8 pieces of a multiple of 64 rows fit in V rounded to 256
     pieces = 1
-    if V >= 16384:
+    if V >= 2048:
         pieces = 8 if 8 * up(-(-V // 8), 64) <= up(V, 256) else 4
     tail = min(256 * (pieces - 1) // pieces, C // 256 * up(H, 256) // 256) if pieces > 1 else 0
     # checked copy of the saved header | queues | dz coefficients | targets |
