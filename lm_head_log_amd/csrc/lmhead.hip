@@ -16,6 +16,8 @@
 //   5. k_zero_skipped  +0.0 log-prob / entropy at skipped rows
 // Backward (twinkle PR #283 section 1: recompute the softmax from saved inputs;
 // SkyRL PR #2374 review: entropy is saved by the forward, not recomputed):
+//   0. k_bwd_check   the saved state against the call's arguments (a
+//                    mismatch leaves the saved state unread and dX, dW zero)
 //   1. k_bwd_rows    per kept row: LSE, upstream grads and target folded into
 //                    the coefficients of dz as a function of the logit
 //   2. k_zero_rows   +0.0 dX rows at skipped positions
@@ -24,7 +26,9 @@
 //      k_dz_tiles    recompute Z^T tile, p = exp(z - LSE),
 //                    dZ = g_lp (onehot - p) - g_H p (z - LSE + H), bf16,
 //                    stored token-major [c][v]
-//      k_dx_tiles    dX[kept rows] = dZ W      (K = vocab)
+//      k_dx_tiles    dX[kept rows] = dZ W      (K = vocab); the tiles of a
+//                    ragged last round as vocabulary pieces, summed in a
+//                    fixed order by k_dx_reduce
 //      k_dw_tiles    dW^T (+)= X_c^T dZ        (K = chunk rows), stored as dW
 // Every GEMM reads a K-major A (W, dZ, X_c^T) and an MN-major B (X_c^T, W, dZ)
 // as they are stored.
