@@ -452,14 +452,18 @@ __device__ __forceinline__ void stat_merge(float& m, float& s, float& b, float m
 // thread 0 adds the totals into per-kernel device counters when the
 // workgroup exits: main-loop and epilogue time and cycles, time spent taking
 // tiles, and the tile count. lmhead_tile_clocks (same build only) reads them.
+// Per XCD it also keeps the earliest workgroup start and the latest
+// workgroup exit of each kernel (lmhead_tile_clocks_xcd), which show how far
+// apart the XCDs finish a launch.
 // ---------------------------------------------------------------------------
 enum { kClkFwd = 0, kClkDz = 1, kClkDx = 2, kClkDw = 3 };
 #ifdef LMHEAD_TILE_CLOCKS
 __device__ unsigned long long g_tile_clock[4][8];
+__device__ unsigned long long g_xcd_clock[4][kXcds][2];  // earliest start, latest exit
 struct TileClock {
-  uint64_t r_end, r_a = 0, r_b = 0, c_a = 0, c_b = 0;
+  uint64_t r0, r_end, r_a = 0, r_b = 0, c_a = 0, c_b = 0;
   uint64_t main = 0, epi = 0, next = 0, n = 0, cmain = 0, cepi = 0;
-  __device__ TileClock() : r_end(__builtin_amdgcn_s_memrealtime()) {}
+  __device__ TileClock() : r0(__builtin_amdgcn_s_memrealtime()), r_end(r0) {}
   __device__ void tile_start() {
     r_a = __builtin_amdgcn_s_memrealtime();
     c_a = __builtin_amdgcn_s_memtime();
@@ -481,6 +485,9 @@ struct TileClock {
     if (threadIdx.x != 0) return;
     const unsigned long long v[7] = {main, epi, next, n, cmain, cepi, 1};
     for (int i = 0; i < 7; ++i) atomicAdd(&g_tile_clock[k][i], v[i]);
+    const int x = xcd_id();
+    atomicMin(&g_xcd_clock[k][x][0], (unsigned long long)r0);
+    atomicMax(&g_xcd_clock[k][x][1], (unsigned long long)__builtin_amdgcn_s_memrealtime());
   }
 };
 #else
@@ -1981,6 +1988,22 @@ LMH_API int lmhead_tile_clocks(unsigned long long* out, int reset) {
   if (reset) {
     static const unsigned long long z[4 * 8] = {};
     if (hipMemcpyToSymbol(HIP_SYMBOL(g_tile_clock), z, sizeof(z)) != hipSuccess) return 1;
+    if (hipDeviceSynchronize() != hipSuccess) return 1;
+  }
+  return 0;
+}
+
+// out[k][x][0..1]: earliest workgroup start and latest workgroup exit of
+// kernel k (fwd, dz, dX, dW) on XCD x, in 100 MHz ticks, since the last reset;
+// a reset sets the starts to the largest value and the exits to 0.
+LMH_API int lmhead_tile_clocks_xcd(unsigned long long* out, int reset) {
+  if (!out || hipDeviceSynchronize() != hipSuccess) return 1;
+  if (hipMemcpyFromSymbol(out, HIP_SYMBOL(g_xcd_clock), sizeof(g_xcd_clock)) != hipSuccess)
+    return 1;
+  if (reset) {
+    unsigned long long z[4 * kXcds * 2];
+    for (int i = 0; i < 4 * kXcds * 2; ++i) z[i] = (i % 2 == 0) ? ~0ull : 0ull;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_xcd_clock), z, sizeof(z)) != hipSuccess) return 1;
     if (hipDeviceSynchronize() != hipSuccess) return 1;
   }
   return 0;

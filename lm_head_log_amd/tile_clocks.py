@@ -7,6 +7,9 @@
         runs forward + backward steps of a synthetic workload on that build and
         prints, per kernel, the time and shader cycles of a tile's main loop and
         epilogue, the time spent taking tiles, and the clock
+    python -m lm_head_log_amd.tile_clocks xcd [--workload dense_rl] [--keep 1.0] [--steps 3]
+        prints, per kernel and step, when each XCD's last workgroup exited,
+        counted from the kernel's first workgroup start
 
 Every workgroup reads the shader clock (s_memtime) and the 100 MHz constant
 clock (s_memrealtime) when it has taken a tile, after the tile's main loop and
@@ -33,7 +36,7 @@ def build() -> str:
     return b.build(verbose=True, defines=("LMHEAD_TILE_CLOCKS",), out=CLOCK_LIB)
 
 
-def run(workload: str, keep: float, steps: int) -> None:
+def run(workload: str, keep: float, steps: int, per_xcd: bool = False) -> None:
     if not os.path.exists(CLOCK_LIB):
         raise SystemExit(f"{CLOCK_LIB} is missing: run `python -m lm_head_log_amd.tile_clocks build`")
     sys.path.insert(0, ROOT)
@@ -83,6 +86,37 @@ def run(workload: str, keep: float, steps: int) -> None:
     out = (ctypes.c_ulonglong * 32)()
     for _ in range(2):
         step()
+    if per_xcd:
+        xq = lib.lmhead_tile_clocks_xcd
+        xq.restype = ctypes.c_int
+        xq.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), ctypes.c_int]
+        xo = (ctypes.c_ulonglong * 64)()
+        rows = {name: [] for name in KERNELS}
+        for _ in range(steps):
+            if xq(xo, 1) != 0:
+                raise SystemExit("lmhead_tile_clocks_xcd failed")
+            step()
+            if xq(xo, 0) != 0:
+                raise SystemExit("lmhead_tile_clocks_xcd failed")
+            a = np.array(xo, dtype=np.float64).reshape(4, 8, 2)
+            for k, name in enumerate(KERNELS):
+                if a[k, :, 1].max() == 0:
+                    continue
+                t0 = a[k, :, 0].min()
+                rows[name].append((a[k, :, 1] - t0) * 1e-2)  # us after the first start
+        print(f"# per-XCD finish: {w.name}, {steps} steps; microseconds from the kernel's first "
+              "workgroup start to each XCD's last workgroup exit (mean over steps)")
+        print(f"{'kernel':10s} {'span_us':>9s} {'spread_us':>9s} {'spread_%':>8s}  per XCD 0..7")
+        for name in KERNELS:
+            if not rows[name]:
+                continue
+            f = np.array(rows[name])
+            span = f.max(axis=1).mean()
+            spread = (f.max(axis=1) - f.min(axis=1)).mean()
+            print(f"{name:10s} {span:9.1f} {spread:9.1f} {100 * spread / span:8.2f}  " +
+                  " ".join(f"{x:8.1f}" for x in f.mean(axis=0)))
+        print("# spread: last XCD exit minus first XCD exit of the same launch")
+        return
     if query(out, 1) != 0:
         raise SystemExit("lmhead_tile_clocks failed")
     for _ in range(steps):
@@ -115,7 +149,7 @@ def run(workload: str, keep: float, steps: int) -> None:
 
 def main() -> None:
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["build", "run"])
+    ap.add_argument("what", choices=["build", "run", "xcd"])
     ap.add_argument("--workload", default="dense_rl",
                     choices=["dense_rl", "packed_grpo", "fp32_stress", "tiny"])
     ap.add_argument("--keep", type=float, default=1.0)
@@ -124,7 +158,7 @@ def main() -> None:
     if args.what == "build":
         print(build())
     else:
-        run(args.workload, args.keep, args.steps)
+        run(args.workload, args.keep, args.steps, per_xcd=args.what == "xcd")
 
 
 if __name__ == "__main__":

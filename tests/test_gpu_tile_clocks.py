@@ -37,13 +37,17 @@ def test_instrumented_build_same_bits_and_tile_counts():
     query = clk.lmhead_tile_clocks
     query.restype = ctypes.c_int
     query.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), ctypes.c_int]
+    xquery = clk.lmhead_tile_clocks_xcd
+    xquery.restype = ctypes.c_int
+    xquery.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), ctypes.c_int]
     out = (ctypes.c_ulonglong * 32)()
+    xout = (ctypes.c_ulonglong * 64)()
     prev = _lib._lib
     _lib._lib = clk
     try:
-        assert query(out, 1) == 0
+        assert query(out, 1) == 0 and xquery(xout, 1) == 0
         got = run(w)
-        assert query(out, 1) == 0
+        assert query(out, 1) == 0 and xquery(xout, 1) == 0
     finally:
         _lib._lib = prev
 
@@ -63,3 +67,10 @@ def test_instrumented_build_same_bits_and_tile_counts():
             f"main {main} ticks / {cmain} cycles, epilogue {epi} ticks / {cepi} cycles")
         assert tiles == expect[k], name
         assert wgs > 0 and main > 0 and epi > 0 and cmain > 0 and cepi > 0, name
+        # per XCD: earliest workgroup start and latest exit (100 MHz ticks);
+        # XCDs that ran none of this kernel's workgroups keep the reset values
+        x = np.array(xout, dtype=np.uint64).reshape(4, 8, 2)[k]
+        ran = x[:, 1] > 0
+        assert ran.any(), name
+        assert (x[ran, 0] < x[ran, 1]).all(), name
+        assert (x[~ran, 0] == np.iinfo(np.uint64).max).all(), name
