@@ -31,7 +31,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
-KERNELS_GEMM = ("fwd_tiles", "dz_tiles", "dx_tiles", "dw_tiles")
+# Tile kernels and the GEMMs one step's launches of each run: dxdw_tiles runs
+# dX's whole tiles and then dW in one launch, dx_tiles then only the pieces of a
+# split dX tail (a part of a GEMM), dw_tiles only a dW of a batch with no rows.
+KERNELS_GEMM = ("fwd_tiles", "dz_tiles", "dxdw_tiles", "dx_tiles", "dw_tiles")
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic_dense_rl_N16384_H4096_V131072.json")
 KERNEL_SOURCES = ("lm_head_log_amd/csrc/lmhead.hip", "lm_head_log_amd/csrc/gemm_core.h")
 
@@ -447,12 +450,27 @@ def main():
     for k, v in kern.items():
         log(f"  kernel {k:13s} {v['ms_per_step']:9.3f} ms/step  "
             f"({v['launches_per_step']:.0f} launches)")
-    dom = max((k for k in kern if k in KERNELS_GEMM), key=lambda k: kern[k]["ms_per_step"])
+    pieces_ms = kern.get("dx_tiles", {}).get("ms_per_step", 0.0)
+
+    def gemm_flops(k):
+        """GEMM flops of one step's launches of tile kernel k, or None where they
+        hold a part of a GEMM: with a split dX tail the combined dX + dW launch
+        carries dX's whole tiles only and dx_tiles the rest."""
+        if k in ("fwd_tiles", "dz_tiles", "dw_tiles"):
+            return fl_gemm
+        if k == "dxdw_tiles":
+            return 2 * fl_gemm if pieces_ms < 0.01 * kern[k]["ms_per_step"] else None
+        if k == "dx_tiles" and "dxdw_tiles" not in kern:
+            return fl_gemm
+        return None
+
+    whole = [k for k in kern if k in KERNELS_GEMM and gemm_flops(k) is not None]
+    dom = max(whole, key=lambda k: kern[k]["ms_per_step"])
     dom_ms = kern[dom]["ms_per_step"]
-    achieved = fl_gemm / (dom_ms * 1e-3) / 1e12
-    for k in KERNELS_GEMM:
-        if k in kern:
-            kern[k]["tflops"] = round(fl_gemm / (kern[k]["ms_per_step"] * 1e-3) / 1e12, 1)
+    achieved = gemm_flops(dom) / (dom_ms * 1e-3) / 1e12
+    for k in whole:
+        kern[k]["tflops"] = round(gemm_flops(k) / (kern[k]["ms_per_step"] * 1e-3) / 1e12, 1)
+        kern[k]["gemms"] = round(gemm_flops(k) / fl_gemm)
 
     probe = None
     if not args.no_probe:

@@ -349,8 +349,10 @@ int lmhead_version(void);
 /* Per-kernel timing for benchmarks (not needed to use the op).
  * Kernel kinds, in order: compact, gather_cols, fwd_tiles, merge,
  * zero_skipped, zero_rows, dz_tiles, dx_tiles, dw_tiles, zero_queues,
- * bwd_rows, merge_shards, dx_reduce. */
-#define LMHEAD_NUM_KERNELS 13
+ * bwd_rows, merge_shards, dx_reduce, dxdw_tiles (dX's whole tiles and then
+ * dW in one launch; dx_tiles is then the split tail's pieces, dw_tiles a dW
+ * launch of a batch with no rows). */
+#define LMHEAD_NUM_KERNELS 14
 
 /* Static name of kernel kind `kind` (NULL if out of range). */
 const char* lmhead_kernel_name(int kind);
@@ -367,10 +369,11 @@ int lmhead_profile_begin(void);
 int lmhead_profile_end(double* ms, int64_t* launches);
 
 /* MFMA ceiling probe for benchmarks (not needed to use the op).
- * Runs the GEMM kernels' inner step -- v_mfma_f32_32x32x16_bf16 in 4 x 4
- * blocks per wave, four waves per workgroup, one workgroup per CU -- with all
- * operands in registers: no loads, no LDS traffic, no barriers. `iters` passes
- * of four k steps each; the flop count is exact. Its rate bounds what the GEMM
+ * Runs the GEMM kernels' inner step -- v_mfma_f32_16x16x32_bf16 in 8 x 8
+ * blocks per wave, in the engine's order, four waves per workgroup, one
+ * workgroup per CU -- with all operands in registers: no loads, no LDS
+ * traffic, no barriers. `iters` passes of two k steps each; the flop count is
+ * exact. Its rate bounds what the GEMM
  * kernels can reach at the clock the chip holds under MFMA load, which
  * depends on how often operand bits switch: operand fragments are read once
  * from `a` and `b` (device bf16 arrays of a_elems / b_elems >= 8 entries,

@@ -51,7 +51,7 @@ SIGNATURES = {
                                   ctypes.POINTER(ctypes.c_double), c_vp]),
 }
 
-NUM_KERNELS = 13
+NUM_KERNELS = 14
 
 _lib = None
 

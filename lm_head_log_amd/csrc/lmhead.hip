@@ -1130,9 +1130,7 @@ __device__ __forceinline__ DxTail dx_tail(const DxParams& P, int rows) {
 }
 
 template <int SHIFT>
-__global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
-  LMH_DECLARE_RING;
-
+__device__ __forceinline__ void dx_tile_loop(const DxParams& P, const Ring& ring) {
   const int n_kept = P.sv.hdr->n_kept;
   const int rows = min(P.C, n_kept - P.c0);
   if (rows <= 0) return;
@@ -1197,7 +1195,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     // row reads are free of bank conflicts.
     const int fence = acc_read_fence();
     lds_barrier();  // every wave is done reading the ring
-    float* stage = reinterpret_cast<float*>(ra0 + wave * 8192);
+    float* stage = reinterpret_cast<float*>(ring.a[0] + wave * 8192);
     const int m0 = tm * kBM + wm * 128;  // first chunk row of the wave's block
     const int n0 = tn * kBN + wn * 128;  // first h of the wave's block
     const int g = lane >> 4;
@@ -1236,6 +1234,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
     clk.tile_done();
   }
   clk.flush(kClkDx);
+}
+
+template <int SHIFT>
+__global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
+  LMH_DECLARE_RING;
+  dx_tile_loop<SHIFT>(P, ring);
 }
 
 // The split tail's dX tiles: the S partial tiles of each are summed in piece
@@ -1387,9 +1391,7 @@ __device__ __forceinline__ void dw_tile_loop(const DwParams& P, const Ring& ring
 // header): the kernel takes the instance whose stage shift runs exactly that
 // many stages, where a shift chosen on the host from the chunk capacity ran
 // up to 11 padding stages per tile (at 23 % kept rows, 11 of 128).
-__global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
-  LMH_DECLARE_RING;
-
+__device__ __forceinline__ void dw_phase(const DwParams& P, const Ring& ring) {
   const int n_kept = P.hdr->n_kept;
   int rows = min(P.C, n_kept - P.c0);
   if (rows <= 0) {
@@ -1405,6 +1407,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
     case 8: dw_tile_loop<8>(P, ring, rows, nk); break;
     default: dw_tile_loop<10>(P, ring, rows, nk); break;
   }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
+  LMH_DECLARE_RING;
+  dw_phase(P, ring);
+}
+
+// dX's whole tiles, then dW, in one launch: a workgroup goes on to dW tiles
+// as soon as its dX tiles are done. dX has few long tiles per workgroup (4 of
+// 2.7 ms at N 16384, H 4096, V 131072), too few to steal, and the XCDs finish
+// them up to 6 % apart; as separate launches every CU waited for the last
+// XCD before dW began. (Two streams cannot do this safely: persistent
+// workgroups keep a CU until their queue is empty, so dW workgroups placed
+// first would hold CUs that dX workgroups need.)
+__global__ __launch_bounds__(kThreads, 1) void k_dxdw_tiles(DxParams X, DwParams W) {
+  LMH_DECLARE_RING;
+  switch (shift_for((X.V + kBK - 1) / kBK)) {
+    case 0: dx_tile_loop<0>(X, ring); break;
+    case 2: dx_tile_loop<2>(X, ring); break;
+    case 4: dx_tile_loop<4>(X, ring); break;
+    case 6: dx_tile_loop<6>(X, ring); break;
+    case 8: dx_tile_loop<8>(X, ring); break;
+    default: dx_tile_loop<10>(X, ring); break;
+  }
+  // every wave has read the dX queue's last broadcast before the dW queue
+  // writes its own (the two may share a word)
+  lds_barrier();
+  dw_phase(W, ring);
 }
 
 // ---------------------------------------------------------------------------
@@ -1452,12 +1482,13 @@ static int check_sizes(int64_t N, int64_t H, int64_t V) {
 // the launch stream around every launch while profiling is on.
 enum KernelKind {
   KK_COMPACT = 0, KK_GATHER_COLS, KK_FWD, KK_MERGE, KK_ZERO_SKIPPED, KK_ZERO_ROWS,
-  KK_DZ, KK_DX, KK_DW, KK_ZERO_QUEUES, KK_BWD_ROWS, KK_MERGE_SHARDS, KK_DX_REDUCE, KK_COUNT
+  KK_DZ, KK_DX, KK_DW, KK_ZERO_QUEUES, KK_BWD_ROWS, KK_MERGE_SHARDS, KK_DX_REDUCE, KK_DXDW,
+  KK_COUNT
 };
 static const char* const kKernelNames[KK_COUNT] = {
     "compact",   "gather_cols", "fwd_tiles", "merge",    "zero_skipped",
     "zero_rows", "dz_tiles",    "dx_tiles",  "dw_tiles", "zero_queues", "bwd_rows",
-    "merge_shards", "dx_reduce"};
+    "merge_shards", "dx_reduce", "dxdw_tiles"};
 
 struct ProfRec {
   hipEvent_t a, b;
@@ -1797,6 +1828,23 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
   }
   const int nv = n_vtiles(V);
   const int64_t nchunks = N > 0 ? (N + G.C - 1) / G.C : 1;
+  auto dw_params = [&](int64_t ch, int c0) {
+    DwParams Wp;
+    Wp.XcT = XcT;
+    Wp.dZ = dZ;
+    Wp.hdr = sv.hdr;
+    Wp.H = (int)H;
+    Wp.V = (int)V;
+    Wp.c0 = c0;
+    Wp.C = (int)G.C;
+    Wp.ldc = G.ldc;
+    Wp.ldz = G.ldz;
+    Wp.accumulate = ch > 0;
+    Wp.dW = grad_weight;
+    Wp.queue = queues + (ch * kBwdQueueSets + 3) * kQueueInts;
+    Wp.steal = 0;
+    return Wp;
+  };
   for (int64_t ch = 0; ch < nchunks; ++ch) {
     const int c0 = (int)(ch * G.C);
     if (N > 0) {
@@ -1844,18 +1892,20 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
       X2.C = (int)G.C;
       X2.dX = grad_hidden;
       const int64_t dx_tiles = dx_tiles_per_chunk(G.C, H);
-      const int dx_grid = persistent_grid(dx_tiles);
+      const int64_t dw_tiles = (int64_t)nv * ((H + kBN - 1) / kBN);
+      // one launch runs dX's whole tiles, then dW's tiles: the grid fits both
+      const int grid = std::max(persistent_grid(dx_tiles), persistent_grid(dw_tiles));
       X2.queue = queues + (ch * kBwdQueueSets + 1) * kQueueInts;
-      X2.steal = steal_for(dx_tiles, dx_grid);
-      X2.G = dx_grid;
+      X2.steal = steal_for(dx_tiles, grid);
+      X2.G = grid;
       X2.S = dx_pieces(V);
       X2.rmax = dx_tail_max(G.C, H, V);
       X2.kp = dx_piece_k(V);
       X2.part = reinterpret_cast<float*>(w + L.part);
       X2.pieces = 0;
-      LMH_TRY(launch_shifted(KK_DX, shift_for((int)((V + kBK - 1) / kBK)), dim3(dx_grid), s, X2,
-                             k_dx_tiles<0>, k_dx_tiles<2>, k_dx_tiles<4>, k_dx_tiles<6>,
-                             k_dx_tiles<8>, k_dx_tiles<10>));
+      DwParams Wp = dw_params(ch, c0);
+      Wp.steal = steal_for(dw_tiles, grid);
+      LMH_TRY(launch(KK_DXDW, k_dxdw_tiles, dim3(grid), dim3(kThreads), s, X2, Wp));
       if (X2.S > 1) {
         // the pieces of a split tail, then their sum; both exit at once when
         // the kept rows leave no tail to split (decided on the device)
@@ -1870,24 +1920,14 @@ static int bwd_impl(const void* hidden, const void* weight, const int32_t* targe
         LMH_TRY(launch(KK_DX_REDUCE, k_dx_reduce, dim3((unsigned)(X2.rmax * (kBM * kBN / 4) / 256)),
                        dim3(256), s, X2));
       }
+    } else {
+      // no rows: dW is written as zeros
+      const int64_t dw_tiles = (int64_t)nv * ((H + kBN - 1) / kBN);
+      const int dw_grid = persistent_grid(dw_tiles);
+      DwParams Wp = dw_params(ch, c0);
+      Wp.steal = steal_for(dw_tiles, dw_grid);
+      LMH_TRY(launch(KK_DW, k_dw_tiles, dim3(dw_grid), dim3(kThreads), s, Wp));
     }
-    DwParams Wp;
-    Wp.XcT = XcT;
-    Wp.dZ = dZ;
-    Wp.hdr = sv.hdr;
-    Wp.H = (int)H;
-    Wp.V = (int)V;
-    Wp.c0 = c0;
-    Wp.C = (int)G.C;
-    Wp.ldc = G.ldc;
-    Wp.ldz = G.ldz;
-    Wp.accumulate = ch > 0;
-    Wp.dW = grad_weight;
-    const int64_t dw_tiles = (int64_t)nv * ((H + kBN - 1) / kBN);
-    const int dw_grid = persistent_grid(dw_tiles);
-    Wp.queue = queues + (ch * kBwdQueueSets + 3) * kQueueInts;
-    Wp.steal = steal_for(dw_tiles, dw_grid);
-    LMH_TRY(launch(KK_DW, k_dw_tiles, dim3(dw_grid), dim3(kThreads), s, Wp));
   }
   return LMHEAD_OK;
 }

@@ -115,7 +115,9 @@ def run(workload: str, keep: float, steps: int, per_xcd: bool = False) -> None:
             spread = (f.max(axis=1) - f.min(axis=1)).mean()
             print(f"{name:10s} {span:9.1f} {spread:9.1f} {100 * spread / span:8.2f}  " +
                   " ".join(f"{x:8.1f}" for x in f.mean(axis=0)))
-        print("# spread: last XCD exit minus first XCD exit of the same launch")
+        print("# spread: last XCD exit minus first XCD exit of the same launch; dx_tiles and dw_tiles")
+        print("# are the two phases of the combined dX + dW launch (a dX tail split's pieces launch, which")
+        print("# runs after it, counts as dx_tiles too and then stretches that row's span)")
         return
     if query(out, 1) != 0:
         raise SystemExit("lmhead_tile_clocks failed")

@@ -25,8 +25,9 @@ def test_traffic_table_is_keyed_by_the_kernel_sources():
     # a stale table (sources changed since the counters were taken) gives None,
     # a current one gives the per-launch bytes of each GEMM kernel
     if tab["source_sha256"] == bench.kernel_source_hash():
-        for k in ("fwd_tiles", "dz_tiles", "dx_tiles", "dw_tiles"):
+        assert "fwd_tiles" in tab["kernels"] and "dz_tiles" in tab["kernels"]
+        for k in tab["kernels"]:
             assert bench.measured_traffic(k, wl) == tab["kernels"][k]["hbm_bytes_per_launch"]
     else:
-        assert bench.measured_traffic("dx_tiles", wl) is None
-    assert bench.measured_traffic("dx_tiles", "another workload") is None
+        assert bench.measured_traffic("dz_tiles", wl) is None
+    assert bench.measured_traffic("dz_tiles", "another workload") is None
