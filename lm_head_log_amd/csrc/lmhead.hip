@@ -1105,8 +1105,9 @@ struct DxParams {
   float* dX;
   int* queue;  // tile-queue counters of this launch (zero before it)
   int steal;
-  // tail split (see kDxPieces)
-  int G;       // grid of the whole-tile launch: its tiles past the last whole round are the tail
+  // tail split (see kDxSplitMinV)
+  int G;       // grid of the launch running the whole tiles (k_dxdw_tiles): its tiles past
+               // the last whole round are the tail
   int S;       // pieces per split tail tile (1: never split)
   int rmax;    // largest tail that is split; `part` holds rmax * S tiles
   int kp;      // vocabulary rows per piece, a multiple of 64
@@ -1236,6 +1237,8 @@ __device__ __forceinline__ void dx_tile_loop(const DxParams& P, const Ring& ring
   clk.flush(kClkDx);
 }
 
+// A split tail's pieces, as a launch of their own (dX's whole tiles run in
+// k_dxdw_tiles, ahead of dW).
 template <int SHIFT>
 __global__ __launch_bounds__(kThreads, 1) void k_dx_tiles(DxParams P) {
   LMH_DECLARE_RING;
@@ -1417,8 +1420,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dw_tiles(DwParams P) {
 // dX's whole tiles, then dW, in one launch: a workgroup goes on to dW tiles
 // as soon as its dX tiles are done. dX has few long tiles per workgroup (4 of
 // 2.7 ms at N 16384, H 4096, V 131072), too few to steal, and the XCDs finish
-// them up to 6 % apart; as separate launches every CU waited for the last
-// XCD before dW began. (Two streams cannot do this safely: persistent
+// them 5-9 % apart; as separate launches every CU waited for the last XCD
+// before dW began. (Two streams cannot do this safely: persistent
 // workgroups keep a CU until their queue is empty, so dW workgroups placed
 // first would hold CUs that dX workgroups need.)
 __global__ __launch_bounds__(kThreads, 1) void k_dxdw_tiles(DxParams X, DwParams W) {
